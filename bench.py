@@ -1,0 +1,188 @@
+"""Benchmark: Muon optimizer steps/s on the MoE expert batch 256 x (2048 x 7168) bf16.
+
+One step = the whole hot path over all 256 matrices: momentum + Nesterov
+input + ||N||_F, normalisation, 10 hybrid Newton-Schulz iterations (each a
+grouped X X^T, A A and (aI + bA + cA^2) X launch) and the fused rescale,
+decay and update.  Inputs are synthetic (seeded, generated on the device with
+the low-rank-plus-noise gradient law) and resident in HBM before timing.
+
+Prints one JSON line.  `roofline` reports the dominant kernel (most total
+time) with its algorithmic FLOPs (or bytes) per launch divided by its average
+launch duration, measured with HIP events on the stream it runs on.
+`cpu_baseline` times the CPU oracle on one of the 256 matrices and scales to
+a step.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Muon optimizer steps/sec + NS TFLOP/s (% bf16 MFMA peak), 256×(2048×7168) batch"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+NS_STAGES = ("gram", "poly", "apply", "apply_update")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_moe_256x2048x7168.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_source_sha():
+    with open(os.path.join(ROOT, "muon_step_amd", "csrc", "ns_gemm.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def cpu_baseline(rows, cols, count):
+    """The oracle as it stands on one matrix of the batch; scaled to one step."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    wl = synth.Workload("moe_256x2048x7168_bf16", 4, (synth.MatrixSpec(rows, cols),))
+    inp = synth.matrix_inputs(wl, 0)
+    t0 = time.perf_counter()
+    oracle.muon_step(inp["w"], inp["g"], inp["m"], param_bf16=True)
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / (dt * count), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"1 of {count} matrices ({rows}x{cols}), full oracle step (fp32 bookkeeping, fp64 "
+                      f"Newton-Schulz) in {dt:.2f} s, scaled x{count}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--experts", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU work of a sharded "
+              "run is the same grouped kernel on that GPU's share of matrices); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import muon_step_amd as ms
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    rows, cols, count = 2048, 7168, args.experts
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    log(f"generating {count} x {rows}x{cols} bf16 inputs on the device")
+    grads = synth.spectral_grad_torch(rows, cols, count, gen, "cuda")
+    params = (torch.randn(count, rows, cols, generator=gen, device="cuda") * synth.gen.PARAM_STD).to(torch.bfloat16)
+    moms = torch.zeros(count, rows, cols, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    mats = [ms.matrix(params[e], grads[e], moms[e]) for e in range(count)]
+    hp = ms.make_hparams(lr=0.02, momentum=0.95, weight_decay=0.1, gamma=0.2, nesterov=True,
+                         ns_precision=ms.MUON_NS_BF16)
+    ctx = ms.Context(0)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        ctx.muon_step(mats, hp, stream)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    ctx.muon_profile_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        ctx.muon_step(mats, hp, stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    stages = ctx.muon_profile_read()
+    ctx.muon_profile_enable(False)
+    ms_per_step = total_ms / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+    for name, st in stages.items():
+        avg = st["total_ms"] / st["launches"]
+        rate = (f"{st['flops'] / st['total_ms'] / 1e9:8.1f} TFLOP/s" if st["flops"] else
+                f"{st['bytes'] / st['total_ms'] / 1e6:8.1f} GB/s")
+        log(f"  {name:18s} launches {st['launches']:5d}  avg {avg:9.4f} ms  total/step "
+            f"{st['total_ms'] / args.steps:9.3f} ms  {rate}")
+
+    ns_ms = sum(stages[k]["total_ms"] for k in NS_STAGES if k in stages)
+    ns_flops = sum(stages[k]["flops"] for k in NS_STAGES if k in stages)
+    ns_tflops = ns_flops / ns_ms / 1e9 if ns_ms else 0.0
+    dense_flops_step = count * 10 * 2 * (2 * cols * rows * rows + rows ** 3)
+    dom_name = max(stages, key=lambda k: stages[k]["total_ms"])
+    dom = stages[dom_name]
+    avg_ms = dom["total_ms"] / dom["launches"]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_stage") == dom_name and tr.get("source_sha256") == gemm_source_sha():
+            traffic = tr.get("hbm_bytes_per_launch")
+    if dom["flops"]:
+        achieved = dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "flops_per_launch": dom["flops"] / dom["launches"], "avg_launch_ms": round(avg_ms, 4)}
+    else:
+        achieved = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "bytes_per_launch": dom["bytes"] / dom["launches"], "avg_launch_ms": round(avg_ms, 4)}
+    elementwise = {}
+    for k in ("momentum_nesterov", "normalize"):
+        if k in stages and stages[k]["total_ms"]:
+            gbs = stages[k]["bytes"] / stages[k]["total_ms"] / 1e6
+            elementwise[k] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                              "ms_per_step": round(stages[k]["total_ms"] / args.steps, 4)}
+    out = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_per_step, 4),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded low-rank-plus-noise bf16 gradients, N(0,0.02) bf16 params, zero fp32 momentum)",
+        "config": {"workload": "moe_256x2048x7168_bf16", "matrices": count, "shape": [rows, cols],
+                   "ns_steps": 10, "schedule": "deepseekv4 8x(3.4445,-4.7750,2.0315)+2x(2,-1.5,0.5)",
+                   "ns_precision": "bf16 MFMA operands, fp32 accumulate, fp32 master X",
+                   "lr": 0.02, "momentum": 0.95, "weight_decay": 0.1, "gamma": 0.2},
+        "ns_tflops": round(ns_tflops, 2),
+        "ns_frac_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4),
+        "ns_dense_equivalent_tflops": round(dense_flops_step * args.steps / ns_ms / 1e9, 2) if ns_ms else None,
+        "ns_ms_per_step": round(ns_ms / args.steps, 3),
+        "elementwise": elementwise,
+        "roofline": roof,
+        "cpu_baseline": None,
+        "pages_context": "NS adds ~5% training FLOPs (DeepSeek-V4 book ch. 6; no hardware given)",
+    }
+    ctx.close()
+    del grads, params, moms, mats
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one matrix")
+        out["cpu_baseline"] = cpu_baseline(rows, cols, count)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,260 @@
+/*
+ * muon_step.h - C ABI of an MI355X (gfx950) Muon optimizer step.
+ *
+ * One call performs, for every weight matrix W (n x m) it is given, the
+ * DeepSeek-V4 Muon update (the Muon deep-dive page "Muon 优化器完全拆解",
+ * section "V4 的完整更新公式，逐行拆解"; the DeepSeek-V4 book, ch. 6 "Muon",
+ * section 5, whose expanded Algorithm 1 writes the normalisation out):
+ *
+ *     M_t  = mu * M_{t-1} + G_t                  momentum accumulate
+ *     N_t  = mu * M_t + G_t                      Nesterov input (nesterov = 1)
+ *     X    = N_t / ||N_t||_F                     (Gram taken on the smaller side)
+ *     for each (a, b, c) of the schedule:  X = a X + b (X X^T) X + c (X X^T)^2 X
+ *     O_t  = X * sqrt(max(n, m)) * gamma
+ *     W_t  = (1 - lr * wd) * W_{t-1} - lr * O_t
+ *
+ * and a second entry point runs the elementwise AdamW step that the pages
+ * assign to embedding and prediction-head tensors (the deep-dive page,
+ * section "为什么嵌入层、输出头、bias、RMSNorm 还在用 AdamW").
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers documented as "device" point to memory of the context's GPU;
+ *     "host" pointers are read before the call returns and may be freed then.
+ *   - Matrices are row-major and contiguous (row pitch == cols elements).
+ *   - Work is enqueued on the given HIP stream (NULL = the null stream); no
+ *     entry point synchronises the stream except where stated.
+ *   - Every argument is validated before anything is enqueued: a non-OK
+ *     status means no work was enqueued.  Launch failures return
+ *     MUON_ERR_DEVICE.  No C++ exception crosses this boundary.
+ *   - A context is not thread-safe; calls on one context must be ordered by
+ *     the caller (one stream at a time, or explicit synchronisation).
+ *   - Results are deterministic: identical inputs give bit-identical outputs
+ *     (no atomics in any reduction).
+ */
+#ifndef MUON_STEP_H
+#define MUON_STEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_STEP_ABI_VERSION 1
+
+typedef enum muon_status {
+    MUON_OK = 0,
+    MUON_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, aliasing, bad enum    */
+    MUON_ERR_UNSUPPORTED = 2,      /* valid but not implemented (dtype combination)  */
+    MUON_ERR_OUT_OF_MEMORY = 3,    /* workspace could not be allocated within cap    */
+    MUON_ERR_DEVICE = 4            /* a HIP call or kernel launch failed             */
+} muon_status;
+
+typedef enum muon_dtype {
+    MUON_F32 = 0,  /* IEEE binary32                                   */
+    MUON_BF16 = 1  /* bfloat16; every cast to it rounds to nearest even */
+} muon_dtype;
+
+/* Arithmetic of the Newton-Schulz products.
+ * MUON_NS_BF16: bf16 MFMA operands, fp32 accumulation, fp32 master copy of X
+ *               between iterations (relative Frobenius error vs fp64 ~1e-2).
+ * MUON_NS_F32:  fp32 MFMA operands and accumulation (error vs fp64 ~1e-6). */
+typedef enum muon_ns_precision { MUON_NS_BF16 = 0, MUON_NS_F32 = 1 } muon_ns_precision;
+
+/* One Newton-Schulz step X <- a X + b (X X^T) X + c (X X^T)^2 X
+ * (DeepSeek-V4 book ch. 6, section 3).  Passed to kernels as fp32. */
+typedef struct muon_ns_coeff {
+    double a, b, c;
+} muon_ns_coeff;
+
+/* One weight matrix handed to muon_step.  Layout: row-major rows x cols.
+ *   param    device, param_dtype, W_{t-1} in, W_t out (in place)
+ *   grad     device, grad_dtype, G_t, read only
+ *   momentum device, fp32, M_{t-1} in, M_t out (in place); the single buffer
+ *            also serves the Nesterov input (the deep-dive page, Nesterov step)
+ *   ns_out   optional device fp32 rows x cols; when non-NULL it receives the
+ *            orthogonalised update O'_t before the sqrt(max)*gamma rescale
+ *            (diagnostics and parity checks).  NULL: nothing is written.
+ * grad must not overlap param, momentum or ns_out; momentum must not overlap
+ * param; no two matrices of one call may share param or momentum memory. */
+typedef struct muon_matrix {
+    void *param;
+    const void *grad;
+    float *momentum;
+    float *ns_out;
+    int64_t rows;
+    int64_t cols;
+    int32_t param_dtype; /* muon_dtype */
+    int32_t grad_dtype;  /* muon_dtype */
+} muon_matrix;
+
+/* Hyper-parameters of Algorithm 1 (the deep-dive page's Algorithm 1 inputs:
+ * learning rate, momentum, weight decay, update scale gamma) plus the
+ * Newton-Schulz schedule.
+ *   schedule      host array of num_ns_steps coefficient triples, applied in
+ *                 order; may be NULL only when num_ns_steps == 0.  The
+ *                 DeepSeek-V4 hybrid schedule is returned by
+ *                 muon_schedule("deepseekv4", ...).
+ *   num_ns_steps  0..64.  0 means X = N / ||N||_F with no iteration.
+ *   nesterov      1: NS input mu*M_t + G_t;  0: NS input M_t.
+ *   ns_precision  muon_ns_precision.
+ * lr, momentum, weight_decay and gamma must be finite. */
+typedef struct muon_hparams {
+    double lr;
+    double momentum;
+    double weight_decay;
+    double gamma;
+    const muon_ns_coeff *schedule;
+    int32_t num_ns_steps;
+    int32_t nesterov;
+    int32_t ns_precision;
+    int32_t reserved; /* must be 0 */
+} muon_hparams;
+
+/* One tensor handed to muon_adamw_step: numel contiguous fp32 elements each
+ * of param (in/out), grad (in), exp_avg (in/out) and exp_avg_sq (in/out).
+ * param_dtype and grad_dtype must be MUON_F32 (other values: UNSUPPORTED).
+ * grad must not overlap the other three; no two of param, exp_avg and
+ * exp_avg_sq may overlap. */
+typedef struct muon_adamw_tensor {
+    void *param;
+    const void *grad;
+    float *exp_avg;
+    float *exp_avg_sq;
+    int64_t numel;
+    int32_t param_dtype;
+    int32_t grad_dtype;
+} muon_adamw_tensor;
+
+/* AdamW with bias correction and decoupled multiplicative decay:
+ *   p <- (1 - lr wd) p;  m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2;
+ *   p <- p - lr * (m / (1 - b1^step)) / (sqrt(v / (1 - b2^step)) + eps)
+ * in fp32 with one rounding per operation in exactly this order (correctly
+ * rounded division and square root); the scalars 1-lr*wd, 1-b1, 1-b2,
+ * 1-b1^step, 1-b2^step are formed in double and rounded once.
+ * step >= 1 counts the steps including this one. */
+typedef struct muon_adamw_hparams {
+    double lr;
+    double beta1;
+    double beta2;
+    double eps;
+    double weight_decay;
+    int64_t step;
+} muon_adamw_hparams;
+
+typedef struct muon_context muon_context; /* opaque */
+
+/* ABI version of the loaded library (MUON_STEP_ABI_VERSION it was built with). */
+int32_t muon_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char *muon_status_string(muon_status status);
+
+/* Named coefficient schedules from the pages:
+ *   "deepseekv4": 8 x (3.4445, -4.7750, 2.0315) then 2 x (2, -1.5, 0.5)
+ *                 (DeepSeek-V4 book ch. 6, sections 4-5)
+ *   "quintic":    5 x (3.4445, -4.7750, 2.0315) (the deep-dive page,
+ *                 "系数怎么调出来的" and the Megatron-Bridge recipe)
+ * Writes min(count, capacity) triples to out (host; may be NULL when
+ * capacity is 0) and returns the schedule's length, or -1 for an unknown
+ * name.  Pure host function. */
+int64_t muon_schedule(const char *name, muon_ns_coeff *out, int64_t capacity);
+
+/* Host-only validation of a muon_step argument list: the exact checks
+ * muon_step performs before it enqueues anything.  Touches no GPU.  On
+ * failure writes a NUL-terminated reason into msg (host, msg_cap bytes;
+ * msg may be NULL when msg_cap is 0). */
+muon_status muon_check_step_args(const muon_matrix *mats, int64_t count, const muon_hparams *hp,
+                                 char *msg, size_t msg_cap);
+
+/* Host-only validation of a muon_adamw_step argument list. */
+muon_status muon_check_adamw_args(const muon_adamw_tensor *ts, int64_t count,
+                                  const muon_adamw_hparams *hp, char *msg, size_t msg_cap);
+
+/* Workspace the library would allocate for this argument list when nothing
+ * caps it: the largest per-group chunk of Newton-Schulz buffers plus the
+ * per-matrix tables.  Pure host function; validates like
+ * muon_check_step_args. */
+muon_status muon_workspace_bytes(const muon_matrix *mats, int64_t count, const muon_hparams *hp,
+                                 size_t *bytes_out);
+
+/* Creates a context on HIP device hip_device.  workspace_cap_bytes bounds
+ * the Newton-Schulz workspace the context may hold (0 = no bound); matrices
+ * of one shape are processed in chunks that fit it.  *out receives the
+ * context (host pointer) or NULL on failure. */
+muon_status muon_create(muon_context **out, int32_t hip_device, size_t workspace_cap_bytes);
+
+/* Waits for the context's outstanding uploads, frees its device memory and
+ * the context.  NULL is accepted (no-op).  Work already enqueued by the
+ * caller on its streams must be complete or ordered before the free. */
+muon_status muon_destroy(muon_context *ctx);
+
+/* Last error message of this context (host string owned by the context,
+ * valid until its next call); "" when the last call succeeded. */
+const char *muon_last_error(const muon_context *ctx);
+
+/* One Muon step over `count` matrices (host array mats).  Matrices with the
+ * same (rows, cols, param_dtype, grad_dtype) are batched: every stage runs
+ * as one grouped launch over all of them.  A matrix whose N_t is all zero
+ * gets the decay-only update W_t = (1 - lr wd) W_{t-1}.  Non-finite values
+ * propagate (IEEE). */
+muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count,
+                      const muon_hparams *hp, void *hip_stream);
+
+/* One AdamW step over `count` tensors (host array ts), one launch. */
+muon_status muon_adamw_step(muon_context *ctx, const muon_adamw_tensor *ts, int64_t count,
+                            const muon_adamw_hparams *hp, void *hip_stream);
+
+/* Normalisation + Newton-Schulz only: x_out (device fp32 rows x cols)
+ * receives NS(n_in / ||n_in||_F) for the device fp32 rows x cols input n_in,
+ * with hp's schedule and precision (lr, momentum, weight_decay, gamma and
+ * nesterov are ignored).  n_in and x_out must not overlap. */
+muon_status muon_ns_only(muon_context *ctx, const float *n_in, float *x_out, int64_t rows,
+                         int64_t cols, const muon_hparams *hp, void *hip_stream);
+
+/* Decay + update given an orthogonalised update x (device fp32 rows x cols,
+ * the unscaled O'_t):  param <- fl(fl(d * param) - fl(s * x)) with
+ * d = fl32(1 - lr*wd), s = fl32(lr * gamma * sqrt(max(rows, cols))), rounded
+ * to bf16 (nearest even) when param_dtype is MUON_BF16.  Exactly the
+ * arithmetic muon_step's last stage performs. */
+muon_status muon_apply_update(muon_context *ctx, void *param, int32_t param_dtype, const float *x,
+                              int64_t rows, int64_t cols, const muon_hparams *hp,
+                              void *hip_stream);
+
+/* Blocks until the context's device memory holds the per-matrix squared
+ * Frobenius norms of the last muon_step's N_t (matrix order of that call)
+ * and copies min(count, capacity) of them to out (host doubles).  Returns
+ * the count through *count_out.  Synchronises the last call's stream. */
+muon_status muon_last_norms(muon_context *ctx, double *out, int64_t capacity, int64_t *count_out);
+
+/* Per-stage timing of a context's launches.  While enabled, every kernel
+ * launch the context makes is bracketed by two HIP events recorded on the
+ * stream it is launched on; the stage's algorithmic work of that launch (the
+ * FLOPs the method must do, counting one triangle of the symmetric X X^T and
+ * A A, and the bytes it must move to and from HBM) is recorded with it.
+ * Stage names: "momentum_nesterov", "norm_finalize", "normalize", "gram",
+ * "poly", "apply", "apply_update" (the last product with the fused decay and
+ * update), "update", "adamw", "import", "export". */
+typedef struct muon_stage_stats {
+    char name[32];
+    int64_t launches;
+    double total_ms; /* sum of the launches' event-measured durations */
+    double flops;    /* algorithmic FLOPs of those launches             */
+    double bytes;    /* algorithmic HBM bytes of those launches         */
+} muon_stage_stats;
+
+/* Enables (1) or disables (0) per-stage timing and discards what was
+ * recorded so far.  Disabled by default. */
+muon_status muon_profile_enable(muon_context *ctx, int32_t enable);
+
+/* Waits for the recorded events, aggregates them per stage into out (host,
+ * capacity entries, stages in first-launch order), writes the number of
+ * stages to *count and discards the records. */
+muon_status muon_profile_read(muon_context *ctx, muon_stage_stats *out, int32_t capacity, int32_t *count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_STEP_H */

@@ -1,0 +1,94 @@
+// Shared device-side types and helpers of the Muon step library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Per-matrix pointers of one grouped launch (device table, one entry per
+// matrix of the chunk being processed).
+struct MatDesc {
+    void *param;        // W, param dtype, rows x cols
+    const void *grad;   // G, grad dtype, rows x cols
+    float *mom;         // M, fp32, rows x cols
+    float *ns_out;      // optional O'_t, fp32, rows x cols (nullptr = skip)
+    int64_t call_index; // position of the matrix in the caller's list
+    int64_t pad_;
+};
+
+// Geometry of one group of same-shape matrices.  The Newton-Schulz iterate is
+// held as X (s x l, row-major, row pitch lp) with s = min(rows, cols),
+// l = max(rows, cols); transposed != 0 when rows > cols (X = N^T).
+struct Geom {
+    int64_t rows, cols;   // W shape
+    int64_t s, l;         // X shape
+    int64_t sp, lp;       // padded X shape (multiples of the GEMM tiles)
+    int32_t transposed;
+    int32_t pad_;
+};
+
+// Workspace of one chunk: matrix e of the chunk owns
+//   xf      + e*x_stride  fp32 master X (sp x lp), read by the current step
+//   xf_next + e*x_stride  where the current step writes X (== xf on the bf16
+//                         path, where only the tile's own epilogue touches it)
+//   xb      + e*x_stride  bf16 operand copy of X (bf16 path only)
+//   xb_next + e*x_stride  where the current step writes it: the product B X
+//                         reads whole column panels of X, so the operand copy
+//                         is double-buffered
+//   af + e*a_stride       fp32 A = X X^T (sp x sp, lower-triangle tiles)
+//   ab + e*a_stride       A as MFMA operand (bf16 or fp32, both triangles)
+//   bb + e*a_stride       B = bA + cA^2 as MFMA operand (both triangles)
+struct Work {
+    float *xf;
+    float *xf_next;
+    void *xb;
+    void *xb_next;
+    float *af;
+    void *ab;
+    void *bb;
+    int64_t x_stride;
+    int64_t a_stride;
+    double *partials;     // per-block sums of N^2
+    double *nrm2;         // per chunk matrix
+    float *inv_norm;      // per chunk matrix: 1/||N||_F (0 when ||N|| == 0)
+    double *call_nrm2;    // per call matrix (indexed by MatDesc::call_index)
+};
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 bits.  gfx950 does this in one
+// instruction (v_cvt_pk_bf16_f32) when the compiler lowers the cast.
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+    __bf16 h = static_cast<__bf16>(f);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 p;
+    p[0] = static_cast<__bf16>(lo);
+    p[1] = static_cast<__bf16>(hi);
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// Blocks whose ids the hardware spreads round-robin over the 8 XCDs are
+// renumbered so that consecutive logical ids run on the same XCD (and share
+// its L2).  Bijective on [0, nblocks).
+__device__ __forceinline__ int64_t xcd_swizzle(int64_t b, int64_t nblocks) {
+    const int64_t n_xcd = 8;
+    int64_t q = nblocks / n_xcd;
+    if (b >= q * n_xcd) return b;
+    return (b % n_xcd) * q + b / n_xcd;
+}
+
+}  // namespace muon

@@ -1,0 +1,493 @@
+// Elementwise and reduction kernels of the Muon step (HBM-bound).
+//
+//  * nesterov_*      : M_t = mu M_{t-1} + G_t, N_t = mu M_t + G_t (deep-dive page,
+//                      "V4 的完整更新公式" steps 1-2; DeepSeek-V4 book ch. 6 §5),
+//                      N_t written into the X workspace in the s x l orientation
+//                      (transposed through LDS when rows > cols), per-block sums of
+//                      N_t^2 in fp64.
+//  * norm_finalize   : ||N_t||_F^2 per matrix from the block sums, fixed order.
+//  * normalize       : X_0 = N_t / ||N_t||_F (book ch. 6 §5, normalisation line),
+//                      fp32 master + bf16 operand copy, zero padding.
+//  * update_*        : W_t = (1 - lr wd) W_{t-1} - lr gamma sqrt(max) X (deep-dive
+//                      page step 4-5), fl32 ops in exactly that order.
+//  * adamw           : the AdamW step of embedding/head tensors.
+//
+// All float arithmetic here is compiled with -ffp-contract=off so every
+// multiply and add rounds once, matching the fp32 bookkeeping reference.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace muon {
+
+template <typename T> __device__ __forceinline__ float load_val(const T *p, int64_t i);
+template <> __device__ __forceinline__ float load_val<float>(const float *p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_val<uint16_t>(const uint16_t *p, int64_t i) {
+    return bf16_bits_to_float(p[i]);
+}
+template <typename T> __device__ __forceinline__ void store_val(T *p, int64_t i, float v);
+template <> __device__ __forceinline__ void store_val<float>(float *p, int64_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void store_val<uint16_t>(uint16_t *p, int64_t i, float v) {
+    p[i] = float_to_bf16_bits(v);
+}
+
+// Deterministic block reduction of one double per thread (fixed tree order).
+template <int NT>
+__device__ __forceinline__ double block_sum(double v, double *sh) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_down(v, off, 64);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    if (lane == 0) sh[wid] = v;
+    __syncthreads();
+    double r = 0.0;
+    if (threadIdx.x == 0) {
+        for (int w = 0; w < NT / 64; ++w) r += sh[w];
+    }
+    return r;  // valid in thread 0
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1, rows <= cols: X = N (no transpose).  Block (e, rb) handles rows
+// [rb*rows_per_block, ...) of matrix e.
+template <typename GradT, bool VEC>
+__global__ __launch_bounds__(256) void nesterov_rows_kernel(const MatDesc *__restrict__ descs,
+                                                            Geom g, Work w, float mu,
+                                                            int nesterov, int rows_per_block,
+                                                            int blocks_per_mat) {
+    __shared__ double sh[4];
+    const int64_t e = blockIdx.x / blocks_per_mat;
+    const int64_t rb = blockIdx.x % blocks_per_mat;
+    const MatDesc d = descs[e];
+    const GradT *__restrict__ gp = static_cast<const GradT *>(d.grad);
+    float *__restrict__ mp = d.mom;
+    float *__restrict__ xf = w.xf + e * w.x_stride;
+    const int64_t r0 = rb * rows_per_block;
+    const int64_t r1 = min<int64_t>(g.rows, r0 + rows_per_block);
+    const int64_t cols = g.cols;
+    double acc = 0.0;
+    if (VEC) {
+        const int64_t cv = cols / 4;
+        const int64_t total = (r1 - r0) * cv;
+        for (int64_t t = threadIdx.x; t < total; t += 256) {
+            const int64_t i = r0 + t / cv;
+            const int64_t j = (t % cv) * 4;
+            const int64_t src = i * cols + j;
+            float gv[4];
+            if constexpr (sizeof(GradT) == 2) {
+                const u32x2 raw = *reinterpret_cast<const u32x2 *>(gp + src);
+                gv[0] = __uint_as_float(raw[0] << 16);
+                gv[1] = __uint_as_float(raw[0] & 0xffff0000u);
+                gv[2] = __uint_as_float(raw[1] << 16);
+                gv[3] = __uint_as_float(raw[1] & 0xffff0000u);
+            } else {
+                const floatx4 raw = *reinterpret_cast<const floatx4 *>(gp + src);
+                gv[0] = raw[0]; gv[1] = raw[1]; gv[2] = raw[2]; gv[3] = raw[3];
+            }
+            floatx4 m = *reinterpret_cast<const floatx4 *>(mp + src);
+            floatx4 mo, no;
+            for (int q = 0; q < 4; ++q) {
+                const float m1 = mu * m[q] + gv[q];
+                const float n = nesterov ? (mu * m1 + gv[q]) : m1;
+                mo[q] = m1;
+                no[q] = n;
+                acc += static_cast<double>(n) * static_cast<double>(n);
+            }
+            *reinterpret_cast<floatx4 *>(mp + src) = mo;
+            *reinterpret_cast<floatx4 *>(xf + i * g.lp + j) = no;
+        }
+    } else {
+        const int64_t total = (r1 - r0) * cols;
+        for (int64_t t = threadIdx.x; t < total; t += 256) {
+            const int64_t i = r0 + t / cols;
+            const int64_t j = t % cols;
+            const int64_t src = i * cols + j;
+            const float gv = load_val<GradT>(gp, src);
+            const float m1 = mu * mp[src] + gv;
+            const float n = nesterov ? (mu * m1 + gv) : m1;
+            mp[src] = m1;
+            xf[i * g.lp + j] = n;
+            acc += static_cast<double>(n) * static_cast<double>(n);
+        }
+    }
+    const double s = block_sum<256>(acc, sh);
+    if (threadIdx.x == 0) w.partials[blockIdx.x] = s;
+}
+
+// Stage 1, rows > cols: X = N^T.  64 x 64 tiles of W transposed through LDS so
+// both the W-side and the X-side accesses are coalesced.
+template <typename GradT>
+__global__ __launch_bounds__(256) void nesterov_tile_kernel(const MatDesc *__restrict__ descs,
+                                                            Geom g, Work w, float mu,
+                                                            int nesterov, int tiles_c,
+                                                            int blocks_per_mat) {
+    __shared__ float tile[64][65];
+    __shared__ double sh[4];
+    const int64_t e = blockIdx.x / blocks_per_mat;
+    const int64_t t = blockIdx.x % blocks_per_mat;
+    const int64_t i0 = (t / tiles_c) * 64;  // W row
+    const int64_t j0 = (t % tiles_c) * 64;  // W col
+    const MatDesc d = descs[e];
+    const GradT *__restrict__ gp = static_cast<const GradT *>(d.grad);
+    float *__restrict__ mp = d.mom;
+    float *__restrict__ xf = w.xf + e * w.x_stride;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    double acc = 0.0;
+    for (int r = 0; r < 16; ++r) {
+        const int ii = ty + 4 * r;
+        const int64_t i = i0 + ii, j = j0 + tx;
+        float n = 0.0f;
+        if (i < g.rows && j < g.cols) {
+            const int64_t src = i * g.cols + j;
+            const float gv = load_val<GradT>(gp, src);
+            const float m1 = mu * mp[src] + gv;
+            n = nesterov ? (mu * m1 + gv) : m1;
+            mp[src] = m1;
+            acc += static_cast<double>(n) * static_cast<double>(n);
+        }
+        tile[ii][tx] = n;
+    }
+    __syncthreads();
+    // X[j][i] = N[i][j]: X row = W col (j0 + jj), X col = W row (i0 + tx)
+    for (int r = 0; r < 16; ++r) {
+        const int jj = ty + 4 * r;
+        const int64_t xr = j0 + jj, xc = i0 + tx;
+        if (xr < g.cols && xc < g.rows) xf[xr * g.lp + xc] = tile[tx][jj];
+    }
+    const double s = block_sum<256>(acc, sh);
+    if (threadIdx.x == 0) w.partials[blockIdx.x] = s;
+}
+
+// ||N||^2 per matrix from its blocks' partial sums, in a fixed order.
+__global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc *__restrict__ descs,
+                                                            Work w, int blocks_per_mat) {
+    __shared__ double sh[4];
+    const int64_t e = blockIdx.x;
+    double acc = 0.0;
+    for (int b = threadIdx.x; b < blocks_per_mat; b += 256) acc += w.partials[e * blocks_per_mat + b];
+    const double s = block_sum<256>(acc, sh);
+    if (threadIdx.x == 0) {
+        w.nrm2[e] = s;
+        w.call_nrm2[descs[e].call_index] = s;
+        // 1/||N||; an all-zero N gives 0, so X = 0 and the update is decay only.
+        w.inv_norm[e] = (s > 0.0) ? static_cast<float>(1.0 / sqrt(s)) : (s == 0.0 ? 0.0f : __builtin_nanf(""));
+    }
+}
+
+// X_0 = N * inv_norm over the padded sp x lp extent (zeros outside s x l).
+// Writes the fp32 master and, when xb != nullptr, the bf16 operand copy.
+__global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int blocks_per_mat,
+                                                        int rows_per_block, int write_bf16) {
+    const int64_t e = blockIdx.x / blocks_per_mat;
+    const int64_t rb = blockIdx.x % blocks_per_mat;
+    const float inv = w.inv_norm[e];
+    float *__restrict__ xf = w.xf + e * w.x_stride;
+    uint16_t *__restrict__ xb = static_cast<uint16_t *>(w.xb) + e * w.x_stride;
+    const int64_t r0 = rb * rows_per_block;
+    const int64_t r1 = min<int64_t>(g.sp, r0 + rows_per_block);
+    const int64_t cv = g.lp / 4;
+    const int64_t total = (r1 - r0) * cv;
+    for (int64_t t = threadIdx.x; t < total; t += 256) {
+        const int64_t i = r0 + t / cv;
+        const int64_t j = (t % cv) * 4;
+        const int64_t off = i * g.lp + j;
+        floatx4 v = {0.f, 0.f, 0.f, 0.f};
+        if (i < g.s) {
+            const floatx4 n = *reinterpret_cast<const floatx4 *>(xf + off);
+            for (int q = 0; q < 4; ++q) v[q] = (j + q < g.l) ? n[q] * inv : 0.0f;
+        }
+        *reinterpret_cast<floatx4 *>(xf + off) = v;
+        if (write_bf16) {
+            u32x2 p;
+            p[0] = pack_bf16x2(v[0], v[1]);
+            p[1] = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<u32x2 *>(xb + off) = p;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decay + update from a plain rows x cols fp32 X (the test hook's form).
+template <typename ParamT>
+__global__ __launch_bounds__(256) void update_plain_kernel(ParamT *__restrict__ p,
+                                                           const float *__restrict__ x, int64_t n,
+                                                           float dscale, float sscale) {
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
+        const float wv = load_val<ParamT>(p, i);
+        const float r = dscale * wv - sscale * x[i];
+        store_val<ParamT>(p, i, r);
+    }
+}
+
+// Decay + update from the workspace X (s x l, pitch lp, transposed when
+// rows > cols), plus the optional ns_out copy in W's orientation.
+template <typename ParamT>
+__global__ __launch_bounds__(256) void update_from_work_kernel(const MatDesc *__restrict__ descs,
+                                                               Geom g, Work w, float dscale,
+                                                               float sscale, int tiles_c,
+                                                               int blocks_per_mat) {
+    __shared__ float tile[64][65];
+    const int64_t e = blockIdx.x / blocks_per_mat;
+    const int64_t t = blockIdx.x % blocks_per_mat;
+    const int64_t i0 = (t / tiles_c) * 64;  // W row
+    const int64_t j0 = (t % tiles_c) * 64;  // W col
+    const MatDesc d = descs[e];
+    ParamT *__restrict__ pp = static_cast<ParamT *>(d.param);
+    const float *__restrict__ xf = w.xf + e * w.x_stride;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    if (g.transposed) {
+        // X row = W col
+        for (int r = 0; r < 16; ++r) {
+            const int jj = ty + 4 * r;
+            const int64_t xr = j0 + jj, xc = i0 + tx;
+            tile[jj][tx] = (xr < g.cols && xc < g.rows) ? xf[xr * g.lp + xc] : 0.0f;
+        }
+        __syncthreads();
+    }
+    for (int r = 0; r < 16; ++r) {
+        const int ii = ty + 4 * r;
+        const int64_t i = i0 + ii, j = j0 + tx;
+        if (i < g.rows && j < g.cols) {
+            const float xv = g.transposed ? tile[tx][ii] : xf[i * g.lp + j];
+            const int64_t dst = i * g.cols + j;
+            const float wv = load_val<ParamT>(pp, dst);
+            store_val<ParamT>(pp, dst, dscale * wv - sscale * xv);
+            if (d.ns_out) d.ns_out[dst] = xv;
+        }
+    }
+}
+
+// Copy of the workspace X into a plain rows x cols output (muon_ns_only).
+__global__ __launch_bounds__(256) void export_x_kernel(Geom g, const float *__restrict__ xf,
+                                                       float *__restrict__ out, int tiles_c) {
+    __shared__ float tile[64][65];
+    const int64_t i0 = (blockIdx.x / tiles_c) * 64;
+    const int64_t j0 = (blockIdx.x % tiles_c) * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    if (g.transposed) {
+        for (int r = 0; r < 16; ++r) {
+            const int jj = ty + 4 * r;
+            const int64_t xr = j0 + jj, xc = i0 + tx;
+            tile[jj][tx] = (xr < g.cols && xc < g.rows) ? xf[xr * g.lp + xc] : 0.0f;
+        }
+        __syncthreads();
+    }
+    for (int r = 0; r < 16; ++r) {
+        const int ii = ty + 4 * r;
+        const int64_t i = i0 + ii, j = j0 + tx;
+        if (i < g.rows && j < g.cols) out[i * g.cols + j] = g.transposed ? tile[tx][ii] : xf[i * g.lp + j];
+    }
+}
+
+// Copy of a plain fp32 N into the momentum-free first stage (muon_ns_only):
+// X = N in s x l orientation plus the per-block sums of N^2.
+__global__ __launch_bounds__(256) void import_n_kernel(Geom g, const float *__restrict__ n_in, Work w,
+                                                       int tiles_c) {
+    __shared__ float tile[64][65];
+    __shared__ double sh[4];
+    const int64_t i0 = (blockIdx.x / tiles_c) * 64;
+    const int64_t j0 = (blockIdx.x % tiles_c) * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    double acc = 0.0;
+    for (int r = 0; r < 16; ++r) {
+        const int ii = ty + 4 * r;
+        const int64_t i = i0 + ii, j = j0 + tx;
+        float v = 0.0f;
+        if (i < g.rows && j < g.cols) {
+            v = n_in[i * g.cols + j];
+            acc += static_cast<double>(v) * static_cast<double>(v);
+            if (!g.transposed) w.xf[i * g.lp + j] = v;
+        }
+        tile[ii][tx] = v;
+    }
+    if (g.transposed) {
+        __syncthreads();
+        for (int r = 0; r < 16; ++r) {
+            const int jj = ty + 4 * r;
+            const int64_t xr = j0 + jj, xc = i0 + tx;
+            if (xr < g.cols && xc < g.rows) w.xf[xr * g.lp + xc] = tile[tx][jj];
+        }
+    }
+    const double s = block_sum<256>(acc, sh);
+    if (threadIdx.x == 0) w.partials[blockIdx.x] = s;
+}
+
+// ---------------------------------------------------------------------------
+// AdamW over a table of tensors.  Block b processes elements
+// [(b - first_block[k]) * 1024, ...) of tensor k, k found by binary search.
+struct AdamwDesc {
+    float *param;
+    const float *grad;
+    float *m;
+    float *v;
+    int64_t numel;
+    int64_t first_block;
+};
+
+__global__ __launch_bounds__(256) void adamw_kernel(const AdamwDesc *__restrict__ descs, int count,
+                                                    AdamwScalars k) {
+    const int64_t b = blockIdx.x;
+    int lo = 0, hi = count - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (descs[mid].first_block <= b) lo = mid; else hi = mid - 1;
+    }
+    const AdamwDesc d = descs[lo];
+    const int64_t base = (b - d.first_block) * 1024;
+    const bool vec = ((reinterpret_cast<uintptr_t>(d.param) | reinterpret_cast<uintptr_t>(d.grad) |
+                       reinterpret_cast<uintptr_t>(d.m) | reinterpret_cast<uintptr_t>(d.v)) & 15) == 0;
+    const int64_t i = base + threadIdx.x * 4;
+    if (vec && i + 4 <= d.numel) {
+        floatx4 p = *reinterpret_cast<const floatx4 *>(d.param + i);
+        const floatx4 gg = *reinterpret_cast<const floatx4 *>(d.grad + i);
+        floatx4 m = *reinterpret_cast<const floatx4 *>(d.m + i);
+        floatx4 v = *reinterpret_cast<const floatx4 *>(d.v + i);
+        for (int q = 0; q < 4; ++q) {
+            const float p1 = k.decay * p[q];
+            const float m1 = k.beta1 * m[q] + k.one_minus_beta1 * gg[q];
+            const float v1 = k.beta2 * v[q] + (k.one_minus_beta2 * gg[q]) * gg[q];
+            const float mh = __fdiv_rn(m1, k.bias_corr1);
+            const float vh = __fdiv_rn(v1, k.bias_corr2);
+            const float den = __fsqrt_rn(vh) + k.eps;
+            p[q] = p1 - k.lr * __fdiv_rn(mh, den);
+            m[q] = m1;
+            v[q] = v1;
+        }
+        *reinterpret_cast<floatx4 *>(d.param + i) = p;
+        *reinterpret_cast<floatx4 *>(d.m + i) = m;
+        *reinterpret_cast<floatx4 *>(d.v + i) = v;
+    } else {
+        for (int q = 0; q < 4; ++q) {
+            const int64_t ii = i + q;
+            if (ii >= d.numel) break;
+            const float p1 = k.decay * d.param[ii];
+            const float m1 = k.beta1 * d.m[ii] + k.one_minus_beta1 * d.grad[ii];
+            const float gv = d.grad[ii];
+            const float v1 = k.beta2 * d.v[ii] + (k.one_minus_beta2 * gv) * gv;
+            const float mh = __fdiv_rn(m1, k.bias_corr1);
+            const float vh = __fdiv_rn(v1, k.bias_corr2);
+            const float den = __fsqrt_rn(vh) + k.eps;
+            d.param[ii] = p1 - k.lr * __fdiv_rn(mh, den);
+            d.m[ii] = m1;
+            d.v[ii] = v1;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+
+int nesterov_blocks_per_mat(const Geom &g, int *rows_per_block, int *tiles_c) {
+    if (g.transposed) {
+        *tiles_c = static_cast<int>((g.cols + 63) / 64);
+        *rows_per_block = 64;
+        return static_cast<int>(((g.rows + 63) / 64) * *tiles_c);
+    }
+    int64_t rpb = 65536 / g.cols;
+    if (rpb < 1) rpb = 1;
+    if (rpb > g.rows) rpb = g.rows;
+    *rows_per_block = static_cast<int>(rpb);
+    *tiles_c = 0;
+    return static_cast<int>((g.rows + rpb - 1) / rpb);
+}
+
+hipError_t launch_nesterov(const MatDesc *descs, int nmat, const Geom &g, const Work &w, float mu,
+                           int nesterov, int grad_bf16, bool vec_ok, hipStream_t st) {
+    int rpb = 0, tc = 0;
+    const int bpm = nesterov_blocks_per_mat(g, &rpb, &tc);
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(bpm) * nmat)), block(256);
+    const bool vec = vec_ok && (g.cols % 4 == 0) && (g.lp % 4 == 0);
+    if (g.transposed) {
+        if (grad_bf16)
+            hipLaunchKernelGGL(nesterov_tile_kernel<uint16_t>, grid, block, 0, st, descs, g, w, mu, nesterov, tc, bpm);
+        else
+            hipLaunchKernelGGL(nesterov_tile_kernel<float>, grid, block, 0, st, descs, g, w, mu, nesterov, tc, bpm);
+    } else if (vec) {
+        if (grad_bf16)
+            hipLaunchKernelGGL((nesterov_rows_kernel<uint16_t, true>), grid, block, 0, st, descs, g, w, mu, nesterov, rpb, bpm);
+        else
+            hipLaunchKernelGGL((nesterov_rows_kernel<float, true>), grid, block, 0, st, descs, g, w, mu, nesterov, rpb, bpm);
+    } else {
+        if (grad_bf16)
+            hipLaunchKernelGGL((nesterov_rows_kernel<uint16_t, false>), grid, block, 0, st, descs, g, w, mu, nesterov, rpb, bpm);
+        else
+            hipLaunchKernelGGL((nesterov_rows_kernel<float, false>), grid, block, 0, st, descs, g, w, mu, nesterov, rpb, bpm);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_finalize(const MatDesc *descs, int nmat, const Work &w, int blocks_per_mat,
+                                hipStream_t st) {
+    hipLaunchKernelGGL(norm_finalize_kernel, dim3(nmat), dim3(256), 0, st, descs, w, blocks_per_mat);
+    return hipGetLastError();
+}
+
+int import_n_blocks(const Geom &g) {
+    const int tc = static_cast<int>((g.cols + 63) / 64);
+    return static_cast<int>(((g.rows + 63) / 64) * tc);
+}
+
+hipError_t launch_import_n(const float *n_in, const Geom &g, const Work &w, hipStream_t st) {
+    const int tc = static_cast<int>((g.cols + 63) / 64);
+    hipLaunchKernelGGL(import_n_kernel, dim3(import_n_blocks(g)), dim3(256), 0, st, g, n_in, w, tc);
+    return hipGetLastError();
+}
+
+hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, bool write_bf16, hipStream_t st) {
+    int64_t rpb = 65536 / g.lp;
+    if (rpb < 1) rpb = 1;
+    const int bpm = static_cast<int>((g.sp + rpb - 1) / rpb);
+    hipLaunchKernelGGL(normalize_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(bpm) * nmat)), dim3(256), 0,
+                       st, g, w, bpm, static_cast<int>(rpb), write_bf16 ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_update_plain(void *param, int param_bf16, const float *x, int64_t n, float d,
+                               float s, hipStream_t st) {
+    int64_t nb = (n + 255) / 256;
+    if (nb > 65536) nb = 65536;
+    if (nb < 1) nb = 1;
+    if (param_bf16)
+        hipLaunchKernelGGL(update_plain_kernel<uint16_t>, dim3(static_cast<unsigned>(nb)), dim3(256), 0, st,
+                           static_cast<uint16_t *>(param), x, n, d, s);
+    else
+        hipLaunchKernelGGL(update_plain_kernel<float>, dim3(static_cast<unsigned>(nb)), dim3(256), 0, st,
+                           static_cast<float *>(param), x, n, d, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_update_from_work(const MatDesc *descs, int nmat, const Geom &g, const Work &w,
+                                   int param_bf16, float d, float s, hipStream_t st) {
+    const int tc = static_cast<int>((g.cols + 63) / 64);
+    const int bpm = static_cast<int>(((g.rows + 63) / 64) * tc);
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(bpm) * nmat));
+    if (param_bf16)
+        hipLaunchKernelGGL(update_from_work_kernel<uint16_t>, grid, dim3(256), 0, st, descs, g, w, d, s, tc, bpm);
+    else
+        hipLaunchKernelGGL(update_from_work_kernel<float>, grid, dim3(256), 0, st, descs, g, w, d, s, tc, bpm);
+    return hipGetLastError();
+}
+
+hipError_t launch_export_x(const Geom &g, const float *xf, float *out, hipStream_t st) {
+    const int tc = static_cast<int>((g.cols + 63) / 64);
+    const int nb = static_cast<int>(((g.rows + 63) / 64) * tc);
+    hipLaunchKernelGGL(export_x_kernel, dim3(nb), dim3(256), 0, st, g, xf, out, tc);
+    return hipGetLastError();
+}
+
+int64_t adamw_blocks(int64_t numel) { return (numel + 1023) / 1024; }
+
+hipError_t launch_adamw(const void *descs_dev, int count, int64_t total_blocks, const AdamwScalars &k,
+                        hipStream_t st) {
+    // Grid y-splitting is not needed: 2^31-1 blocks cover 2.2e12 elements.
+    hipLaunchKernelGGL(adamw_kernel, dim3(static_cast<unsigned>(total_blocks)), dim3(256), 0, st,
+                       static_cast<const AdamwDesc *>(descs_dev), count, k);
+    return hipGetLastError();
+}
+
+size_t adamw_desc_size() { return sizeof(AdamwDesc); }
+
+void adamw_fill_desc(void *dst, float *param, const float *grad, float *m, float *v, int64_t numel,
+                     int64_t first_block) {
+    AdamwDesc d{param, grad, m, v, numel, first_block};
+    *static_cast<AdamwDesc *>(dst) = d;
+}
+
+}  // namespace muon

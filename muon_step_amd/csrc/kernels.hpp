@@ -1,0 +1,56 @@
+// Internal launchers of the Muon step library (host side of the kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace muon {
+
+struct AdamwScalars {
+    float decay, beta1, beta2, one_minus_beta1, one_minus_beta2, bias_corr1, bias_corr2, lr, eps;
+};
+
+// Newton-Schulz GEMM tile: every padded X dimension is a multiple of this.
+constexpr int kTile = 256;
+
+// ---- elementwise (elementwise.hip)
+int nesterov_blocks_per_mat(const Geom &g, int *rows_per_block, int *tiles_c);
+hipError_t launch_nesterov(const MatDesc *descs, int nmat, const Geom &g, const Work &w, float mu,
+                           int nesterov, int grad_bf16, bool vec_ok, hipStream_t st);
+hipError_t launch_norm_finalize(const MatDesc *descs, int nmat, const Work &w, int blocks_per_mat,
+                                hipStream_t st);
+hipError_t launch_import_n(const float *n_in, const Geom &g, const Work &w, hipStream_t st);
+int import_n_blocks(const Geom &g);
+hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, bool write_bf16, hipStream_t st);
+hipError_t launch_update_plain(void *param, int param_bf16, const float *x, int64_t n, float d,
+                               float s, hipStream_t st);
+hipError_t launch_update_from_work(const MatDesc *descs, int nmat, const Geom &g, const Work &w,
+                                   int param_bf16, float d, float s, hipStream_t st);
+hipError_t launch_export_x(const Geom &g, const float *xf, float *out, hipStream_t st);
+int64_t adamw_blocks(int64_t numel);
+hipError_t launch_adamw(const void *descs_dev, int count, int64_t total_blocks, const AdamwScalars &k,
+                        hipStream_t st);
+size_t adamw_desc_size();
+void adamw_fill_desc(void *dst, float *param, const float *grad, float *m, float *v, int64_t numel,
+                     int64_t first_block);
+
+// ---- Newton-Schulz products (ns_bf16.hip, ns_f32.hip)
+// One Newton-Schulz step on every matrix of the chunk:
+//   A = X X^T (lower-triangle tiles, mirrored), B = b A + c A A (lower-triangle
+//   tiles, mirrored), X <- a X + B X.
+// When `final_update` is set, the last product writes W_t (and ns_out) instead
+// of X:  W <- d W - s (a X + B X).
+struct NsStep {
+    float a, b, c;
+    int final_update;
+    int param_bf16;
+    float dscale, sscale;
+};
+
+// kind: 0 = A = X X^T, 1 = B = bA + cA^2, 2 = X <- aX + BX (or the fused update).
+hipError_t launch_ns_stage(int kind, bool bf16, const MatDesc *descs, int nmat, const Geom &g, const Work &w,
+                           const NsStep &p, hipStream_t st);
+
+}  // namespace muon
