@@ -59,6 +59,9 @@ typedef enum muon_dtype {
 /* Arithmetic of the Newton-Schulz products.
  * MUON_NS_BF16: bf16 MFMA operands, fp32 accumulation, fp32 master copy of X
  *               between iterations (relative Frobenius error vs fp64 ~1e-2).
+ *               Matrices whose smaller side is at most 16 use the fp32
+ *               products instead (too few singular directions for the bf16
+ *               rounding of X to average out; their cost is negligible).
  * MUON_NS_F32:  fp32 MFMA operands and accumulation (error vs fp64 ~1e-6). */
 typedef enum muon_ns_precision { MUON_NS_BF16 = 0, MUON_NS_F32 = 1 } muon_ns_precision;
 

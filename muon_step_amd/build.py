@@ -24,7 +24,9 @@ SOURCES = ["runtime.cpp", "elementwise.hip", "ns_gemm.hip"]
 
 # -ffp-contract=off: every fp32 multiply and add of the bookkeeping rounds once.
 # packed-fp32-ops disabled: no v_pk_{add,mul,fma}_f32 in device code.
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}",
+# -fhip-fp32-correctly-rounded-divide-sqrt: fp32 '/' is the IEEE division sequence.
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+          f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           f"-I{INCLUDE}", "-Wall", "-Wno-unused-function"]
 

@@ -10,7 +10,9 @@
 //                      fp32 master + bf16 operand copy, zero padding.
 //  * update_*        : W_t = (1 - lr wd) W_{t-1} - lr gamma sqrt(max) X (deep-dive
 //                      page step 4-5), fl32 ops in exactly that order.
-//  * adamw           : the AdamW step of embedding/head tensors.
+//  * adamw           : the AdamW step of embedding/head tensors (division is the
+//                      IEEE div_scale/div_fmas/div_fixup sequence the build selects
+//                      with -fhip-fp32-correctly-rounded-divide-sqrt; sqrt_rn below).
 //
 // All float arithmetic here is compiled with -ffp-contract=off so every
 // multiply and add rounds once, matching the fp32 bookkeeping reference.
@@ -28,6 +30,30 @@ template <typename T> __device__ __forceinline__ void store_val(T *p, int64_t i,
 template <> __device__ __forceinline__ void store_val<float>(float *p, int64_t i, float v) { p[i] = v; }
 template <> __device__ __forceinline__ void store_val<uint16_t>(uint16_t *p, int64_t i, float v) {
     p[i] = float_to_bf16_bits(v);
+}
+
+// Correctly rounded fp32 square root.  The hardware estimate v_sqrt_f32
+// (within 1 ulp) is corrected by the signs of the exact FMA residuals
+// x - s*pred(s) and x - s*succ(s): the true root lies below the midpoint
+// (s + pred(s))/2 iff x <= s*pred(s), because no float x falls strictly between
+// s*pred(s) and the square of that midpoint (Markstein's FMA-based square-root
+// rounding; Muller et al., Handbook of Floating-Point Arithmetic, square-root
+// chapter).  Inputs below 2^-96 are scaled by 2^32 so the residuals cannot
+// underflow; zeros, infinities, NaN and negative inputs take the hardware result.
+__device__ __forceinline__ float sqrt_rn(float x) {
+    if (!(x > 0.0f) || x == __builtin_inff()) return __builtin_amdgcn_sqrtf(x);
+    const bool tiny = x < 0x1p-96f;
+    const float xs = tiny ? x * 0x1p32f : x;
+    float s = __builtin_amdgcn_sqrtf(xs);
+    for (int i = 0; i < 2; ++i) {
+        const float dn = __uint_as_float(__float_as_uint(s) - 1u);
+        const float up = __uint_as_float(__float_as_uint(s) + 1u);
+        const float r_dn = __builtin_fmaf(-dn, s, xs);
+        const float r_up = __builtin_fmaf(-up, s, xs);
+        if (r_dn <= 0.0f) s = dn;
+        else if (r_up > 0.0f) s = up;
+    }
+    return tiny ? s * 0x1p-16f : s;
 }
 
 // Deterministic block reduction of one double per thread (fixed tree order).
@@ -345,7 +371,7 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamwDesc *__restrict_
             const float v1 = k.beta2 * v[q] + (k.one_minus_beta2 * gg[q]) * gg[q];
             const float mh = __fdiv_rn(m1, k.bias_corr1);
             const float vh = __fdiv_rn(v1, k.bias_corr2);
-            const float den = __fsqrt_rn(vh) + k.eps;
+            const float den = sqrt_rn(vh) + k.eps;
             p[q] = p1 - k.lr * __fdiv_rn(mh, den);
             m[q] = m1;
             v[q] = v1;
@@ -363,7 +389,7 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamwDesc *__restrict_
             const float v1 = k.beta2 * d.v[ii] + (k.one_minus_beta2 * gv) * gv;
             const float mh = __fdiv_rn(m1, k.bias_corr1);
             const float vh = __fdiv_rn(v1, k.bias_corr2);
-            const float den = __fsqrt_rn(vh) + k.eps;
+            const float den = sqrt_rn(vh) + k.eps;
             d.param[ii] = p1 - k.lr * __fdiv_rn(mh, den);
             d.m[ii] = m1;
             d.v[ii] = v1;

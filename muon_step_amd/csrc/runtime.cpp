@@ -27,6 +27,12 @@ namespace {
 constexpr int64_t kMaxNsSteps = 64;
 constexpr int64_t kMaxDim = int64_t(1) << 31;   // rows, cols
 constexpr int64_t kMaxElems = int64_t(1) << 40; // rows * cols
+// Groups whose smaller side is at most this run the fp32 Newton-Schulz
+// products even when bf16 is requested: with so few singular directions the
+// bf16 rounding of X does not average out, and their cost is negligible.
+constexpr int64_t kThinF32Side = 16;
+
+bool use_bf16(int32_t precision, int64_t s) { return precision == MUON_NS_BF16 && s > kThinF32Side; }
 
 void set_msg(char *msg, size_t cap, const char *fmt, ...) {
     if (!msg || cap == 0) return;
@@ -211,6 +217,7 @@ Geom make_geom(int64_t rows, int64_t cols) {
 
 struct GroupPlan {
     Geom g;
+    bool bf16;                    // bf16 Newton-Schulz products for this group
     int32_t param_dtype, grad_dtype;
     std::vector<int64_t> members; // indices into the caller's list
     int64_t chunk = 0;            // matrices per chunk
@@ -252,7 +259,7 @@ Layout chunk_layout(const Geom &g, bool bf16, int64_t n) {
     return L;
 }
 
-muon_status plan_groups(const muon_matrix *mats, int64_t count, bool bf16, size_t cap, std::vector<GroupPlan> *out,
+muon_status plan_groups(const muon_matrix *mats, int64_t count, int32_t precision, size_t cap, std::vector<GroupPlan> *out,
                         size_t *ws_bytes, size_t *partial_count, int64_t *max_chunk, char *msg, size_t msg_cap) {
     std::map<std::tuple<int64_t, int64_t, int32_t, int32_t>, size_t> index;
     out->clear();
@@ -262,6 +269,7 @@ muon_status plan_groups(const muon_matrix *mats, int64_t count, bool bf16, size_
         if (it == index.end()) {
             GroupPlan gp;
             gp.g = make_geom(mats[i].rows, mats[i].cols);
+            gp.bf16 = use_bf16(precision, gp.g.s);
             gp.param_dtype = mats[i].param_dtype;
             gp.grad_dtype = mats[i].grad_dtype;
             index.emplace(key, out->size());
@@ -275,6 +283,7 @@ muon_status plan_groups(const muon_matrix *mats, int64_t count, bool bf16, size_
     *partial_count = 0;
     *max_chunk = 0;
     for (GroupPlan &gp : *out) {
+        const bool bf16 = gp.bf16;
         const size_t per = per_matrix_bytes(gp.g, bf16);
         int64_t n = static_cast<int64_t>(gp.members.size());
         if (cap) {
@@ -619,7 +628,7 @@ muon_status muon_workspace_bytes(const muon_matrix *mats, int64_t count, const m
     std::vector<GroupPlan> plan;
     size_t ws = 0, parts = 0;
     int64_t mc = 0;
-    s = plan_groups(mats, count, hp->ns_precision == MUON_NS_BF16, 0, &plan, &ws, &parts, &mc, nullptr, 0);
+    s = plan_groups(mats, count, hp->ns_precision, 0, &plan, &ws, &parts, &mc, nullptr, 0);
     if (s != MUON_OK) return s;
     *bytes_out = ws + tabs_bytes(parts, mc) + align_up(static_cast<size_t>(count) * sizeof(double)) +
                  align_up(static_cast<size_t>(count) * sizeof(MatDesc));
@@ -670,11 +679,10 @@ muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count,
     muon_status s = check_step(mats, count, hp, msg, sizeof msg);
     if (s != MUON_OK) return fail(ctx, s, "%s", msg);
     if (count == 0) { ctx->err.clear(); return MUON_OK; }
-    const bool bf16 = hp->ns_precision == MUON_NS_BF16;
     std::vector<GroupPlan> plan;
     size_t ws = 0, parts = 0;
     int64_t max_chunk = 0;
-    s = plan_groups(mats, count, bf16, ctx->cap, &plan, &ws, &parts, &max_chunk, msg, sizeof msg);
+    s = plan_groups(mats, count, hp->ns_precision, ctx->cap, &plan, &ws, &parts, &max_chunk, msg, sizeof msg);
     if (s != MUON_OK) return fail(ctx, s, "%s", msg);
     DeviceGuard guard(ctx->device);
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -702,6 +710,7 @@ muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count,
     const float mu = static_cast<float>(hp->momentum);
     size_t pos = 0;
     for (const GroupPlan &gp : plan) {
+        const bool bf16 = gp.bf16;
         float d = 0.f, sc = 0.f;
         muon_scalars(hp, gp.g.rows, gp.g.cols, &d, &sc);
         const int64_t n_all = static_cast<int64_t>(gp.members.size());
@@ -748,8 +757,8 @@ muon_status muon_ns_only(muon_context *ctx, const float *n_in, float *x_out, int
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(n_in), b0 = reinterpret_cast<uintptr_t>(x_out);
     const uintptr_t nb = static_cast<uintptr_t>(rows * cols) * 4;
     if (a0 < b0 + nb && b0 < a0 + nb) return fail(ctx, MUON_ERR_INVALID_ARGUMENT, "n_in and x_out overlap");
-    const bool bf16 = hp->ns_precision == MUON_NS_BF16;
     const Geom g = make_geom(rows, cols);
+    const bool bf16 = use_bf16(hp->ns_precision, g.s);
     const size_t need = chunk_layout(g, bf16, 1).total;
     if (ctx->cap && need > ctx->cap)
         return fail(ctx, MUON_ERR_OUT_OF_MEMORY, "matrix needs %zu bytes of workspace, above the cap", need);
