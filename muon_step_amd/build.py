@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libmuon_step.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["runtime.cpp", "elementwise.hip", "ns_gemm.hip"]
+SOURCES = ["runtime.cpp", "elementwise.hip", "ns_gemm_bf16.hip", "ns_gemm_f32.hip"]
 
 # -ffp-contract=off: every fp32 multiply and add of the bookkeeping rounds once.
 # packed-fp32-ops disabled: no v_pk_{add,mul,fma}_f32 in device code.

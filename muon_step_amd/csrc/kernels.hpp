@@ -50,7 +50,14 @@ struct NsStep {
 };
 
 // kind: 0 = A = X X^T, 1 = B = bA + cA^2, 2 = X <- aX + BX (or the fused update).
-hipError_t launch_ns_stage(int kind, bool bf16, const MatDesc *descs, int nmat, const Geom &g, const Work &w,
-                           const NsStep &p, hipStream_t st);
+hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const Geom &g, const Work &w,
+                                const NsStep &p, hipStream_t st);
+hipError_t launch_ns_stage_f32(int kind, const MatDesc *descs, int nmat, const Geom &g, const Work &w,
+                               const NsStep &p, hipStream_t st);
+inline hipError_t launch_ns_stage(int kind, bool bf16, const MatDesc *descs, int nmat, const Geom &g,
+                                  const Work &w, const NsStep &p, hipStream_t st) {
+    return bf16 ? launch_ns_stage_bf16(kind, descs, nmat, g, w, p, st)
+                : launch_ns_stage_f32(kind, descs, nmat, g, w, p, st);
+}
 
 }  // namespace muon

@@ -1,4 +1,6 @@
-// Grouped Newton-Schulz products on gfx950 matrix cores.
+// Grouped Newton-Schulz products with fp32 operands (the MUON_NS_F32 path and
+// thin matrices) on gfx950 matrix cores (v_mfma_f32_32x32x2_f32).  The bf16
+// path lives in ns_gemm_bf16.hip.
 //
 // One Newton-Schulz step X <- a X + b (X X^T) X + c (X X^T)^2 X (DeepSeek-V4
 // book ch. 6 §3; the deep-dive page, "Newton-Schulz 迭代") is evaluated as
@@ -27,6 +29,7 @@
 #include "kernels.hpp"
 
 namespace muon {
+namespace f32path {
 
 enum Kind { GRAM = 0, POLY = 1, APPLY = 2 };
 
@@ -37,7 +40,7 @@ constexpr int TILE_BYTES = 256 * 128;           // 256 rows x 128-byte K slab
 constexpr int SMEM_BYTES = 4 * TILE_BYTES;      // 2 stages x (P, Q)
 
 // 16-byte chunk index of (row, chunk) inside a 256 x 8-chunk tile.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
 template <bool BF16> struct ElemT;
 template <> struct ElemT<true> { using T = uint16_t; static constexpr int BK = 64; };
@@ -343,14 +346,11 @@ static hipError_t launch_one(const MatDesc *descs, int nmat, const Geom &g, cons
     return hipGetLastError();
 }
 
-hipError_t launch_ns_stage(int kind, bool bf16, const MatDesc *descs, int nmat, const Geom &g, const Work &w,
-                           const NsStep &p, hipStream_t st) {
-    if (bf16) {
-        if (kind == GRAM) return launch_one<GRAM, true, 0>(descs, nmat, g, w, p, st);
-        if (kind == POLY) return launch_one<POLY, true, 0>(descs, nmat, g, w, p, st);
-        if (p.final_update && p.param_bf16) return launch_one<APPLY, true, 1>(descs, nmat, g, w, p, st);
-        return launch_one<APPLY, true, 0>(descs, nmat, g, w, p, st);
-    }
+}  // namespace f32path
+
+hipError_t launch_ns_stage_f32(int kind, const MatDesc *descs, int nmat, const Geom &g, const Work &w,
+                               const NsStep &p, hipStream_t st) {
+    using namespace f32path;
     if (kind == GRAM) return launch_one<GRAM, false, 0>(descs, nmat, g, w, p, st);
     if (kind == POLY) return launch_one<POLY, false, 0>(descs, nmat, g, w, p, st);
     if (p.final_update && p.param_bf16) return launch_one<APPLY, false, 1>(descs, nmat, g, w, p, st);
