@@ -37,8 +37,21 @@ def log(*a):
 
 
 def gemm_source_sha():
-    with open(os.path.join(ROOT, "muon_step_amd", "csrc", "ns_gemm.hip"), "rb") as f:
+    """Hash of the bf16 Newton-Schulz kernel source the stored traffic counters were taken on."""
+    with open(os.path.join(ROOT, "muon_step_amd", "csrc", "ns_gemm_bf16.hip"), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
+
+
+def copy_calibration():
+    """A plain 1 GiB device-to-device copy: the reference for scaling FETCH_SIZE
+    and WRITE_SIZE (profile this mode with rocprofv3 --pmc)."""
+    import torch
+    x = torch.full((1 << 28,), 1.0, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": x.numel() * 4}), flush=True)
 
 
 def cpu_baseline(rows, cols, count):
@@ -69,7 +82,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--experts", type=int, default=256)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB copy (reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU work of a sharded "
               "run is the same grouped kernel on that GPU's share of matrices); run with --gpus 1.",
