@@ -51,7 +51,7 @@ struct Cfg {
     static constexpr int P_BLOCKS = P_BYTES / 1024 / NWAVES;  // 1 KB DMA blocks per wave and stage
     static constexpr int Q_BLOCKS = Q_BYTES / 1024 / NWAVES;
     static constexpr int LPS = P_BLOCKS + Q_BLOCKS;    // DMA instructions per wave per stage
-    static constexpr int EPI_BYTES = (NWAVES == 8) ? 16384 : 8192;  // epilogue staging per wave
+    static constexpr int EPI_BYTES = 8192;             // epilogue staging per wave and round
     static constexpr int EPI_ROWS = EPI_BYTES / 256;   // rows of 64 fp32 per staging round
 };
 using Big = Cfg<512, 256, 4>;   // GRAM, POLY
@@ -96,26 +96,18 @@ template <class C, int S> __device__ __forceinline__ char *slot_q() {
     }
 }
 
-// Epilogue staging area of wave w (EPI_BYTES, reusing the ring).
-template <class C> __device__ __forceinline__ char *epi_region(int wave) {
-    if constexpr (C::NWAVES == 8) {
-        switch (wave) {
-            case 0: return lds_p0;
-            case 1: return lds_p1;
-            case 2: return lds_p2;
-            case 3: return lds_p3;
-            case 4: return lds_q0;
-            case 5: return lds_q1;
-            case 6: return lds_q2;
-            default: return lds_q3;
-        }
-    } else {
-        switch (wave) {
-            case 0: return lds_p0;
-            case 1: return lds_p1;
-            case 2: return lds_p2;
-            default: return lds_h0;
-        }
+// APPLY stages its epilogue through two areas per wave so the next round's
+// DMA overlaps this round's arithmetic and stores.  The first areas of all
+// waves lie in {p0, p1} and the second in {p2, h0, h1}: disjoint LDS
+// objects, so the compiler's tracking of LDS DMA makes a read of one area
+// wait only for the DMA that filled it.
+__device__ __forceinline__ char *epi_first(int wave) { return (wave < 2 ? lds_p0 : lds_p1) + (wave & 1) * 8192; }
+__device__ __forceinline__ char *epi_second(int wave) {
+    switch (wave) {
+        case 0: return lds_p2;
+        case 1: return lds_p2 + 8192;
+        case 2: return lds_h0;
+        default: return lds_h1;
     }
 }
 
@@ -442,6 +434,181 @@ __global__ __launch_bounds__(Big::NT, 2) void ns_sym_kernel(Geom g, Work w, NsSt
 
 // --------------------------------------------------------------------- a X + B X
 
+// Output block of one wave in the apply epilogue.
+struct ApplyTile {
+    int64_t e;     // matrix
+    int64_t row0;  // first output row
+    int64_t col0;  // first output column
+};
+
+// Row gi's four columns gj .. gj+3 of a X + B X, from the staged fp32 X and
+// the accumulator.
+__device__ __forceinline__ floatx4 apply_value(const floatx16 &acc, const char *reg, int lrow, int lcol, int c4,
+                                               float a) {
+    const floatx4 x = *reinterpret_cast<const floatx4 *>(reg + epi_offset(lrow, lcol >> 2));
+    floatx4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = a * x[q] + acc[4 * c4 + q];
+    return v;
+}
+
+// s_waitcnt vmcnt(N) that no memory access is moved across.
+template <int N> __device__ __forceinline__ void fenced_wait_vmcnt() {
+    asm volatile("" ::: "memory");
+    wait_vmcnt<N>();
+    asm volatile("" ::: "memory");
+}
+
+// Epilogue of an intermediate step: X' = a X + B X is written as fp32 master
+// and bf16 operand copy (zero outside s x l).  Per round of EPI_ROWS rows the
+// wave's fp32 X arrives in a staging area by DMA; every lane reads its
+// accumulator-layout elements, forms a X + B X and writes it back in place;
+// the area is then read row-contiguously (16 lanes per 256-byte row) so the
+// global stores move whole rows.  Two staging areas: the DMA of round h+2 is
+// issued once round h's reads are done, so one round is always in flight.
+// Per round and lane: EPI_ROWS/4 DMA instructions and 2*EPI_ROWS/4 stores,
+// unconditionally; every vector-memory instruction retires in issue order,
+// so the wait before round h allows exactly the instructions issued after
+// round h's DMA: round h-1's stores and round h+1's DMA.
+__device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Pair::MI][Pair::NI], const Geom &g,
+                                                    const Work &w, const NsStep &p, const ApplyTile &t,
+                                                    char *const (&area)[2], int lane) {
+    using C = Pair;
+    constexpr int ROUNDS = C::WM / C::EPI_ROWS;
+    constexpr int DMA_PER_ROUND = C::EPI_ROWS / 4;
+    constexpr int STORES_PER_ROUND = 2 * (C::EPI_ROWS / 4);
+    static_assert(ROUNDS == 4 && C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
+    const float *xin = w.xf + t.e * w.x_stride;
+    float *xf_out = w.xf_next + t.e * w.x_stride;
+    uint16_t *xb_out = static_cast<uint16_t *>(w.xb_next) + t.e * w.x_stride;
+    dma_epi<C>(area[0], reinterpret_cast<const char *>(xin + t.row0 * g.lp + t.col0), g.lp * 4, lane);
+    dma_epi<C>(area[1], reinterpret_cast<const char *>(xin + (t.row0 + C::EPI_ROWS) * g.lp + t.col0), g.lp * 4,
+               lane);
+#pragma unroll
+    for (int h = 0; h < ROUNDS; ++h) {
+        if (h == 0)
+            fenced_wait_vmcnt<DMA_PER_ROUND>();
+        else if (h + 1 < ROUNDS)
+            fenced_wait_vmcnt<STORES_PER_ROUND + DMA_PER_ROUND>();
+        else
+            fenced_wait_vmcnt<STORES_PER_ROUND>();
+        char *reg = area[h & 1];
+        {
+            // All of this lane's reads are issued before any write.
+            const int lrow = lane & 31;
+            floatx4 v[C::NI][4];
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4)
+                    v[ni][c4] = apply_value(acc[h][ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, p.a);
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
+                    *reinterpret_cast<floatx4 *>(reg + epi_offset(lrow, lcol >> 2)) = v[ni][c4];
+                }
+        }
+        wait_lgkm0();  // the wave's in-place writes land before its row-contiguous reads
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r4 = 0; r4 < C::EPI_ROWS / 4; ++r4) {
+            const int lrow = 4 * r4 + (lane >> 4), chunk = lane & 15;
+            floatx4 v = *reinterpret_cast<const floatx4 *>(reg + epi_offset(lrow, chunk));
+            const int64_t gi = t.row0 + C::EPI_ROWS * h + lrow;
+            const int64_t gj = t.col0 + 4 * chunk;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (gi >= g.s || gj + q >= g.l) v[q] = 0.0f;
+            const int64_t idx = gi * g.lp + gj;
+            *reinterpret_cast<floatx4 *>(xf_out + idx) = v;
+            u32x2 pk;
+            pk[0] = pack_bf16x2(v[0], v[1]);
+            pk[1] = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<u32x2 *>(xb_out + idx) = pk;
+        }
+        if (h + 2 < ROUNDS) {
+            wait_lgkm0();  // this round's LDS reads are done before the DMA refills the area
+            asm volatile("" ::: "memory");
+            dma_epi<C>(area[h & 1],
+                       reinterpret_cast<const char *>(xin + (t.row0 + C::EPI_ROWS * (h + 2)) * g.lp + t.col0),
+                       g.lp * 4, lane);
+        }
+    }
+}
+
+// Epilogue of the last step: W <- d W - s_scale X' (and O' = X' when asked),
+// orientation-aware.  One staging area, one round at a time.
+template <int PARAM_BF16>
+__device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Pair::MI][Pair::NI], const MatDesc &d,
+                                                      const Geom &g, const Work &w, const NsStep &p,
+                                                      const ApplyTile &t, char *reg, int lane) {
+    using C = Pair;
+    constexpr int ROUNDS = C::WM / C::EPI_ROWS;
+    static_assert(C::EPI_ROWS == 32, "one 32-row accumulator block per round");
+    const float *xin = w.xf + t.e * w.x_stride;
+    const bool vec_w = !g.transposed && (g.cols % 4 == 0);
+#pragma unroll
+    for (int h = 0; h < ROUNDS; ++h) {
+        dma_epi<C>(reg, reinterpret_cast<const char *>(xin + (t.row0 + C::EPI_ROWS * h) * g.lp + t.col0), g.lp * 4,
+                   lane);
+        fenced_wait_vmcnt<0>();
+        const int lrow = lane & 31;
+        const int64_t gi = t.row0 + C::EPI_ROWS * h + lrow;
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
+                const int64_t gj = t.col0 + lcol;
+                const floatx4 v = apply_value(acc[h][ni], reg, lrow, lcol, c4, p.a);
+                if (gi >= g.s) continue;
+                if (vec_w && gj + 3 < g.l) {
+                    // W row gi, columns gj .. gj+3
+                    const int64_t widx = gi * g.cols + gj;
+                    if (PARAM_BF16) {
+                        uint16_t *pp = static_cast<uint16_t *>(d.param) + widx;
+                        const u32x2 wv = *reinterpret_cast<const u32x2 *>(pp);
+                        u32x2 o;
+                        o[0] = pack_bf16x2(p.dscale * __uint_as_float(wv[0] << 16) - p.sscale * v[0],
+                                           p.dscale * __uint_as_float(wv[0] & 0xffff0000u) - p.sscale * v[1]);
+                        o[1] = pack_bf16x2(p.dscale * __uint_as_float(wv[1] << 16) - p.sscale * v[2],
+                                           p.dscale * __uint_as_float(wv[1] & 0xffff0000u) - p.sscale * v[3]);
+                        *reinterpret_cast<u32x2 *>(pp) = o;
+                    } else {
+                        float *pp = static_cast<float *>(d.param) + widx;
+                        const floatx4 wv = *reinterpret_cast<const floatx4 *>(pp);
+                        floatx4 o;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) o[q] = p.dscale * wv[q] - p.sscale * v[q];
+                        *reinterpret_cast<floatx4 *>(pp) = o;
+                    }
+                    if (d.ns_out) *reinterpret_cast<floatx4 *>(d.ns_out + widx) = v;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (gj + q >= g.l) continue;
+                        const int64_t widx = g.transposed ? ((gj + q) * g.cols + gi) : (gi * g.cols + gj + q);
+                        if (PARAM_BF16) {
+                            uint16_t *pp = static_cast<uint16_t *>(d.param);
+                            const float wv = bf16_bits_to_float(pp[widx]);
+                            pp[widx] = float_to_bf16_bits(p.dscale * wv - p.sscale * v[q]);
+                        } else {
+                            float *pp = static_cast<float *>(d.param);
+                            pp[widx] = p.dscale * pp[widx] - p.sscale * v[q];
+                        }
+                        if (d.ns_out) d.ns_out[widx] = v[q];
+                    }
+                }
+            }
+        if (h + 1 < ROUNDS) {
+            wait_lgkm0();  // this round's LDS reads finish before the next DMA overwrites them
+            asm volatile("" ::: "memory");
+        }
+    }
+}
+
 template <int PARAM_BF16>
 __global__ __launch_bounds__(Pair::NT, 2) void ns_apply_kernel(const MatDesc *__restrict__ descs, Geom g, Work w,
                                                                NsStep p, int64_t tiles_per_mat, int64_t nblocks) {
@@ -474,92 +641,16 @@ __global__ __launch_bounds__(Pair::NT, 2) void ns_apply_kernel(const MatDesc *__
     // Swapped product: acc[mi][ni][4*c4 + q] holds output row
     //   m = wm*WM + mi*32 + lane%32,  columns n = wn*WN + ni*32 + 8*c4 + 4*(lane/32) + q, q = 0..3
     // The fp32 X of the aX term is staged through LDS in rounds of EPI_ROWS
-    // rows, each wave loading its own slice with the DMA (all of it in flight
-    // at once), then read back in the accumulator layout.
-    const float *xin = w.xf + e * w.x_stride;
-    const int64_t row0 = static_cast<int64_t>(ti) * C::BM + wm * C::WM;  // first output row of this wave
-    const int64_t col0 = static_cast<int64_t>(tj) * C::BN + wn * C::WN;  // first output column
-    char *reg = epi_region<C>(wave);
+    // rows, each wave loading its own slice with the DMA, then read back in
+    // the accumulator layout.
+    const ApplyTile t_{e, static_cast<int64_t>(ti) * C::BM + wm * C::WM, static_cast<int64_t>(tj) * C::BN + wn * C::WN};
+    char *const area[2] = {epi_first(wave), epi_second(wave)};
     wait_lgkm0();
     stage_barrier();  // every wave is done with the operand ring
-    // The descriptor (param, ns_out) is needed only by the fused update.
-    MatDesc d{};
-    if (p.final_update) d = descs[e];
-    const bool vec_w = !g.transposed && (g.cols % 4 == 0);
-    constexpr int ROUNDS = C::WM / C::EPI_ROWS;
-    constexpr int MI_PER_ROUND = C::EPI_ROWS / 32;
-#pragma unroll
-    for (int h = 0; h < ROUNDS; ++h) {
-        dma_epi<C>(reg, reinterpret_cast<const char *>(xin + (row0 + C::EPI_ROWS * h) * g.lp + col0), g.lp * 4, lane);
-        wait_vmcnt<0>();
-#pragma unroll
-        for (int mh = 0; mh < MI_PER_ROUND; ++mh) {
-            const int mi = MI_PER_ROUND * h + mh;
-            const int lrow = mh * 32 + (lane & 31);
-            const int64_t gi = row0 + C::EPI_ROWS * h + lrow;
-#pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-#pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) {
-                    const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
-                    const int64_t gj = col0 + lcol;
-                    const floatx4 x = *reinterpret_cast<const floatx4 *>(reg + epi_offset(lrow, lcol >> 2));
-                    floatx4 v;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = p.a * x[q] + acc[mi][ni][4 * c4 + q];
-                    if (!p.final_update) {
-                        const int64_t idx = gi * g.lp + gj;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (gi >= g.s || gj + q >= g.l) v[q] = 0.0f;
-                        *reinterpret_cast<floatx4 *>(w.xf_next + e * w.x_stride + idx) = v;
-                        u32x2 pk;
-                        pk[0] = pack_bf16x2(v[0], v[1]);
-                        pk[1] = pack_bf16x2(v[2], v[3]);
-                        *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(w.xb_next) + e * w.x_stride + idx) = pk;
-                    } else if (gi < g.s) {
-                        if (vec_w && gj + 3 < g.l) {
-                            // W row gi, columns gj .. gj+3
-                            const int64_t widx = gi * g.cols + gj;
-                            if (PARAM_BF16) {
-                                uint16_t *pp = static_cast<uint16_t *>(d.param) + widx;
-                                const u32x2 wv = *reinterpret_cast<const u32x2 *>(pp);
-                                u32x2 o;
-                                o[0] = pack_bf16x2(p.dscale * __uint_as_float(wv[0] << 16) - p.sscale * v[0],
-                                                   p.dscale * __uint_as_float(wv[0] & 0xffff0000u) - p.sscale * v[1]);
-                                o[1] = pack_bf16x2(p.dscale * __uint_as_float(wv[1] << 16) - p.sscale * v[2],
-                                                   p.dscale * __uint_as_float(wv[1] & 0xffff0000u) - p.sscale * v[3]);
-                                *reinterpret_cast<u32x2 *>(pp) = o;
-                            } else {
-                                float *pp = static_cast<float *>(d.param) + widx;
-                                const floatx4 wv = *reinterpret_cast<const floatx4 *>(pp);
-                                floatx4 o;
-#pragma unroll
-                                for (int q = 0; q < 4; ++q) o[q] = p.dscale * wv[q] - p.sscale * v[q];
-                                *reinterpret_cast<floatx4 *>(pp) = o;
-                            }
-                            if (d.ns_out) *reinterpret_cast<floatx4 *>(d.ns_out + widx) = v;
-                        } else {
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                if (gj + q >= g.l) continue;
-                                const int64_t widx = g.transposed ? ((gj + q) * g.cols + gi) : (gi * g.cols + gj + q);
-                                if (PARAM_BF16) {
-                                    uint16_t *pp = static_cast<uint16_t *>(d.param);
-                                    const float wv = bf16_bits_to_float(pp[widx]);
-                                    pp[widx] = float_to_bf16_bits(p.dscale * wv - p.sscale * v[q]);
-                                } else {
-                                    float *pp = static_cast<float *>(d.param);
-                                    pp[widx] = p.dscale * pp[widx] - p.sscale * v[q];
-                                }
-                                if (d.ns_out) d.ns_out[widx] = v[q];
-                            }
-                        }
-                    }
-                }
-        }
-        if (h + 1 < ROUNDS) wait_lgkm0();  // this round's LDS reads finish before the next DMA overwrites them
-    }
+    if (p.final_update)
+        apply_epilogue_update<PARAM_BF16>(acc, descs[e], g, w, p, t_, area[0], lane);
+    else
+        apply_epilogue_next(acc, g, w, p, t_, area, lane);
 }
 
 }  // namespace bf16path
