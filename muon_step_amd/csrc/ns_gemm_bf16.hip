@@ -538,70 +538,104 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Pair::
     }
 }
 
+// W <- d W - s_scale X' for X' row gi, columns gj .. gj+3 (W row-major with
+// the orientation of X'), and O' = X' when asked.  VEC: the four W elements
+// are 4-aligned and inside the matrix.
+template <int PARAM_BF16>
+__device__ __forceinline__ void update_row4(const MatDesc &d, const Geom &g, const NsStep &p, int64_t gi, int64_t gj,
+                                            const floatx4 &v) {
+    if (!g.transposed && (g.cols % 4 == 0) && gj + 3 < g.l) {
+        const int64_t widx = gi * g.cols + gj;
+        if (PARAM_BF16) {
+            uint16_t *pp = static_cast<uint16_t *>(d.param) + widx;
+            const u32x2 wv = *reinterpret_cast<const u32x2 *>(pp);
+            u32x2 o;
+            o[0] = pack_bf16x2(p.dscale * __uint_as_float(wv[0] << 16) - p.sscale * v[0],
+                               p.dscale * __uint_as_float(wv[0] & 0xffff0000u) - p.sscale * v[1]);
+            o[1] = pack_bf16x2(p.dscale * __uint_as_float(wv[1] << 16) - p.sscale * v[2],
+                               p.dscale * __uint_as_float(wv[1] & 0xffff0000u) - p.sscale * v[3]);
+            *reinterpret_cast<u32x2 *>(pp) = o;
+        } else {
+            float *pp = static_cast<float *>(d.param) + widx;
+            const floatx4 wv = *reinterpret_cast<const floatx4 *>(pp);
+            floatx4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = p.dscale * wv[q] - p.sscale * v[q];
+            *reinterpret_cast<floatx4 *>(pp) = o;
+        }
+        if (d.ns_out) *reinterpret_cast<floatx4 *>(d.ns_out + widx) = v;
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (gj + q >= g.l) continue;
+        const int64_t widx = g.transposed ? ((gj + q) * g.cols + gi) : (gi * g.cols + gj + q);
+        if (PARAM_BF16) {
+            uint16_t *pp = static_cast<uint16_t *>(d.param);
+            const float wv = bf16_bits_to_float(pp[widx]);
+            pp[widx] = float_to_bf16_bits(p.dscale * wv - p.sscale * v[q]);
+        } else {
+            float *pp = static_cast<float *>(d.param);
+            pp[widx] = p.dscale * pp[widx] - p.sscale * v[q];
+        }
+        if (d.ns_out) d.ns_out[widx] = v[q];
+    }
+}
+
 // Epilogue of the last step: W <- d W - s_scale X' (and O' = X' when asked),
-// orientation-aware.  One staging area, one round at a time.
+// orientation-aware.  One staging area, one round at a time.  For W in the
+// orientation of X', the values are written back to the staging area and
+// the update walks whole rows (16 lanes per 64-column row); for transposed W
+// the accumulator layout already puts 32 consecutive X' rows, i.e. 32
+// consecutive elements of a W row, in consecutive lanes.
 template <int PARAM_BF16>
 __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Pair::MI][Pair::NI], const MatDesc &d,
                                                       const Geom &g, const Work &w, const NsStep &p,
                                                       const ApplyTile &t, char *reg, int lane) {
     using C = Pair;
     constexpr int ROUNDS = C::WM / C::EPI_ROWS;
-    static_assert(C::EPI_ROWS == 32, "one 32-row accumulator block per round");
+    static_assert(C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
     const float *xin = w.xf + t.e * w.x_stride;
-    const bool vec_w = !g.transposed && (g.cols % 4 == 0);
 #pragma unroll
     for (int h = 0; h < ROUNDS; ++h) {
         dma_epi<C>(reg, reinterpret_cast<const char *>(xin + (t.row0 + C::EPI_ROWS * h) * g.lp + t.col0), g.lp * 4,
                    lane);
         fenced_wait_vmcnt<0>();
         const int lrow = lane & 31;
-        const int64_t gi = t.row0 + C::EPI_ROWS * h + lrow;
+        if (g.transposed) {
+            const int64_t gi = t.row0 + C::EPI_ROWS * h + lrow;
 #pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni)
+            for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
-                const int64_t gj = t.col0 + lcol;
-                const floatx4 v = apply_value(acc[h][ni], reg, lrow, lcol, c4, p.a);
-                if (gi >= g.s) continue;
-                if (vec_w && gj + 3 < g.l) {
-                    // W row gi, columns gj .. gj+3
-                    const int64_t widx = gi * g.cols + gj;
-                    if (PARAM_BF16) {
-                        uint16_t *pp = static_cast<uint16_t *>(d.param) + widx;
-                        const u32x2 wv = *reinterpret_cast<const u32x2 *>(pp);
-                        u32x2 o;
-                        o[0] = pack_bf16x2(p.dscale * __uint_as_float(wv[0] << 16) - p.sscale * v[0],
-                                           p.dscale * __uint_as_float(wv[0] & 0xffff0000u) - p.sscale * v[1]);
-                        o[1] = pack_bf16x2(p.dscale * __uint_as_float(wv[1] << 16) - p.sscale * v[2],
-                                           p.dscale * __uint_as_float(wv[1] & 0xffff0000u) - p.sscale * v[3]);
-                        *reinterpret_cast<u32x2 *>(pp) = o;
-                    } else {
-                        float *pp = static_cast<float *>(d.param) + widx;
-                        const floatx4 wv = *reinterpret_cast<const floatx4 *>(pp);
-                        floatx4 o;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) o[q] = p.dscale * wv[q] - p.sscale * v[q];
-                        *reinterpret_cast<floatx4 *>(pp) = o;
-                    }
-                    if (d.ns_out) *reinterpret_cast<floatx4 *>(d.ns_out + widx) = v;
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        if (gj + q >= g.l) continue;
-                        const int64_t widx = g.transposed ? ((gj + q) * g.cols + gi) : (gi * g.cols + gj + q);
-                        if (PARAM_BF16) {
-                            uint16_t *pp = static_cast<uint16_t *>(d.param);
-                            const float wv = bf16_bits_to_float(pp[widx]);
-                            pp[widx] = float_to_bf16_bits(p.dscale * wv - p.sscale * v[q]);
-                        } else {
-                            float *pp = static_cast<float *>(d.param);
-                            pp[widx] = p.dscale * pp[widx] - p.sscale * v[q];
-                        }
-                        if (d.ns_out) d.ns_out[widx] = v[q];
-                    }
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
+                    const floatx4 v = apply_value(acc[h][ni], reg, lrow, lcol, c4, p.a);
+                    if (gi < g.s) update_row4<PARAM_BF16>(d, g, p, gi, t.col0 + lcol, v);
                 }
+        } else {
+            floatx4 v[C::NI][4];
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4)
+                    v[ni][c4] = apply_value(acc[h][ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, p.a);
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
+                    *reinterpret_cast<floatx4 *>(reg + epi_offset(lrow, lcol >> 2)) = v[ni][c4];
+                }
+            wait_lgkm0();  // the wave's in-place writes land before its row-contiguous reads
+            asm volatile("" ::: "memory");
+#pragma unroll 4
+            for (int r4 = 0; r4 < C::EPI_ROWS / 4; ++r4) {
+                const int rrow = 4 * r4 + (lane >> 4), chunk = lane & 15;
+                const floatx4 x = *reinterpret_cast<const floatx4 *>(reg + epi_offset(rrow, chunk));
+                const int64_t gi = t.row0 + C::EPI_ROWS * h + rrow;
+                if (gi < g.s) update_row4<PARAM_BF16>(d, g, p, gi, t.col0 + 4 * chunk, x);
             }
+        }
         if (h + 1 < ROUNDS) {
             wait_lgkm0();  // this round's LDS reads finish before the next DMA overwrites them
             asm volatile("" ::: "memory");
