@@ -1,0 +1,235 @@
+"""GPU parity at the workloads' full sizes.
+
+The 256 x 2048x7168 expert batch runs exactly as bench.py times it (one call
+over all matrices, inputs from the same seeded device generator); sampled
+experts are checked against the oracle one by one and every expert against
+properties that hold at any size.  The dense-block, aspect-ratio and 16B-MoE
+workloads run at their real shapes; matrices whose oracle finishes in seconds
+are compared with it, the rest through the same properties.  AdamW on the
+102400x2048 tensors is compared bit for bit on sampled elements.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import BF16_TOL, assert_bitexact, rel_fro, say, scale_of, to_np
+
+pytestmark = pytest.mark.gpu
+
+LR, MU, WD, GAMMA = 0.02, 0.95, 0.1, 0.2
+
+
+@pytest.fixture(scope="module")
+def torch_mod():
+    import torch
+    assert torch.cuda.is_available()
+    return torch
+
+
+def _ms():
+    import muon_step_amd as ms
+    return ms
+
+
+def _ns_norm_band(torch, w0, w1, rows, cols):
+    """||O'_t||_F / sqrt(min(n, m)) recovered from the update W1 = fl(d W0) - fl(s X).
+
+    The ratio is the root-mean-square singular value of O'_t.  The two
+    refining steps leave every singular value close to 1, so the ratio must
+    sit inside [0.95, 1.05]; a matrix that was skipped, zeroed or mixed up
+    with another lands far outside."""
+    d, s = oracle.muon_scalars_f32(LR, WD, GAMMA, rows, cols)
+    x = (float(d) * w0.float() - w1.float()) / float(s)
+    return float(torch.linalg.vector_norm(x.double())) / math.sqrt(min(rows, cols))
+
+
+def _check_sampled(mats_dev, idx, w0_host, g_host, m0_host, rows, cols):
+    """Oracle step for one matrix; compares momentum, ||N||^2, O_t and W_t."""
+    p, g, m, o = mats_dev
+    ref = oracle.muon_step(w0_host, g_host, m0_host, lr=LR, momentum=MU, weight_decay=WD, gamma=GAMMA,
+                           param_bf16=True)
+    assert_bitexact(to_np(m), ref["m_new"], f"momentum of matrix {idx}")
+    x_gpu = to_np(o)
+    err = rel_fro(x_gpu * scale_of(rows, cols, GAMMA), ref["o"])
+    say(f"  matrix {idx} {rows}x{cols}: O rel err {err:.3e}")
+    assert err <= BF16_TOL
+    w_ref = oracle.apply_update_f32(w0_host, x_gpu, LR, WD, GAMMA, True)
+    assert_bitexact(to_np(p), w_ref, f"param of matrix {idx}")
+    return ref
+
+
+def test_moe_expert_batch_full_size(torch_mod):
+    """256 x 2048x7168 bf16 in one call, as timed by bench.py; experts 0, 97 and 255
+    against the oracle, all 256 against the norm band."""
+    torch = torch_mod
+    ms = _ms()
+    rows, cols, count = 2048, 7168, 256
+    say("moe 256 x 2048x7168: generating inputs on the device")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    grads = synth.spectral_grad_torch(rows, cols, count, gen, "cuda")
+    params = (torch.randn(count, rows, cols, generator=gen, device="cuda") * synth.gen.PARAM_STD).to(torch.bfloat16)
+    moms = torch.zeros(count, rows, cols, dtype=torch.float32, device="cuda")
+    w0 = params.clone()
+    sampled = (0, 97, 255)
+    outs = {e: torch.empty(rows, cols, dtype=torch.float32, device="cuda") for e in sampled}
+    mats = [ms.matrix(params[e], grads[e], moms[e], outs.get(e)) for e in range(count)]
+    ctx = ms.Context(0)
+    try:
+        say("moe 256 x 2048x7168: one Muon step")
+        ctx.muon_step(mats, ms.make_hparams(lr=LR, momentum=MU, weight_decay=WD, gamma=GAMMA))
+        torch.cuda.synchronize()
+        norms = ctx.muon_last_norms(count)
+    finally:
+        ctx.close()
+    for e in sampled:
+        say(f"moe expert {e}: oracle")
+        g_host = to_np(grads[e])
+        m0 = np.zeros((rows, cols), np.float32)
+        ref = _check_sampled((params[e], grads[e], moms[e], outs[e]), e, to_np(w0[e]), g_host, m0, rows, cols)
+        nrm2 = float(np.sum(ref["n"].astype(np.float64) ** 2))
+        assert abs(norms[e] - nrm2) <= 1e-12 * nrm2
+    bands = [_ns_norm_band(torch, w0[e], params[e], rows, cols) for e in range(count)]
+    say(f"moe norm band over 256 experts: [{min(bands):.4f}, {max(bands):.4f}]")
+    assert all(0.95 < b < 1.05 for b in bands)
+    assert bool(torch.isfinite(params.float()).all())
+    # every expert's momentum is exactly (1 + 0) * G: zero prior momentum
+    assert bool((moms == grads.float()).all())
+
+
+def _run_workload_sampled(torch, specs, seed, oracle_names, cap_bytes=0):
+    """One call over the workload's matrices (device-generated spectral grads, params
+    N(0, 0.02), prefilled momentum where the spec says so); the named matrices
+    against the oracle, every matrix against the norm band and W = update(W0, O')."""
+    ms = _ms()
+    by_shape = {}
+    for i, sp in enumerate(specs):
+        by_shape.setdefault((sp.rows, sp.cols), []).append(i)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    grads, prior = [None] * len(specs), [None] * len(specs)
+    for (rows, cols), ids in by_shape.items():
+        g = synth.spectral_grad_torch(rows, cols, len(ids), gen, "cuda")
+        pf = [i for i in ids if specs[i].prefill_momentum]
+        gp = synth.spectral_grad_torch(rows, cols, len(pf), gen, "cuda") if pf else None
+        for k, i in enumerate(ids):
+            grads[i] = g[k]
+        for k, i in enumerate(pf):
+            prior[i] = gp[k]
+    params, moms, outs, w0 = [], [], [], []
+    for i, sp in enumerate(specs):
+        p = (torch.randn(sp.rows, sp.cols, generator=gen, device="cuda") * synth.gen.PARAM_STD).to(torch.bfloat16)
+        m = prior[i].float() if prior[i] is not None else torch.zeros(sp.rows, sp.cols, device="cuda")
+        params.append(p)
+        w0.append(p.clone())
+        moms.append(m)
+        outs.append(torch.empty(sp.rows, sp.cols, dtype=torch.float32, device="cuda"))
+    m0 = [to_np(m) if sp.name in oracle_names else None for sp, m in zip(specs, moms)]
+    mats = [ms.matrix(params[i], grads[i], moms[i], outs[i]) for i in range(len(specs))]
+    ctx = ms.Context(0, cap_bytes)
+    try:
+        ctx.muon_step(mats, ms.make_hparams(lr=LR, momentum=MU, weight_decay=WD, gamma=GAMMA))
+        torch.cuda.synchronize()
+    finally:
+        ctx.close()
+    for i, sp in enumerate(specs):
+        band = _ns_norm_band(torch, w0[i], params[i], sp.rows, sp.cols)
+        x = to_np(outs[i])
+        w_ref = oracle.apply_update_f32(to_np(w0[i]), x, LR, WD, GAMMA, True)
+        assert_bitexact(to_np(params[i]), w_ref, f"param of {sp.name}")
+        line = f"  {sp.name} {sp.rows}x{sp.cols}: norm band {band:.4f}"
+        if sp.name in oracle_names:
+            ref = oracle.muon_step(to_np(w0[i]), to_np(grads[i]), m0[i], lr=LR, momentum=MU, weight_decay=WD,
+                                   gamma=GAMMA, param_bf16=True)
+            assert_bitexact(to_np(moms[i]), ref["m_new"], f"momentum of {sp.name}")
+            err = rel_fro(x * scale_of(sp.rows, sp.cols, GAMMA), ref["o"])
+            line += f", O rel err {err:.3e}"
+            assert err <= BF16_TOL
+        say(line)
+        assert 0.95 < band < 1.05
+
+
+def test_aspect_ratio_set_full_size(torch_mod):
+    """1024x16384, 16384x1024, 7168^2 and 512x32768, momentum pre-filled; the three
+    thin shapes against the oracle, the square one against the properties."""
+    wl = synth.WORKLOADS["aspect_stress_bf16"]
+    say("aspect-ratio set")
+    _run_workload_sampled(torch_mod, list(wl.matrices), wl.base_seed, {"wide", "tall", "very_wide"})
+
+
+def test_dense_block_full_size(torch_mod):
+    """Four 4096^2, two 4096x14336 and one 14336x4096 in one call; one 4096^2 against
+    the oracle, every matrix against the properties."""
+    wl = synth.WORKLOADS["dense_block_bf16"]
+    say("dense block")
+    _run_workload_sampled(torch_mod, list(wl.matrices), wl.base_seed, {"attn0"})
+
+
+def test_moe16b_full_step(torch_mod):
+    """The full 16B-MoE optimizer step in two calls: Muon over all 27 x (4 + 192)
+    matrices (workspace capped at 24 GiB, so each shape group runs in chunks) and
+    AdamW over the 102400x2048 embedding and head.  One matrix per shape against
+    the oracle, 96 spread over the list against the norm band, AdamW bit-exact on
+    8192 sampled elements of each tensor (first, last and random positions)."""
+    torch = torch_mod
+    ms = _ms()
+    wl = synth.WORKLOADS["moe16b_full_step"]
+    specs = list(wl.matrices)
+    say(f"16B-MoE step: {len(specs)} Muon matrices, generating inputs on the device")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.base_seed)
+    by_shape = {}
+    for i, sp in enumerate(specs):
+        by_shape.setdefault((sp.rows, sp.cols), []).append(i)
+    grads = [None] * len(specs)
+    for (rows, cols), ids in by_shape.items():
+        g = synth.spectral_grad_torch(rows, cols, len(ids), gen, "cuda")
+        for k, i in enumerate(ids):
+            grads[i] = g[k]
+    params = [(torch.randn(sp.rows, sp.cols, generator=gen, device="cuda") * synth.gen.PARAM_STD).to(torch.bfloat16)
+              for sp in specs]
+    moms = [torch.zeros(sp.rows, sp.cols, device="cuda") for sp in specs]
+    checked = {ids[len(ids) // 2] for ids in by_shape.values()}
+    banded = set(range(0, len(specs), len(specs) // 96)) | checked
+    w0 = {i: params[i].clone() for i in banded}
+    outs = {i: torch.empty(specs[i].rows, specs[i].cols, device="cuda") for i in checked}
+    mats = [ms.matrix(params[i], grads[i], moms[i], outs.get(i)) for i in range(len(specs))]
+    numel = 102400 * 2048
+    ad = []
+    for name, n in wl.adamw:
+        assert n == numel
+        p = torch.randn(n, generator=gen, device="cuda") * synth.gen.PARAM_STD
+        g = torch.randn(n, generator=gen, device="cuda")
+        ad.append((name, p, g, torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")))
+    rs = np.random.default_rng(wl.base_seed)
+    pick = np.unique(np.concatenate([np.arange(2048), np.arange(numel - 2048, numel),
+                                     rs.integers(0, numel, 4096)]))
+    pick_t = torch.from_numpy(pick).cuda()
+    ad_before = [(name, to_np(p[pick_t]), to_np(g[pick_t])) for name, p, g, _, _ in ad]
+    ahp = ms.adamw_hparams(lr=LR, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=WD, step=1)
+    ctx = ms.Context(0, 24 << 30)
+    try:
+        say("16B-MoE step: Muon over every matrix, then AdamW")
+        ctx.muon_step(mats, ms.make_hparams(lr=LR, momentum=MU, weight_decay=WD, gamma=GAMMA))
+        ctx.muon_adamw_step([ms.adamw_tensor(p, g, m, v) for _, p, g, m, v in ad], ahp)
+        torch.cuda.synchronize()
+    finally:
+        ctx.close()
+    for i in sorted(checked):
+        sp = specs[i]
+        _check_sampled((params[i], grads[i], moms[i], outs[i]), sp.name, to_np(w0[i]), to_np(grads[i]),
+                       np.zeros((sp.rows, sp.cols), np.float32), sp.rows, sp.cols)
+    bands = [_ns_norm_band(torch, w0[i], params[i], specs[i].rows, specs[i].cols) for i in sorted(banded)]
+    say(f"16B-MoE norm band over {len(bands)} matrices: [{min(bands):.4f}, {max(bands):.4f}]")
+    assert all(0.95 < b < 1.05 for b in bands)
+    for (name, p0, g0), (_, p, _, m, v) in zip(ad_before, ad):
+        z = np.zeros_like(p0)
+        p_ref, m_ref, v_ref = oracle.adamw_step_f32(p0, g0, z, z, LR, 0.9, 0.95, 1e-8, WD, 1)
+        assert_bitexact(to_np(p[pick_t]), p_ref, f"AdamW {name} param")
+        assert_bitexact(to_np(m[pick_t]), m_ref, f"AdamW {name} exp_avg")
+        assert_bitexact(to_np(v[pick_t]), v_ref, f"AdamW {name} exp_avg_sq")
+        say(f"  AdamW {name}: {len(pick)} sampled elements bit-exact")
