@@ -47,11 +47,16 @@ struct Geom {
 //   af + e*a_stride       fp32 A = X X^T (sp x sp, lower-triangle tiles)
 //   ab + e*a_stride       A as MFMA operand (bf16 or fp32, both triangles)
 //   bb + e*a_stride       B = bA + cA^2 as MFMA operand (both triangles)
+// Newton-Schulz workspace of one chunk of same-shape matrices.  fp32 path: X
+// in xf / xf_next (fp32).  bf16 path: X as a pair of bf16 arrays, hi in
+// xb / xb_next (ping-pong: it is the operand every tile of the B X product
+// reads) and lo in xl (updated in place), xf == xf_next == nullptr.
 struct Work {
     float *xf;
     float *xf_next;
     void *xb;
     void *xb_next;
+    void *xl;
     float *af;
     void *ab;
     void *bb;
@@ -79,6 +84,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     p[0] = static_cast<__bf16>(lo);
     p[1] = static_cast<__bf16>(hi);
     return __builtin_bit_cast(uint32_t, p);
+}
+
+// A float kept as two bfloat16: hi = bf16(x), lo = bf16(x - hi).  x - hi is
+// exact in fp32 (hi is within half a bf16 ulp of x), so hi + lo carries x to
+// about 2^-17 relative, and hi + lo is exact in fp32.
+__device__ __forceinline__ void split_bf16(float x, uint16_t *hi, uint16_t *lo) {
+    const uint16_t h = float_to_bf16_bits(x);
+    *hi = h;
+    *lo = float_to_bf16_bits(x - bf16_bits_to_float(h));
+}
+__device__ __forceinline__ float join_bf16(uint16_t hi, uint16_t lo) {
+    return bf16_bits_to_float(hi) + bf16_bits_to_float(lo);
+}
+// Four consecutive values: hi and lo as packed bf16 pairs.
+__device__ __forceinline__ void split_bf16x4(const floatx4 &v, u32x2 *hi, u32x2 *lo) {
+    u32x2 h, l;
+    h[0] = pack_bf16x2(v[0], v[1]);
+    h[1] = pack_bf16x2(v[2], v[3]);
+    l[0] = pack_bf16x2(v[0] - __uint_as_float(h[0] << 16), v[1] - __uint_as_float(h[0] & 0xffff0000u));
+    l[1] = pack_bf16x2(v[2] - __uint_as_float(h[1] << 16), v[3] - __uint_as_float(h[1] & 0xffff0000u));
+    *hi = h;
+    *lo = l;
+}
+__device__ __forceinline__ floatx4 join_bf16x4(const u32x2 &h, const u32x2 &l) {
+    floatx4 v;
+    v[0] = __uint_as_float(h[0] << 16) + __uint_as_float(l[0] << 16);
+    v[1] = __uint_as_float(h[0] & 0xffff0000u) + __uint_as_float(l[0] & 0xffff0000u);
+    v[2] = __uint_as_float(h[1] << 16) + __uint_as_float(l[1] << 16);
+    v[3] = __uint_as_float(h[1] & 0xffff0000u) + __uint_as_float(l[1] & 0xffff0000u);
+    return v;
 }
 
 // Blocks whose ids the hardware spreads round-robin over the 8 XCDs are

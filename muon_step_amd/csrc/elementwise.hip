@@ -3,11 +3,12 @@
 //  * nesterov_*      : M_t = mu M_{t-1} + G_t, N_t = mu M_t + G_t (deep-dive page,
 //                      "V4 的完整更新公式" steps 1-2; DeepSeek-V4 book ch. 6 §5),
 //                      N_t written into the X workspace in the s x l orientation
-//                      (transposed through LDS when rows > cols), per-block sums of
-//                      N_t^2 in fp64.
+//                      (transposed through LDS when rows > cols) as fp32, or on the
+//                      bf16 path as the bf16 pair (hi, lo), per-block sums of N_t^2
+//                      in fp64.
 //  * norm_finalize   : ||N_t||_F^2 per matrix from the block sums, fixed order.
 //  * normalize       : X_0 = N_t / ||N_t||_F (book ch. 6 §5, normalisation line),
-//                      fp32 master + bf16 operand copy, zero padding.
+//                      fp32 (fp32 path) or the bf16 pair (hi, lo), zero padding.
 //  * update_*        : W_t = (1 - lr wd) W_{t-1} - lr gamma sqrt(max) X (deep-dive
 //                      page step 4-5), fl32 ops in exactly that order.
 //  * adamw           : the AdamW step of embedding/head tensors (division is the
@@ -70,6 +71,22 @@ __device__ __forceinline__ double block_sum(double v, double *sh) {
     return r;  // valid in thread 0
 }
 
+// Read access to one matrix's workspace X: fp32, or the bf16 pair (hi, lo).
+struct XView {
+    const float *xf;  // fp32 path; nullptr on the bf16 path
+    const uint16_t *xh;
+    const uint16_t *xl;
+    __device__ __forceinline__ float at(int64_t i) const { return xf ? xf[i] : join_bf16(xh[i], xl[i]); }
+};
+
+// N into the first matrix's workspace slot (fp32, or the bf16 pair in (xb_next, xl)).
+__device__ __forceinline__ void store_n(const Work &w, int64_t i, float v) {
+    if (w.xf)
+        w.xf[i] = v;
+    else
+        split_bf16(v, static_cast<uint16_t *>(w.xb_next) + i, static_cast<uint16_t *>(w.xl) + i);
+}
+
 // ---------------------------------------------------------------------------
 // Stage 1, rows <= cols: X = N (no transpose).  Block (e, rb) handles rows
 // [rb*rows_per_block, ...) of matrix e.
@@ -84,7 +101,9 @@ __global__ __launch_bounds__(256) void nesterov_rows_kernel(const MatDesc *__res
     const MatDesc d = descs[e];
     const GradT *__restrict__ gp = static_cast<const GradT *>(d.grad);
     float *__restrict__ mp = d.mom;
-    float *__restrict__ xf = w.xf + e * w.x_stride;
+    float *__restrict__ xf = w.xf ? w.xf + e * w.x_stride : nullptr;  // fp32 path
+    uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb_next) + e * w.x_stride;  // bf16 path
+    uint16_t *__restrict__ xl = static_cast<uint16_t *>(w.xl) + e * w.x_stride;
     const int64_t r0 = rb * rows_per_block;
     const int64_t r1 = min<int64_t>(g.rows, r0 + rows_per_block);
     const int64_t cols = g.cols;
@@ -117,7 +136,15 @@ __global__ __launch_bounds__(256) void nesterov_rows_kernel(const MatDesc *__res
                 acc += static_cast<double>(n) * static_cast<double>(n);
             }
             *reinterpret_cast<floatx4 *>(mp + src) = mo;
-            *reinterpret_cast<floatx4 *>(xf + i * g.lp + j) = no;
+            const int64_t dst = i * g.lp + j;
+            if (xf) {
+                *reinterpret_cast<floatx4 *>(xf + dst) = no;
+            } else {
+                u32x2 h, l;
+                split_bf16x4(no, &h, &l);
+                *reinterpret_cast<u32x2 *>(xh + dst) = h;
+                *reinterpret_cast<u32x2 *>(xl + dst) = l;
+            }
         }
     } else {
         const int64_t total = (r1 - r0) * cols;
@@ -129,7 +156,10 @@ __global__ __launch_bounds__(256) void nesterov_rows_kernel(const MatDesc *__res
             const float m1 = mu * mp[src] + gv;
             const float n = nesterov ? (mu * m1 + gv) : m1;
             mp[src] = m1;
-            xf[i * g.lp + j] = n;
+            if (xf)
+                xf[i * g.lp + j] = n;
+            else
+                split_bf16(n, xh + i * g.lp + j, xl + i * g.lp + j);
             acc += static_cast<double>(n) * static_cast<double>(n);
         }
     }
@@ -153,7 +183,9 @@ __global__ __launch_bounds__(256) void nesterov_tile_kernel(const MatDesc *__res
     const MatDesc d = descs[e];
     const GradT *__restrict__ gp = static_cast<const GradT *>(d.grad);
     float *__restrict__ mp = d.mom;
-    float *__restrict__ xf = w.xf + e * w.x_stride;
+    float *__restrict__ xf = w.xf ? w.xf + e * w.x_stride : nullptr;  // fp32 path
+    uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb_next) + e * w.x_stride;  // bf16 path
+    uint16_t *__restrict__ xl = static_cast<uint16_t *>(w.xl) + e * w.x_stride;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     double acc = 0.0;
     for (int r = 0; r < 16; ++r) {
@@ -175,7 +207,12 @@ __global__ __launch_bounds__(256) void nesterov_tile_kernel(const MatDesc *__res
     for (int r = 0; r < 16; ++r) {
         const int jj = ty + 4 * r;
         const int64_t xr = j0 + jj, xc = i0 + tx;
-        if (xr < g.cols && xc < g.rows) xf[xr * g.lp + xc] = tile[tx][jj];
+        if (xr < g.cols && xc < g.rows) {
+            if (xf)
+                xf[xr * g.lp + xc] = tile[tx][jj];
+            else
+                split_bf16(tile[tx][jj], xh + xr * g.lp + xc, xl + xr * g.lp + xc);
+        }
     }
     const double s = block_sum<256>(acc, sh);
     if (threadIdx.x == 0) w.partials[blockIdx.x] = s;
@@ -198,14 +235,17 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc *__res
 }
 
 // X_0 = N * inv_norm over the padded sp x lp extent (zeros outside s x l).
-// Writes the fp32 master and, when xb != nullptr, the bf16 operand copy.
-__global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int blocks_per_mat,
-                                                        int rows_per_block, int write_bf16) {
+// fp32 path: in place in xf.  bf16 path: N as (hi, lo) in (xb_next, xl), X_0
+// as (hi, lo) in (xb, xl), lo in place.
+__global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int blocks_per_mat, int rows_per_block) {
     const int64_t e = blockIdx.x / blocks_per_mat;
     const int64_t rb = blockIdx.x % blocks_per_mat;
     const float inv = w.inv_norm[e];
-    float *__restrict__ xf = w.xf + e * w.x_stride;
-    uint16_t *__restrict__ xb = static_cast<uint16_t *>(w.xb) + e * w.x_stride;
+    const bool split = w.xf == nullptr;
+    float *__restrict__ xf = split ? nullptr : w.xf + e * w.x_stride;
+    const uint16_t *__restrict__ nh = static_cast<const uint16_t *>(w.xb_next) + e * w.x_stride;
+    uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb) + e * w.x_stride;
+    uint16_t *__restrict__ xl = static_cast<uint16_t *>(w.xl) + e * w.x_stride;
     const int64_t r0 = rb * rows_per_block;
     const int64_t r1 = min<int64_t>(g.sp, r0 + rows_per_block);
     const int64_t cv = g.lp / 4;
@@ -216,15 +256,22 @@ __global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int bloc
         const int64_t off = i * g.lp + j;
         floatx4 v = {0.f, 0.f, 0.f, 0.f};
         if (i < g.s) {
-            const floatx4 n = *reinterpret_cast<const floatx4 *>(xf + off);
+            floatx4 n;
+            if (split) {
+                // entries past column l of the N pair are never written: mask them
+                n = join_bf16x4(*reinterpret_cast<const u32x2 *>(nh + off), *reinterpret_cast<const u32x2 *>(xl + off));
+            } else {
+                n = *reinterpret_cast<const floatx4 *>(xf + off);
+            }
             for (int q = 0; q < 4; ++q) v[q] = (j + q < g.l) ? n[q] * inv : 0.0f;
         }
-        *reinterpret_cast<floatx4 *>(xf + off) = v;
-        if (write_bf16) {
-            u32x2 p;
-            p[0] = pack_bf16x2(v[0], v[1]);
-            p[1] = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<u32x2 *>(xb + off) = p;
+        if (split) {
+            u32x2 h, l;
+            split_bf16x4(v, &h, &l);
+            *reinterpret_cast<u32x2 *>(xh + off) = h;
+            *reinterpret_cast<u32x2 *>(xl + off) = l;
+        } else {
+            *reinterpret_cast<floatx4 *>(xf + off) = v;
         }
     }
 }
@@ -256,14 +303,15 @@ __global__ __launch_bounds__(256) void update_from_work_kernel(const MatDesc *__
     const int64_t j0 = (t % tiles_c) * 64;  // W col
     const MatDesc d = descs[e];
     ParamT *__restrict__ pp = static_cast<ParamT *>(d.param);
-    const float *__restrict__ xf = w.xf + e * w.x_stride;
+    const XView xv_{w.xf ? w.xf + e * w.x_stride : nullptr, static_cast<const uint16_t *>(w.xb) + e * w.x_stride,
+                    static_cast<const uint16_t *>(w.xl) + e * w.x_stride};
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     if (g.transposed) {
         // X row = W col
         for (int r = 0; r < 16; ++r) {
             const int jj = ty + 4 * r;
             const int64_t xr = j0 + jj, xc = i0 + tx;
-            tile[jj][tx] = (xr < g.cols && xc < g.rows) ? xf[xr * g.lp + xc] : 0.0f;
+            tile[jj][tx] = (xr < g.cols && xc < g.rows) ? xv_.at(xr * g.lp + xc) : 0.0f;
         }
         __syncthreads();
     }
@@ -271,7 +319,7 @@ __global__ __launch_bounds__(256) void update_from_work_kernel(const MatDesc *__
         const int ii = ty + 4 * r;
         const int64_t i = i0 + ii, j = j0 + tx;
         if (i < g.rows && j < g.cols) {
-            const float xv = g.transposed ? tile[tx][ii] : xf[i * g.lp + j];
+            const float xv = g.transposed ? tile[tx][ii] : xv_.at(i * g.lp + j);
             const int64_t dst = i * g.cols + j;
             const float wv = load_val<ParamT>(pp, dst);
             store_val<ParamT>(pp, dst, dscale * wv - sscale * xv);
@@ -281,8 +329,7 @@ __global__ __launch_bounds__(256) void update_from_work_kernel(const MatDesc *__
 }
 
 // Copy of the workspace X into a plain rows x cols output (muon_ns_only).
-__global__ __launch_bounds__(256) void export_x_kernel(Geom g, const float *__restrict__ xf,
-                                                       float *__restrict__ out, int tiles_c) {
+__global__ __launch_bounds__(256) void export_x_kernel(Geom g, XView x, float *__restrict__ out, int tiles_c) {
     __shared__ float tile[64][65];
     const int64_t i0 = (blockIdx.x / tiles_c) * 64;
     const int64_t j0 = (blockIdx.x % tiles_c) * 64;
@@ -291,14 +338,14 @@ __global__ __launch_bounds__(256) void export_x_kernel(Geom g, const float *__re
         for (int r = 0; r < 16; ++r) {
             const int jj = ty + 4 * r;
             const int64_t xr = j0 + jj, xc = i0 + tx;
-            tile[jj][tx] = (xr < g.cols && xc < g.rows) ? xf[xr * g.lp + xc] : 0.0f;
+            tile[jj][tx] = (xr < g.cols && xc < g.rows) ? x.at(xr * g.lp + xc) : 0.0f;
         }
         __syncthreads();
     }
     for (int r = 0; r < 16; ++r) {
         const int ii = ty + 4 * r;
         const int64_t i = i0 + ii, j = j0 + tx;
-        if (i < g.rows && j < g.cols) out[i * g.cols + j] = g.transposed ? tile[tx][ii] : xf[i * g.lp + j];
+        if (i < g.rows && j < g.cols) out[i * g.cols + j] = g.transposed ? tile[tx][ii] : x.at(i * g.lp + j);
     }
 }
 
@@ -319,7 +366,7 @@ __global__ __launch_bounds__(256) void import_n_kernel(Geom g, const float *__re
         if (i < g.rows && j < g.cols) {
             v = n_in[i * g.cols + j];
             acc += static_cast<double>(v) * static_cast<double>(v);
-            if (!g.transposed) w.xf[i * g.lp + j] = v;
+            if (!g.transposed) store_n(w, i * g.lp + j, v);
         }
         tile[ii][tx] = v;
     }
@@ -328,7 +375,7 @@ __global__ __launch_bounds__(256) void import_n_kernel(Geom g, const float *__re
         for (int r = 0; r < 16; ++r) {
             const int jj = ty + 4 * r;
             const int64_t xr = j0 + jj, xc = i0 + tx;
-            if (xr < g.cols && xc < g.rows) w.xf[xr * g.lp + xc] = tile[tx][jj];
+            if (xr < g.cols && xc < g.rows) store_n(w, xr * g.lp + xc, tile[tx][jj]);
         }
     }
     const double s = block_sum<256>(acc, sh);
@@ -456,12 +503,12 @@ hipError_t launch_import_n(const float *n_in, const Geom &g, const Work &w, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, bool write_bf16, hipStream_t st) {
+hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, hipStream_t st) {
     int64_t rpb = 65536 / g.lp;
     if (rpb < 1) rpb = 1;
     const int bpm = static_cast<int>((g.sp + rpb - 1) / rpb);
     hipLaunchKernelGGL(normalize_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(bpm) * nmat)), dim3(256), 0,
-                       st, g, w, bpm, static_cast<int>(rpb), write_bf16 ? 1 : 0);
+                       st, g, w, bpm, static_cast<int>(rpb));
     return hipGetLastError();
 }
 
@@ -491,10 +538,11 @@ hipError_t launch_update_from_work(const MatDesc *descs, int nmat, const Geom &g
     return hipGetLastError();
 }
 
-hipError_t launch_export_x(const Geom &g, const float *xf, float *out, hipStream_t st) {
+hipError_t launch_export_x(const Geom &g, const Work &w, float *out, hipStream_t st) {
     const int tc = static_cast<int>((g.cols + 63) / 64);
     const int nb = static_cast<int>(((g.rows + 63) / 64) * tc);
-    hipLaunchKernelGGL(export_x_kernel, dim3(nb), dim3(256), 0, st, g, xf, out, tc);
+    const XView x{w.xf, static_cast<const uint16_t *>(w.xb), static_cast<const uint16_t *>(w.xl)};
+    hipLaunchKernelGGL(export_x_kernel, dim3(nb), dim3(256), 0, st, g, x, out, tc);
     return hipGetLastError();
 }
 

@@ -23,12 +23,12 @@ hipError_t launch_norm_finalize(const MatDesc *descs, int nmat, const Work &w, i
                                 hipStream_t st);
 hipError_t launch_import_n(const float *n_in, const Geom &g, const Work &w, hipStream_t st);
 int import_n_blocks(const Geom &g);
-hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, bool write_bf16, hipStream_t st);
+hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, hipStream_t st);
 hipError_t launch_update_plain(void *param, int param_bf16, const float *x, int64_t n, float d,
                                float s, hipStream_t st);
 hipError_t launch_update_from_work(const MatDesc *descs, int nmat, const Geom &g, const Work &w,
                                    int param_bf16, float d, float s, hipStream_t st);
-hipError_t launch_export_x(const Geom &g, const float *xf, float *out, hipStream_t st);
+hipError_t launch_export_x(const Geom &g, const Work &w, float *out, hipStream_t st);
 int64_t adamw_blocks(int64_t numel);
 hipError_t launch_adamw(const void *descs_dev, int count, int64_t total_blocks, const AdamwScalars &k,
                         hipStream_t st);

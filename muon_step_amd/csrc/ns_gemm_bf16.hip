@@ -36,11 +36,12 @@ namespace bf16path {
 
 enum Kind { GRAM = 0, POLY = 1, APPLY = 2 };
 
-template <int NT_, int BN_, int STAGES_>
+template <int NT_, int BN_, int STAGES_, int WN_ = 64>
 struct Cfg {
     static constexpr int NT = NT_, NWAVES = NT / 64;
+    static constexpr int WAVES_PER_SIMD = NWAVES / 4;  // one workgroup per CU
     static constexpr int BM = 256, BN = BN_;
-    static constexpr int WM = 128, WN = 64, MI = WM / 32, NI = WN / 32;
+    static constexpr int WM = 128, WN = WN_, MI = WM / 32, NI = WN / 32;
     static constexpr int WAVES_N = BN / WN, WAVES_M = BM / WM;
     static_assert(WAVES_N * WAVES_M == NWAVES, "wave grid");
     static constexpr int STAGES = STAGES_;
@@ -260,11 +261,13 @@ struct Src {
 
 // One pipeline step: stage kt (slot S) is consumed while up to WAIT/LPS later
 // stages may still be in flight.  With ISSUE the DMA of stage kt+STAGES-1
-// refills the slot stage kt-1 used, which every wave finished before this
-// barrier.
+// refills the slot stage kt-1 used: each wave waits for its own reads of that
+// slot to return (lgkmcnt 0) before the barrier, so after it no read of the
+// slot is outstanding, wherever the compiler placed the products.
 template <class C, int KIND, int S, int WAIT, bool ISSUE>
 __device__ __forceinline__ void pipeline_step(floatx16 (&acc)[C::MI][C::NI], const Src &src, int kt, int wave,
                                               int wm, int wn, int lane) {
+    wait_lgkm0();
     wait_vmcnt<WAIT>();
     stage_barrier();
     if constexpr (ISSUE)
@@ -348,6 +351,23 @@ __device__ __forceinline__ void dma_epi(char *dst, const char *src, int64_t ld, 
     }
 }
 
+// DMA of EPI_ROWS rows x 64 bf16 (128 bytes per row, X_hi or X_lo) starting
+// at `src` (row pitch ld bytes) into a staging area: instructions of 8 rows
+// each; lane i carries row i/8, chunk i%8 stored at chunk (i%8) ^ ((row/2)%8),
+// so 16 consecutive rows reading one chunk touch 16 distinct bank groups.
+template <class C>
+__device__ __forceinline__ void dma_bf16_rows(char *dst, const char *src, int64_t ld, int lane) {
+#pragma unroll
+    for (int t = 0; t < C::EPI_ROWS / 8; ++t) {
+        const int row = 8 * t + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        __builtin_amdgcn_global_load_lds(src + row * ld + chunk * 16, (lds_void_t *)(dst + t * 1024), 16, 0, 0);
+    }
+}
+__device__ __forceinline__ int pair_offset(int row, int col) {
+    return row * 128 + ((((col >> 3) ^ ((row >> 1) & 7))) << 4) + ((col & 7) << 1);
+}
+
 __device__ __forceinline__ void tri_decode(int64_t t, int *ti, int *tj) {
     int i = static_cast<int>((sqrt(8.0 * static_cast<double>(t) + 1.0) - 1.0) * 0.5);
     while (static_cast<int64_t>(i + 1) * (i + 2) / 2 <= t) ++i;
@@ -358,10 +378,9 @@ __device__ __forceinline__ void tri_decode(int64_t t, int *ti, int *tj) {
 
 // ------------------------------------------------------------------------ A, B
 
-template <int KIND>
-__global__ __launch_bounds__(Big::NT, 2) void ns_sym_kernel(Geom g, Work w, NsStep p, int64_t tiles_per_mat,
-                                                            int64_t nblocks) {
-    using C = Big;
+template <class C, int KIND>
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void ns_sym_kernel(Geom g, Work w, NsStep p,
+                                                                          int64_t tiles_per_mat, int64_t nblocks) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int64_t L = xcd_swizzle(blockIdx.x, nblocks);
@@ -441,15 +460,43 @@ struct ApplyTile {
     int64_t col0;  // first output column
 };
 
-// Row gi's four columns gj .. gj+3 of a X + B X, from the staged fp32 X and
-// the accumulator.
+// Row lrow's four columns lcol .. lcol+3 of a X + B X, with X = X_hi + X_lo
+// staged in `reg` (X_hi rows in the first PAIR_HALF bytes, X_lo rows after).
+constexpr int PAIR_HALF = 4096;
 __device__ __forceinline__ floatx4 apply_value(const floatx16 &acc, const char *reg, int lrow, int lcol, int c4,
                                                float a) {
-    const floatx4 x = *reinterpret_cast<const floatx4 *>(reg + epi_offset(lrow, lcol >> 2));
+    const u32x2 h = *reinterpret_cast<const u32x2 *>(reg + pair_offset(lrow, lcol));
+    const u32x2 l = *reinterpret_cast<const u32x2 *>(reg + PAIR_HALF + pair_offset(lrow, lcol));
+    const floatx4 x = join_bf16x4(h, l);
     floatx4 v;
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = a * x[q] + acc[4 * c4 + q];
     return v;
+}
+
+// The wave's 32 x 64 block of values, computed in the accumulator layout from
+// the X pair staged in `reg`, rewritten in place as fp32 rows (256 bytes each)
+// for the row-contiguous pass.  All of the lane's reads precede its writes, and
+// one wave's LDS accesses execute in order, so no value is overwritten before
+// it is read.
+template <class C>
+__device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char *reg, float a, int lane) {
+    const int lrow = lane & 31;
+    floatx4 v[C::NI][4];
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) v[ni][c4] = apply_value(accm[ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, a);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
+            *reinterpret_cast<floatx4 *>(reg + epi_offset(lrow, lcol >> 2)) = v[ni][c4];
+        }
+    wait_lgkm0();  // the wave's writes land before its row-contiguous reads
+    asm volatile("" ::: "memory");
 }
 
 // s_waitcnt vmcnt(N) that no memory access is moved across.
@@ -459,31 +506,38 @@ template <int N> __device__ __forceinline__ void fenced_wait_vmcnt() {
     asm volatile("" ::: "memory");
 }
 
-// Epilogue of an intermediate step: X' = a X + B X is written as fp32 master
-// and bf16 operand copy (zero outside s x l).  Per round of EPI_ROWS rows the
-// wave's fp32 X arrives in a staging area by DMA; every lane reads its
-// accumulator-layout elements, forms a X + B X and writes it back in place;
-// the area is then read row-contiguously (16 lanes per 256-byte row) so the
-// global stores move whole rows.  Two staging areas: the DMA of round h+2 is
-// issued once round h's reads are done, so one round is always in flight.
-// Per round and lane: EPI_ROWS/4 DMA instructions and 2*EPI_ROWS/4 stores,
-// unconditionally; every vector-memory instruction retires in issue order,
-// so the wait before round h allows exactly the instructions issued after
-// round h's DMA: round h-1's stores and round h+1's DMA.
+// Epilogue of an intermediate step: X' = a X + B X is written as the bf16 pair
+// (X'_hi to xb_next, X'_lo to xl in place; zero outside s x l).  Per round of
+// EPI_ROWS rows the wave's X_hi and X_lo rows arrive in a staging area by DMA;
+// the values are formed in the accumulator layout and rewritten there as fp32
+// rows, then read row-contiguously (16 lanes per row) so the stores move whole
+// rows.  Two staging areas: the DMA of round h+2 is issued once round h's
+// reads are done, so one round is always in flight.  Per round and lane:
+// 2*EPI_ROWS/8 DMA instructions and 2*EPI_ROWS/4 stores, unconditionally;
+// every vector-memory instruction retires in issue order, so the wait before
+// round h allows exactly the instructions issued after round h's DMA: round
+// h-1's stores and round h+1's DMA.
 __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Pair::MI][Pair::NI], const Geom &g,
                                                     const Work &w, const NsStep &p, const ApplyTile &t,
                                                     char *const (&area)[2], int lane) {
     using C = Pair;
     constexpr int ROUNDS = C::WM / C::EPI_ROWS;
-    constexpr int DMA_PER_ROUND = C::EPI_ROWS / 4;
+    constexpr int DMA_PER_ROUND = 2 * (C::EPI_ROWS / 8);
     constexpr int STORES_PER_ROUND = 2 * (C::EPI_ROWS / 4);
     static_assert(ROUNDS == 4 && C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
-    const float *xin = w.xf + t.e * w.x_stride;
-    float *xf_out = w.xf_next + t.e * w.x_stride;
-    uint16_t *xb_out = static_cast<uint16_t *>(w.xb_next) + t.e * w.x_stride;
-    dma_epi<C>(area[0], reinterpret_cast<const char *>(xin + t.row0 * g.lp + t.col0), g.lp * 4, lane);
-    dma_epi<C>(area[1], reinterpret_cast<const char *>(xin + (t.row0 + C::EPI_ROWS) * g.lp + t.col0), g.lp * 4,
-               lane);
+    static_assert(C::EPI_ROWS * 128 == PAIR_HALF, "X_hi and X_lo rows fill one staging area");
+    uint16_t *xl = static_cast<uint16_t *>(w.xl) + t.e * w.x_stride;
+    uint16_t *xh_out = static_cast<uint16_t *>(w.xb_next) + t.e * w.x_stride;
+    const int64_t first = t.row0 * g.lp + t.col0;
+    const char *hi_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xb) + t.e * w.x_stride + first);
+    const char *lo_in = reinterpret_cast<const char *>(xl + first);
+    const int64_t ld = g.lp * 2;
+    auto dma_round = [&](char *dst, int h) {
+        dma_bf16_rows<C>(dst, hi_in + C::EPI_ROWS * h * ld, ld, lane);
+        dma_bf16_rows<C>(dst + PAIR_HALF, lo_in + C::EPI_ROWS * h * ld, ld, lane);
+    };
+    dma_round(area[0], 0);
+    dma_round(area[1], 1);
 #pragma unroll
     for (int h = 0; h < ROUNDS; ++h) {
         if (h == 0)
@@ -493,25 +547,7 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Pair::
         else
             fenced_wait_vmcnt<STORES_PER_ROUND>();
         char *reg = area[h & 1];
-        {
-            // All of this lane's reads are issued before any write.
-            const int lrow = lane & 31;
-            floatx4 v[C::NI][4];
-#pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-#pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4)
-                    v[ni][c4] = apply_value(acc[h][ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, p.a);
-#pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-#pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) {
-                    const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
-                    *reinterpret_cast<floatx4 *>(reg + epi_offset(lrow, lcol >> 2)) = v[ni][c4];
-                }
-        }
-        wait_lgkm0();  // the wave's in-place writes land before its row-contiguous reads
-        asm volatile("" ::: "memory");
+        stage_values<C>(acc[h], reg, p.a, lane);
 #pragma unroll
         for (int r4 = 0; r4 < C::EPI_ROWS / 4; ++r4) {
             const int lrow = 4 * r4 + (lane >> 4), chunk = lane & 15;
@@ -522,18 +558,15 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Pair::
             for (int q = 0; q < 4; ++q)
                 if (gi >= g.s || gj + q >= g.l) v[q] = 0.0f;
             const int64_t idx = gi * g.lp + gj;
-            *reinterpret_cast<floatx4 *>(xf_out + idx) = v;
-            u32x2 pk;
-            pk[0] = pack_bf16x2(v[0], v[1]);
-            pk[1] = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<u32x2 *>(xb_out + idx) = pk;
+            u32x2 hi, lo;
+            split_bf16x4(v, &hi, &lo);
+            *reinterpret_cast<u32x2 *>(xh_out + idx) = hi;
+            *reinterpret_cast<u32x2 *>(xl + idx) = lo;
         }
         if (h + 2 < ROUNDS) {
             wait_lgkm0();  // this round's LDS reads are done before the DMA refills the area
             asm volatile("" ::: "memory");
-            dma_epi<C>(area[h & 1],
-                       reinterpret_cast<const char *>(xin + (t.row0 + C::EPI_ROWS * (h + 2)) * g.lp + t.col0),
-                       g.lp * 4, lane);
+            dma_round(area[h & 1], h + 2);
         }
     }
 }
@@ -584,10 +617,10 @@ __device__ __forceinline__ void update_row4(const MatDesc &d, const Geom &g, con
 
 // Epilogue of the last step: W <- d W - s_scale X' (and O' = X' when asked),
 // orientation-aware.  One staging area, one round at a time.  For W in the
-// orientation of X', the values are written back to the staging area and
-// the update walks whole rows (16 lanes per 64-column row); for transposed W
-// the accumulator layout already puts 32 consecutive X' rows, i.e. 32
-// consecutive elements of a W row, in consecutive lanes.
+// orientation of X' the values are rewritten as fp32 rows and the update walks
+// whole rows (16 lanes per 64-column row); for transposed W the accumulator
+// layout already puts 32 consecutive X' rows, i.e. 32 consecutive elements of
+// a W row, in consecutive lanes.
 template <int PARAM_BF16>
 __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Pair::MI][Pair::NI], const MatDesc &d,
                                                       const Geom &g, const Work &w, const NsStep &p,
@@ -595,11 +628,14 @@ __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Pair
     using C = Pair;
     constexpr int ROUNDS = C::WM / C::EPI_ROWS;
     static_assert(C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
-    const float *xin = w.xf + t.e * w.x_stride;
+    const int64_t first = t.row0 * g.lp + t.col0;
+    const char *hi_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xb) + t.e * w.x_stride + first);
+    const char *lo_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xl) + t.e * w.x_stride + first);
+    const int64_t ld = g.lp * 2;
 #pragma unroll
     for (int h = 0; h < ROUNDS; ++h) {
-        dma_epi<C>(reg, reinterpret_cast<const char *>(xin + (t.row0 + C::EPI_ROWS * h) * g.lp + t.col0), g.lp * 4,
-                   lane);
+        dma_bf16_rows<C>(reg, hi_in + C::EPI_ROWS * h * ld, ld, lane);
+        dma_bf16_rows<C>(reg + PAIR_HALF, lo_in + C::EPI_ROWS * h * ld, ld, lane);
         fenced_wait_vmcnt<0>();
         const int lrow = lane & 31;
         if (g.transposed) {
@@ -613,21 +649,7 @@ __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Pair
                     if (gi < g.s) update_row4<PARAM_BF16>(d, g, p, gi, t.col0 + lcol, v);
                 }
         } else {
-            floatx4 v[C::NI][4];
-#pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-#pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4)
-                    v[ni][c4] = apply_value(acc[h][ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, p.a);
-#pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-#pragma unroll
-                for (int c4 = 0; c4 < 4; ++c4) {
-                    const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
-                    *reinterpret_cast<floatx4 *>(reg + epi_offset(lrow, lcol >> 2)) = v[ni][c4];
-                }
-            wait_lgkm0();  // the wave's in-place writes land before its row-contiguous reads
-            asm volatile("" ::: "memory");
+            stage_values<C>(acc[h], reg, p.a, lane);
 #pragma unroll 4
             for (int r4 = 0; r4 < C::EPI_ROWS / 4; ++r4) {
                 const int rrow = 4 * r4 + (lane >> 4), chunk = lane & 15;
@@ -693,15 +715,15 @@ hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const 
                                 const NsStep &p, hipStream_t st) {
     using namespace bf16path;
     if (kind == GRAM || kind == POLY) {
-        const int64_t nt = g.sp / Big::BM;
+        using C = Big;
+        const int64_t nt = g.sp / C::BM;
         const int64_t tiles = nt * (nt + 1) / 2;
         const int64_t nblocks = tiles * nmat;
+        const dim3 grid(static_cast<unsigned>(nblocks)), block(C::NT);
         if (kind == GRAM)
-            hipLaunchKernelGGL(ns_sym_kernel<GRAM>, dim3(static_cast<unsigned>(nblocks)), dim3(Big::NT), 0, st, g, w,
-                               p, tiles, nblocks);
+            ns_sym_kernel<C, GRAM><<<grid, block, 0, st>>>(g, w, p, tiles, nblocks);
         else
-            hipLaunchKernelGGL(ns_sym_kernel<POLY>, dim3(static_cast<unsigned>(nblocks)), dim3(Big::NT), 0, st, g, w,
-                               p, tiles, nblocks);
+            ns_sym_kernel<C, POLY><<<grid, block, 0, st>>>(g, w, p, tiles, nblocks);
         return hipGetLastError();
     }
     const int64_t tiles = (g.sp / Pair::BM) * (g.lp / Pair::BN);

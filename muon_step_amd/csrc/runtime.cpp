@@ -233,24 +233,28 @@ size_t per_matrix_bytes(const Geom &g, bool bf16) {
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-    size_t xf0, xf1, xb0, xb1, af, ab, bb, total;
+    size_t xf0, xf1, xb0, xb1, xl, af, ab, bb, total;
+    bool has_xf;
 };
 
 Layout chunk_layout(const Geom &g, bool bf16, int64_t n) {
     const size_t x = static_cast<size_t>(g.sp * g.lp) * n, a = static_cast<size_t>(g.sp * g.sp) * n;
     Layout L{};
     size_t off = 0;
-    L.xf0 = off; off = align_up(off + x * 4);
     if (bf16) {
-        L.xf1 = L.xf0;
+        // X as the bf16 pair: hi ping-pong + lo (in place); no fp32 X.
+        L.has_xf = false;
         L.xb0 = off; off = align_up(off + x * 2);
         L.xb1 = off; off = align_up(off + x * 2);
+        L.xl = off; off = align_up(off + x * 2);
         L.af = off; off = align_up(off + a * 4);
         L.ab = off; off = align_up(off + a * 2);
         L.bb = off; off = align_up(off + a * 2);
     } else {
+        L.has_xf = true;
+        L.xf0 = off; off = align_up(off + x * 4);
         L.xf1 = off; off = align_up(off + x * 4);
-        L.xb0 = L.xb1 = 0;
+        L.xb0 = L.xb1 = L.xl = 0;
         L.af = off; off = align_up(off + a * 4);
         L.ab = off; off = align_up(off + a * 4);
         L.bb = off; off = align_up(off + a * 4);
@@ -478,10 +482,11 @@ Work chunk_work(muon_context *ctx, const Geom &g, bool bf16, int64_t n, int bpm,
     const Layout L = chunk_layout(g, bf16, n);
     char *base = static_cast<char *>(ctx->ws.p);
     Work w{};
-    w.xf = reinterpret_cast<float *>(base + L.xf0);
-    w.xf_next = reinterpret_cast<float *>(base + L.xf1);
+    w.xf = L.has_xf ? reinterpret_cast<float *>(base + L.xf0) : nullptr;
+    w.xf_next = L.has_xf ? reinterpret_cast<float *>(base + L.xf1) : nullptr;
     w.xb = bf16 ? static_cast<void *>(base + L.xb0) : nullptr;
     w.xb_next = bf16 ? static_cast<void *>(base + L.xb1) : nullptr;
+    w.xl = bf16 ? static_cast<void *>(base + L.xl) : nullptr;
     w.af = reinterpret_cast<float *>(base + L.af);
     w.ab = base + L.ab;
     w.bb = base + L.bb;
@@ -516,12 +521,13 @@ void ns_work(int stage, const Geom &g, bool bf16, int n, bool ns_out, int psize,
             *bytes = s * s * es + s * (s + 1) / 2 * 4 + s * s * es;
             break;
         case ST_APPLY:
+            // B, X operand, then X_lo in and (X_hi, X_lo) out; fp32 path: X in, X out
             *flops = 2 * s * s * l;
-            *bytes = s * s * es + s * l * es + s * l * 4 + s * l * (4 + (bf16 ? es : 0));
+            *bytes = s * s * es + s * l * es + (bf16 ? s * l * 6 : s * l * 8);
             break;
         default:  // ST_APPLY_UPDATE
             *flops = 2 * s * s * l;
-            *bytes = s * s * es + s * l * es + s * l * 4 + s * l * 2.0 * psize + (ns_out ? s * l * 4 : 0);
+            *bytes = s * s * es + s * l * es + s * l * (bf16 ? 2 : 4) + s * l * 2.0 * psize + (ns_out ? s * l * 4 : 0);
             break;
     }
     *flops *= n;
@@ -530,13 +536,13 @@ void ns_work(int stage, const Geom &g, bool bf16, int n, bool ns_out, int psize,
 
 // Runs normalisation + the NS schedule (+ the fused update when `update`) on
 // one chunk whose first stage already wrote X = N and the norms.  Returns the
-// workspace view whose xf holds the final X (meaningful when !update).
+// workspace view holding the final X in xf (fp32 path) or xb + xl (bf16 path),
+// meaningful when !update.
 muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom &g, Work &w, bool bf16,
                    const muon_hparams *hp, bool update, int param_bf16, bool any_ns_out, float d, float s,
                    hipStream_t st) {
     const double xe = static_cast<double>(g.s) * g.l * nmat;
-    hipError_t e = timed(ctx, ST_NORMALIZE, 0.0, xe * (bf16 ? 10.0 : 8.0), st,
-                         [&] { return muon::launch_normalize(nmat, g, w, bf16, st); });
+    hipError_t e = timed(ctx, ST_NORMALIZE, 0.0, xe * 8.0, st, [&] { return muon::launch_normalize(nmat, g, w, st); });
     if (e != hipSuccess) return hip_fail(ctx, e, "normalize launch");
     const int psize = param_bf16 ? 2 : 4;
     for (int it = 0; it < hp->num_ns_steps; ++it) {
@@ -783,7 +789,7 @@ muon_status muon_ns_only(muon_context *ctx, const float *n_in, float *x_out, int
     if (e != hipSuccess) return hip_fail(ctx, e, "norm launch");
     s = run_ns(ctx, ddev, 1, g, w, bf16, hp, false, 0, false, 0.f, 0.f, st);
     if (s != MUON_OK) return s;
-    e = timed(ctx, ST_EXPORT, 0.0, elems * 8.0, st, [&] { return muon::launch_export_x(g, w.xf, x_out, st); });
+    e = timed(ctx, ST_EXPORT, 0.0, elems * 8.0, st, [&] { return muon::launch_export_x(g, w, x_out, st); });
     if (e != hipSuccess) return hip_fail(ctx, e, "export launch");
     ctx->last_stream = st;
     ctx->last_count = 1;
