@@ -4,8 +4,8 @@
 //                      "V4 的完整更新公式" steps 1-2; DeepSeek-V4 book ch. 6 §5),
 //                      N_t written into the X workspace in the s x l orientation
 //                      (transposed through LDS when rows > cols) as fp32, or on the
-//                      bf16 path as the bf16 pair (hi, lo), per-block sums of N_t^2
-//                      in fp64.
+//                      bf16 path as the bf16 pair (hi, lo) the first Newton-Schulz
+//                      step reads directly, per-block sums of N_t^2 in fp64.
 //  * norm_finalize   : ||N_t||_F^2 per matrix from the block sums, fixed order.
 //  * normalize       : X_0 = N_t / ||N_t||_F (book ch. 6 §5, normalisation line),
 //                      fp32 (fp32 path) or the bf16 pair (hi, lo), zero padding.
@@ -79,12 +79,12 @@ struct XView {
     __device__ __forceinline__ float at(int64_t i) const { return xf ? xf[i] : join_bf16(xh[i], xl[i]); }
 };
 
-// N into the first matrix's workspace slot (fp32, or the bf16 pair in (xb_next, xl)).
+// N into the first matrix's workspace slot (fp32, or the bf16 pair in (xb, xl)).
 __device__ __forceinline__ void store_n(const Work &w, int64_t i, float v) {
     if (w.xf)
         w.xf[i] = v;
     else
-        split_bf16(v, static_cast<uint16_t *>(w.xb_next) + i, static_cast<uint16_t *>(w.xl) + i);
+        split_bf16(v, static_cast<uint16_t *>(w.xb) + i, static_cast<uint16_t *>(w.xl) + i);
 }
 
 // ---------------------------------------------------------------------------
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void nesterov_rows_kernel(const MatDesc *__res
     const GradT *__restrict__ gp = static_cast<const GradT *>(d.grad);
     float *__restrict__ mp = d.mom;
     float *__restrict__ xf = w.xf ? w.xf + e * w.x_stride : nullptr;  // fp32 path
-    uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb_next) + e * w.x_stride;  // bf16 path
+    uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb) + e * w.x_stride;  // bf16 path
     uint16_t *__restrict__ xl = static_cast<uint16_t *>(w.xl) + e * w.x_stride;
     const int64_t r0 = rb * rows_per_block;
     const int64_t r1 = min<int64_t>(g.rows, r0 + rows_per_block);
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void nesterov_tile_kernel(const MatDesc *__res
     const GradT *__restrict__ gp = static_cast<const GradT *>(d.grad);
     float *__restrict__ mp = d.mom;
     float *__restrict__ xf = w.xf ? w.xf + e * w.x_stride : nullptr;  // fp32 path
-    uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb_next) + e * w.x_stride;  // bf16 path
+    uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb) + e * w.x_stride;  // bf16 path
     uint16_t *__restrict__ xl = static_cast<uint16_t *>(w.xl) + e * w.x_stride;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     double acc = 0.0;
@@ -234,16 +234,15 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc *__res
     }
 }
 
-// X_0 = N * inv_norm over the padded sp x lp extent (zeros outside s x l).
-// fp32 path: in place in xf.  bf16 path: N as (hi, lo) in (xb_next, xl), X_0
-// as (hi, lo) in (xb, xl), lo in place.
+// X_0 = N * inv_norm over the padded sp x lp extent (zeros outside s x l), in
+// place: fp32 in xf, or the bf16 pair in (xb, xl).  The bf16 path runs it only
+// for an empty schedule; otherwise its first step applies inv_norm itself.
 __global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int blocks_per_mat, int rows_per_block) {
     const int64_t e = blockIdx.x / blocks_per_mat;
     const int64_t rb = blockIdx.x % blocks_per_mat;
     const float inv = w.inv_norm[e];
     const bool split = w.xf == nullptr;
     float *__restrict__ xf = split ? nullptr : w.xf + e * w.x_stride;
-    const uint16_t *__restrict__ nh = static_cast<const uint16_t *>(w.xb_next) + e * w.x_stride;
     uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb) + e * w.x_stride;
     uint16_t *__restrict__ xl = static_cast<uint16_t *>(w.xl) + e * w.x_stride;
     const int64_t r0 = rb * rows_per_block;
@@ -259,7 +258,7 @@ __global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int bloc
             floatx4 n;
             if (split) {
                 // entries past column l of the N pair are never written: mask them
-                n = join_bf16x4(*reinterpret_cast<const u32x2 *>(nh + off), *reinterpret_cast<const u32x2 *>(xl + off));
+                n = join_bf16x4(*reinterpret_cast<const u32x2 *>(xh + off), *reinterpret_cast<const u32x2 *>(xl + off));
             } else {
                 n = *reinterpret_cast<const floatx4 *>(xf + off);
             }
@@ -273,6 +272,19 @@ __global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int bloc
         } else {
             *reinterpret_cast<floatx4 *>(xf + off) = v;
         }
+    }
+}
+
+// Zeros the padding (outside s x l, inside sp x lp) of the bf16 pair (xb, xl)
+// that the momentum pass leaves untouched.  Block (e, i) handles padded row i.
+__global__ __launch_bounds__(256) void pad_zero_kernel(Geom g, Work w) {
+    const int64_t e = blockIdx.x / g.sp;
+    const int64_t i = blockIdx.x % g.sp;
+    uint16_t *xh = static_cast<uint16_t *>(w.xb) + e * w.x_stride + i * g.lp;
+    uint16_t *xl = static_cast<uint16_t *>(w.xl) + e * w.x_stride + i * g.lp;
+    for (int64_t j = (i < g.s ? g.l : 0) + threadIdx.x; j < g.lp; j += 256) {
+        xh[j] = 0;
+        xl[j] = 0;
     }
 }
 
@@ -512,6 +524,10 @@ hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, hipStream_t 
     return hipGetLastError();
 }
 
+hipError_t launch_pad_zero(int nmat, const Geom &g, const Work &w, hipStream_t st) {
+    hipLaunchKernelGGL(pad_zero_kernel, dim3(static_cast<unsigned>(g.sp * nmat)), dim3(256), 0, st, g, w);
+    return hipGetLastError();
+}
 hipError_t launch_update_plain(void *param, int param_bf16, const float *x, int64_t n, float d,
                                float s, hipStream_t st) {
     int64_t nb = (n + 255) / 256;

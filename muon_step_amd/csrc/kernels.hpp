@@ -24,6 +24,7 @@ hipError_t launch_norm_finalize(const MatDesc *descs, int nmat, const Work &w, i
 hipError_t launch_import_n(const float *n_in, const Geom &g, const Work &w, hipStream_t st);
 int import_n_blocks(const Geom &g);
 hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, hipStream_t st);
+hipError_t launch_pad_zero(int nmat, const Geom &g, const Work &w, hipStream_t st);
 hipError_t launch_update_plain(void *param, int param_bf16, const float *x, int64_t n, float d,
                                float s, hipStream_t st);
 hipError_t launch_update_from_work(const MatDesc *descs, int nmat, const Geom &g, const Work &w,
@@ -47,6 +48,9 @@ struct NsStep {
     int final_update;
     int param_bf16;
     float dscale, sscale;
+    // bf16 path, first step: the workspace X holds N itself; the Gram is
+    // scaled by inv_norm^2 and a X + B X by inv_norm (X_0 = N inv_norm).
+    int unnormalized;
 };
 
 // kind: 0 = A = X X^T, 1 = B = bA + cA^2, 2 = X <- aX + BX (or the fused update).

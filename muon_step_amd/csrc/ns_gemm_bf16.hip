@@ -422,6 +422,8 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void ns_sym_kernel(Geom g
     float *af = w.af + e * w.a_stride;
     uint16_t *dst = static_cast<uint16_t *>(KIND == GRAM ? w.ab : w.bb) + e * w.a_stride;
     const bool mirror = ti != tj;
+    // first step on the bf16 path: X holds N, so A = inv (N N^T) inv
+    const float scale = (KIND == GRAM && p.unnormalized) ? w.inv_norm[e] : 1.0f;
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
@@ -435,8 +437,10 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void ns_sym_kernel(Geom g
                 for (int q = 0; q < 4; ++q) {
                     const int64_t gi = gi0 + q;
                     v[q] = acc[mi][ni][4 * r4 + q];
-                    if (KIND == GRAM)
+                    if (KIND == GRAM) {
+                        v[q] = (v[q] * scale) * scale;
                         af[gi * g.sp + gj] = v[q];
+                    }
                     else
                         v[q] = p.b * af[gi * g.sp + gj] + p.c * v[q];
                     dst[gi * g.sp + gj] = float_to_bf16_bits(v[q]);
@@ -460,17 +464,18 @@ struct ApplyTile {
     int64_t col0;  // first output column
 };
 
-// Row lrow's four columns lcol .. lcol+3 of a X + B X, with X = X_hi + X_lo
-// staged in `reg` (X_hi rows in the first PAIR_HALF bytes, X_lo rows after).
+// Row lrow's four columns lcol .. lcol+3 of (a X + B X) * scale, with
+// X = X_hi + X_lo staged in `reg` (X_hi rows in the first PAIR_HALF bytes,
+// X_lo rows after).  scale is 1, or inv_norm when X still holds N.
 constexpr int PAIR_HALF = 4096;
 __device__ __forceinline__ floatx4 apply_value(const floatx16 &acc, const char *reg, int lrow, int lcol, int c4,
-                                               float a) {
+                                               float a, float scale) {
     const u32x2 h = *reinterpret_cast<const u32x2 *>(reg + pair_offset(lrow, lcol));
     const u32x2 l = *reinterpret_cast<const u32x2 *>(reg + PAIR_HALF + pair_offset(lrow, lcol));
     const floatx4 x = join_bf16x4(h, l);
     floatx4 v;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = a * x[q] + acc[4 * c4 + q];
+    for (int q = 0; q < 4; ++q) v[q] = (a * x[q] + acc[4 * c4 + q]) * scale;
     return v;
 }
 
@@ -480,13 +485,15 @@ __device__ __forceinline__ floatx4 apply_value(const floatx16 &acc, const char *
 // one wave's LDS accesses execute in order, so no value is overwritten before
 // it is read.
 template <class C>
-__device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char *reg, float a, int lane) {
+__device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char *reg, float a, float scale,
+                                             int lane) {
     const int lrow = lane & 31;
     floatx4 v[C::NI][4];
 #pragma unroll
     for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) v[ni][c4] = apply_value(accm[ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, a);
+        for (int c4 = 0; c4 < 4; ++c4)
+            v[ni][c4] = apply_value(accm[ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, a, scale);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int ni = 0; ni < C::NI; ++ni)
@@ -532,6 +539,7 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Pair::
     const char *hi_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xb) + t.e * w.x_stride + first);
     const char *lo_in = reinterpret_cast<const char *>(xl + first);
     const int64_t ld = g.lp * 2;
+    const float scale = p.unnormalized ? w.inv_norm[t.e] : 1.0f;
     auto dma_round = [&](char *dst, int h) {
         dma_bf16_rows<C>(dst, hi_in + C::EPI_ROWS * h * ld, ld, lane);
         dma_bf16_rows<C>(dst + PAIR_HALF, lo_in + C::EPI_ROWS * h * ld, ld, lane);
@@ -547,7 +555,7 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Pair::
         else
             fenced_wait_vmcnt<STORES_PER_ROUND>();
         char *reg = area[h & 1];
-        stage_values<C>(acc[h], reg, p.a, lane);
+        stage_values<C>(acc[h], reg, p.a, scale, lane);
 #pragma unroll
         for (int r4 = 0; r4 < C::EPI_ROWS / 4; ++r4) {
             const int lrow = 4 * r4 + (lane >> 4), chunk = lane & 15;
@@ -632,6 +640,7 @@ __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Pair
     const char *hi_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xb) + t.e * w.x_stride + first);
     const char *lo_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xl) + t.e * w.x_stride + first);
     const int64_t ld = g.lp * 2;
+    const float scale = p.unnormalized ? w.inv_norm[t.e] : 1.0f;
 #pragma unroll
     for (int h = 0; h < ROUNDS; ++h) {
         dma_bf16_rows<C>(reg, hi_in + C::EPI_ROWS * h * ld, ld, lane);
@@ -645,11 +654,11 @@ __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Pair
 #pragma unroll
                 for (int c4 = 0; c4 < 4; ++c4) {
                     const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
-                    const floatx4 v = apply_value(acc[h][ni], reg, lrow, lcol, c4, p.a);
+                    const floatx4 v = apply_value(acc[h][ni], reg, lrow, lcol, c4, p.a, scale);
                     if (gi < g.s) update_row4<PARAM_BF16>(d, g, p, gi, t.col0 + lcol, v);
                 }
         } else {
-            stage_values<C>(acc[h], reg, p.a, lane);
+            stage_values<C>(acc[h], reg, p.a, scale, lane);
 #pragma unroll 4
             for (int r4 = 0; r4 < C::EPI_ROWS / 4; ++r4) {
                 const int rrow = 4 * r4 + (lane >> 4), chunk = lane & 15;

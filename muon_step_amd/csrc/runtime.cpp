@@ -542,7 +542,16 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
                    const muon_hparams *hp, bool update, int param_bf16, bool any_ns_out, float d, float s,
                    hipStream_t st) {
     const double xe = static_cast<double>(g.s) * g.l * nmat;
-    hipError_t e = timed(ctx, ST_NORMALIZE, 0.0, xe * 8.0, st, [&] { return muon::launch_normalize(nmat, g, w, st); });
+    // bf16 path with a schedule: X stays N and the first step applies 1/||N||
+    // (only the padding needs zeros); otherwise a normalisation pass.
+    const bool fold = bf16 && hp->num_ns_steps > 0;
+    hipError_t e = hipSuccess;
+    if (!fold) {
+        e = timed(ctx, ST_NORMALIZE, 0.0, xe * 8.0, st, [&] { return muon::launch_normalize(nmat, g, w, st); });
+    } else if (g.sp > g.s || g.lp > g.l) {
+        const double pad = (static_cast<double>(g.sp) * g.lp - static_cast<double>(g.s) * g.l) * nmat;
+        e = timed(ctx, ST_NORMALIZE, 0.0, pad * 4.0, st, [&] { return muon::launch_pad_zero(nmat, g, w, st); });
+    }
     if (e != hipSuccess) return hip_fail(ctx, e, "normalize launch");
     const int psize = param_bf16 ? 2 : 4;
     for (int it = 0; it < hp->num_ns_steps; ++it) {
@@ -554,6 +563,7 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
         p.param_bf16 = param_bf16;
         p.dscale = d;
         p.sscale = s;
+        p.unnormalized = (fold && it == 0) ? 1 : 0;
         for (int kind = 0; kind < 3; ++kind) {
             const int stage = kind == 0 ? ST_GRAM : kind == 1 ? ST_POLY : (p.final_update ? ST_APPLY_UPDATE : ST_APPLY);
             double fl = 0, by = 0;
