@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import math
+import re
 import os
 import sys
 import time
@@ -37,9 +38,16 @@ def log(*a):
 
 
 def gemm_source_sha():
-    """Hash of the bf16 Newton-Schulz kernel source the stored traffic counters were taken on."""
-    with open(os.path.join(ROOT, "muon_step_amd", "csrc", "ns_gemm_bf16.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """Hash of the bf16 Newton-Schulz kernel sources (comments and blank
+    space removed) the stored traffic counters were taken on."""
+    h = hashlib.sha256()
+    for name in ("ns_gemm_bf16.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "muon_step_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
 
 
 def copy_calibration():
@@ -182,7 +190,7 @@ def main():
         "data": "synthetic (seeded low-rank-plus-noise bf16 gradients, N(0,0.02) bf16 params, zero fp32 momentum)",
         "config": {"workload": "moe_256x2048x7168_bf16", "matrices": count, "shape": [rows, cols],
                    "ns_steps": 10, "schedule": "deepseekv4 8x(3.4445,-4.7750,2.0315)+2x(2,-1.5,0.5)",
-                   "ns_precision": "bf16 MFMA operands, fp32 accumulate, fp32 master X",
+                   "ns_precision": "bf16 MFMA operands, fp32 accumulate, X kept as a bf16 (hi, lo) pair",
                    "lr": 0.02, "momentum": 0.95, "weight_decay": 0.1, "gamma": 0.2},
         "ns_tflops": round(ns_tflops, 2),
         "ns_frac_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4),

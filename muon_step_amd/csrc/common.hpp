@@ -37,13 +37,14 @@ struct Geom {
 };
 
 // Workspace of one chunk: matrix e of the chunk owns
-//   xf      + e*x_stride  fp32 master X (sp x lp), read by the current step
-//   xf_next + e*x_stride  where the current step writes X (== xf on the bf16
-//                         path, where only the tile's own epilogue touches it)
-//   xb      + e*x_stride  bf16 operand copy of X (bf16 path only)
-//   xb_next + e*x_stride  where the current step writes it: the product B X
-//                         reads whole column panels of X, so the operand copy
-//                         is double-buffered
+//   xf      + e*x_stride  fp32 X (sp x lp), read by the current step (fp32 path)
+//   xf_next + e*x_stride  where the current step writes X (fp32 path)
+//   xb      + e*x_stride  X_hi = bf16(X), the MFMA operand (bf16 path)
+//   xb_next + e*x_stride  where the current step writes X_hi: the product B X
+//                         reads whole column panels of X, so X_hi is
+//                         double-buffered
+//   xl      + e*x_stride  X_lo = bf16(X - X_hi), rewritten in place by the
+//                         tile that owns the elements (bf16 path)
 //   af + e*a_stride       fp32 A = X X^T (sp x sp, lower-triangle tiles)
 //   ab + e*a_stride       A as MFMA operand (bf16 or fp32, both triangles)
 //   bb + e*a_stride       B = bA + cA^2 as MFMA operand (both triangles)

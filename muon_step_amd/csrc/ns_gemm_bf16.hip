@@ -12,7 +12,7 @@
 //                             only, written mirrored.  Row i of A serves as
 //                             column i, so both operands are K-contiguous.
 //   APPLY : X' = a X + B X    s x l, K = s.  The aX term is added in fp32 from
-//                             the fp32 master X.  The last step instead
+//                             X = X_hi + X_lo.  The last step instead
 //                             writes W <- d W - s_scale X' (and O'_t).
 //
 // Data movement.  Every wave owns a 128 x 64 output block and multiplies with
@@ -21,7 +21,7 @@
 // (global_load_lds_dwordx4) into a ring of LDS stages; each wave waits on its
 // own outstanding-load counter, then one barrier per stage.  GRAM and POLY use
 // 256 x 256 tiles, 8 waves and a 4-stage ring (128 KB).  APPLY, whose
-// epilogue moves ~10 bytes per output element, uses 256 x 128 tiles, 4 waves
+// epilogue moves 8 bytes per output element, uses 256 x 128 tiles, 4 waves
 // and a 3-stage ring (72 KB) so two workgroups share a CU and one's epilogue
 // overlaps the other's MFMAs.  The LDS layouts are XOR-swizzled so that every
 // 16-lane phase of a fragment read touches all 64 banks once.  The X operand

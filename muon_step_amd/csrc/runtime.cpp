@@ -508,7 +508,7 @@ size_t tabs_bytes(size_t partials, int64_t max_chunk) {
 
 // Algorithmic work of one Newton-Schulz stage over n matrices of geometry g:
 // FLOPs counting one triangle of the symmetric products, and the bytes a
-// kernel must move at least once (operands, fp32 master, outputs).
+// kernel must move at least once (operands, X for the aX term, outputs).
 void ns_work(int stage, const Geom &g, bool bf16, int n, bool ns_out, int psize, double *flops, double *bytes) {
     const double s = static_cast<double>(g.s), l = static_cast<double>(g.l), es = bf16 ? 2.0 : 4.0;
     switch (stage) {
