@@ -27,7 +27,12 @@
 // 16-lane phase of a fragment read touches all 64 banks once.  The X operand
 // of B X is stored as it lies in memory (k rows, n contiguous) and read with
 // ds_read_b64_tr_b16, which hands each lane four consecutive k of one column.
-// Block ids are renumbered so one matrix's tiles share an XCD (and its L2).
+// The products are issued with the operands swapped, so each lane's
+// accumulators hold four consecutive columns of one output row; every
+// epilogue stages its block through LDS in rounds of 32 rows and stores
+// whole rows (GRAM/POLY also store the block's columns as rows of the
+// mirrored tile).  Block ids are renumbered so one matrix's tiles share an
+// XCD (and its L2).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -119,6 +124,13 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
 }
 // s_waitcnt lgkmcnt(0) only (vmcnt and expcnt at their maxima: no wait).
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// s_waitcnt vmcnt(N) that no memory access is moved across.
+template <int N> __device__ __forceinline__ void fenced_wait_vmcnt() {
+    asm volatile("" ::: "memory");
+    wait_vmcnt<N>();
+    asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ void stage_barrier() {
     asm volatile("" ::: "memory");
@@ -277,7 +289,7 @@ __device__ __forceinline__ void pipeline_step(floatx16 (&acc)[C::MI][C::NI], con
     for (int ks = 0; ks < 2; ++ks) {
         Frags<C> f;
         read_frags<C, KIND, S>(f, ks, wm, wn, lane);
-        mma_frags<C, KIND == APPLY>(acc, f);
+        mma_frags<C, true>(acc, f);
     }
 }
 
@@ -378,6 +390,126 @@ __device__ __forceinline__ void tri_decode(int64_t t, int *ti, int *tj) {
 
 // ------------------------------------------------------------------------ A, B
 
+// Epilogue staging areas of the 8-wave GRAM/POLY kernel (8 KB each, inside
+// the operand ring, free once every wave has left the main loop): the first
+// area of wave w lies in p(w/2), the second in q(w/2).
+template <int WHICH> __device__ __forceinline__ char *sym_area(int wave) {
+    const int off = (wave & 1) * 8192;
+    switch (wave >> 1) {
+        case 0: return (WHICH ? lds_q0 : lds_p0) + off;
+        case 1: return (WHICH ? lds_q1 : lds_p1) + off;
+        case 2: return (WHICH ? lds_q2 : lds_p2) + off;
+        default: return (WHICH ? lds_q3 : lds_p3) + off;
+    }
+}
+
+// Epilogue of GRAM and POLY.  The wave's 128 x 64 block is finished in four
+// rounds of 32 rows staged in LDS.  POLY first brings the matching rows of the
+// fp32 A by DMA (two areas, the next round in flight).  The values (GRAM: A,
+// times inv_norm^2 on the bf16 path's first step; POLY: b A + c A A) are
+// formed in the accumulator layout and written in place as fp32 rows; the
+// rows are stored whole (GRAM: fp32 A and its bf16 operand copy; POLY: bf16
+// B), and for an off-diagonal tile each column of the block is stored as 32
+// consecutive bf16 of a row of the mirrored tile.  Vector-memory instructions
+// retire in issue order; the wait before POLY's round h allows what was issued
+// after round h's DMA: round h-1's stores (at least ROW_STORES) and round h+1's
+// DMA.
+template <class C, int KIND>
+__device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI], const Geom &g, const Work &w,
+                                             const NsStep &p, int64_t e, int ti, int tj, int wm, int wn,
+                                             char *const (&area)[2], int lane) {
+    constexpr int ROUNDS = C::WM / C::EPI_ROWS;
+    constexpr int DMA_PER_ROUND = C::EPI_ROWS / 4;
+    constexpr int ROW_STORES = C::EPI_ROWS / 4;
+    static_assert(ROUNDS == C::MI && C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
+    const int64_t ld = g.sp;
+    const int64_t row0 = static_cast<int64_t>(ti) * C::BM + wm * C::WM;
+    const int64_t col0 = static_cast<int64_t>(tj) * C::BN + wn * C::WN;
+    float *af = w.af + e * w.a_stride;
+    uint16_t *dst = static_cast<uint16_t *>(KIND == GRAM ? w.ab : w.bb) + e * w.a_stride;
+    const bool mirror = ti != tj;
+    // first step on the bf16 path: X holds N, so A = inv (N N^T) inv
+    const float scale = (KIND == GRAM && p.unnormalized) ? w.inv_norm[e] : 1.0f;
+    const char *a_in = reinterpret_cast<const char *>(af + row0 * ld + col0);
+    if constexpr (KIND == POLY) {
+        dma_epi<C>(area[0], a_in, ld * 4, lane);
+        dma_epi<C>(area[1], a_in + C::EPI_ROWS * ld * 4, ld * 4, lane);
+    }
+    const int lrow = lane & 31;
+#pragma unroll
+    for (int h = 0; h < ROUNDS; ++h) {
+        char *reg = area[h & 1];
+        if constexpr (KIND == POLY) {
+            if (h == 0)
+                fenced_wait_vmcnt<DMA_PER_ROUND>();
+            else if (h + 1 < ROUNDS)
+                fenced_wait_vmcnt<ROW_STORES + DMA_PER_ROUND>();
+            else
+                fenced_wait_vmcnt<ROW_STORES>();
+        }
+        floatx4 v[C::NI][4];
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
+                if constexpr (KIND == GRAM) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[ni][c4][q] = (acc[h][ni][4 * c4 + q] * scale) * scale;
+                } else {
+                    const floatx4 a4 = *reinterpret_cast<const floatx4 *>(reg + epi_offset(lrow, lcol >> 2));
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[ni][c4][q] = p.b * a4[q] + p.c * acc[h][ni][4 * c4 + q];
+                }
+            }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
+                *reinterpret_cast<floatx4 *>(reg + epi_offset(lrow, lcol >> 2)) = v[ni][c4];
+            }
+        wait_lgkm0();  // the wave's writes land before its row and column reads
+        asm volatile("" ::: "memory");
+        const int64_t rbase = row0 + C::EPI_ROWS * h;
+#pragma unroll
+        for (int r4 = 0; r4 < C::EPI_ROWS / 4; ++r4) {
+            const int rrow = 4 * r4 + (lane >> 4), chunk = lane & 15;
+            const floatx4 x = *reinterpret_cast<const floatx4 *>(reg + epi_offset(rrow, chunk));
+            const int64_t idx = (rbase + rrow) * ld + col0 + 4 * chunk;
+            if constexpr (KIND == GRAM) *reinterpret_cast<floatx4 *>(af + idx) = x;
+            u32x2 pk;
+            pk[0] = pack_bf16x2(x[0], x[1]);
+            pk[1] = pack_bf16x2(x[2], x[3]);
+            *reinterpret_cast<u32x2 *>(dst + idx) = pk;
+        }
+        if (mirror) {
+            // column c of the block -> row col0 + c of the mirrored tile; lane
+            // (c, part) moves rows 8*part .. 8*part+7 of the round
+#pragma unroll
+            for (int t = 0; t < C::WN / 16; ++t) {
+                const int c = 16 * t + (lane >> 2), part = lane & 3;
+                float f[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    f[k] = *reinterpret_cast<const float *>(reg + epi_offset(8 * part + k, c >> 2) + (c & 3) * 4);
+                u32x4 pk;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) pk[k] = pack_bf16x2(f[2 * k], f[2 * k + 1]);
+                *reinterpret_cast<u32x4 *>(dst + (col0 + c) * ld + rbase + 8 * part) = pk;
+            }
+        }
+        if constexpr (KIND == POLY) {
+            if (h + 2 < ROUNDS) {
+                wait_lgkm0();  // this round's LDS reads are done before the DMA refills the area
+                asm volatile("" ::: "memory");
+                dma_epi<C>(reg, a_in + C::EPI_ROWS * (h + 2) * ld * 4, ld * 4, lane);
+            }
+        }
+    }
+}
+
 template <class C, int KIND>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void ns_sym_kernel(Geom g, Work w, NsStep p,
                                                                           int64_t tiles_per_mat, int64_t nblocks) {
@@ -415,44 +547,12 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void ns_sym_kernel(Geom g
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
     main_loop4<C, KIND>(acc, src, static_cast<int>(kdim / C::BK), wave, wm, wn, lane);
 
-    // acc[mi][ni][r] holds output (row, col) of the tile:
-    //   row = wm*WM + mi*32 + 8*(r/4) + 4*(lane/32) + r%4,  col = wn*WN + ni*32 + lane%32
-    const int64_t row_base = static_cast<int64_t>(ti) * C::BM + wm * C::WM + 4 * (lane >> 5);
-    const int64_t col_base = static_cast<int64_t>(tj) * C::BN + wn * C::WN + (lane & 31);
-    float *af = w.af + e * w.a_stride;
-    uint16_t *dst = static_cast<uint16_t *>(KIND == GRAM ? w.ab : w.bb) + e * w.a_stride;
-    const bool mirror = ti != tj;
-    // first step on the bf16 path: X holds N, so A = inv (N N^T) inv
-    const float scale = (KIND == GRAM && p.unnormalized) ? w.inv_norm[e] : 1.0f;
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int64_t gi0 = row_base + mi * 32 + 8 * r4;
-                const int64_t gj = col_base + ni * 32;
-                float v[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t gi = gi0 + q;
-                    v[q] = acc[mi][ni][4 * r4 + q];
-                    if (KIND == GRAM) {
-                        v[q] = (v[q] * scale) * scale;
-                        af[gi * g.sp + gj] = v[q];
-                    }
-                    else
-                        v[q] = p.b * af[gi * g.sp + gj] + p.c * v[q];
-                    dst[gi * g.sp + gj] = float_to_bf16_bits(v[q]);
-                }
-                if (mirror) {
-                    // rows gi0..gi0+3 of column gj become 4 consecutive columns of row gj
-                    u32x2 pk;
-                    pk[0] = pack_bf16x2(v[0], v[1]);
-                    pk[1] = pack_bf16x2(v[2], v[3]);
-                    *reinterpret_cast<u32x2 *>(dst + gj * g.sp + gi0) = pk;
-                }
-            }
+    // acc[mi][ni][4*c4 + q] holds output row wm*WM + mi*32 + lane%32, column
+    // wn*WN + ni*32 + 8*c4 + 4*(lane/32) + q of the tile.
+    wait_lgkm0();
+    stage_barrier();  // every wave is done with the operand ring
+    char *const area[2] = {sym_area<0>(wave), sym_area<1>(wave)};
+    sym_epilogue<C, KIND>(acc, g, w, p, e, ti, tj, wm, wn, area, lane);
 }
 
 // --------------------------------------------------------------------- a X + B X
@@ -506,12 +606,6 @@ __device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char
     asm volatile("" ::: "memory");
 }
 
-// s_waitcnt vmcnt(N) that no memory access is moved across.
-template <int N> __device__ __forceinline__ void fenced_wait_vmcnt() {
-    asm volatile("" ::: "memory");
-    wait_vmcnt<N>();
-    asm volatile("" ::: "memory");
-}
 
 // Epilogue of an intermediate step: X' = a X + B X is written as the bf16 pair
 // (X'_hi to xb_next, X'_lo to xl in place; zero outside s x l).  Per round of
