@@ -15,24 +15,24 @@
 //                             X = X_hi + X_lo.  The last step instead
 //                             writes W <- d W - s_scale X' (and O'_t).
 //
-// Data movement.  Every wave owns a 128 x 64 output block and multiplies with
-// v_mfma_f32_32x32x16_bf16 into fp32 accumulators.  Operand slabs of 32 k are
-// copied global -> LDS by the direct 16-byte-per-lane DMA
-// (global_load_lds_dwordx4) into a ring of LDS stages; each wave waits on its
-// own outstanding-load counter, then one barrier per stage.  GRAM and POLY use
-// 256 x 256 tiles, 8 waves and a 4-stage ring (128 KB).  APPLY, whose
-// epilogue moves 8 bytes per output element, uses 256 x 128 tiles, 4 waves
-// and a 3-stage ring (72 KB) so two workgroups share a CU and one's epilogue
-// overlaps the other's MFMAs.  The LDS layouts are XOR-swizzled so that every
-// 16-lane phase of a fragment read touches all 64 banks once.  The X operand
-// of B X is stored as it lies in memory (k rows, n contiguous) and read with
-// ds_read_b64_tr_b16, which hands each lane four consecutive k of one column.
-// The products are issued with the operands swapped, so each lane's
-// accumulators hold four consecutive columns of one output row; every
-// epilogue stages its block through LDS in rounds of 32 rows and stores
-// whole rows (GRAM/POLY also store the block's columns as rows of the
-// mirrored tile).  Block ids are renumbered so one matrix's tiles share an
-// XCD (and its L2).
+// Data movement.  All three products use 256 x 256 tiles, one workgroup of
+// 8 waves per CU (two per SIMD), each wave owning a 128 x 64 block computed
+// with v_mfma_f32_32x32x16_bf16 into fp32 accumulators.  Operand slabs of
+// 32 k are copied global -> LDS by the 16-byte-per-lane DMA
+// (global_load_lds_dwordx4) into a 4-stage ring (128 KB).  Within a stage
+// every product is followed by at most one fragment read for the next 16-k
+// substep and one DMA for a later stage, so LDS reads and copies run under
+// the MFMAs; one barrier per stage, between its two substeps.  The LDS
+// layouts are XOR-swizzled so that every 16-lane phase of a fragment read
+// touches all 64 banks once.  The X operand of B X is stored as it lies in
+// memory (k rows, n contiguous) and read with ds_read_b64_tr_b16, which hands
+// each lane four consecutive k of one column.  The products are issued with
+// the operands swapped, so each lane's accumulators hold four consecutive
+// columns of one output row; every epilogue stages its block through LDS in
+// rounds of 32 rows and stores whole rows (GRAM/POLY also store the block's
+// columns as rows of the mirrored tile; APPLY moves 8 bytes per output
+// element: X_hi and X_lo in and out).  Block ids are renumbered so one
+// matrix's tiles share an XCD (and its L2).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -41,15 +41,16 @@ namespace bf16path {
 
 enum Kind { GRAM = 0, POLY = 1, APPLY = 2 };
 
-template <int NT_, int BN_, int STAGES_, int WN_ = 64>
+// Tile geometry shared by the three products: 256 x 256 output tiles, 8
+// waves (two per SIMD, one workgroup per CU), each owning a 128 x 64 block,
+// and a ring of four 32-k stages.
 struct Cfg {
-    static constexpr int NT = NT_, NWAVES = NT / 64;
-    static constexpr int WAVES_PER_SIMD = NWAVES / 4;  // one workgroup per CU
-    static constexpr int BM = 256, BN = BN_;
-    static constexpr int WM = 128, WN = WN_, MI = WM / 32, NI = WN / 32;
+    static constexpr int NT = 512, NWAVES = NT / 64;
+    static constexpr int BM = 256, BN = 256;
+    static constexpr int WM = 128, WN = 64, MI = WM / 32, NI = WN / 32;
     static constexpr int WAVES_N = BN / WN, WAVES_M = BM / WM;
     static_assert(WAVES_N * WAVES_M == NWAVES, "wave grid");
-    static constexpr int STAGES = STAGES_;
+    static constexpr int STAGES = 4;
     static constexpr int BK = 32;                      // k per stage
     static constexpr int P_BYTES = BM * 64;            // 256 rows x 32 bf16
     static constexpr int Q_BYTES = BN * 64;            // BN rows x 32 bf16, or 32 k-rows x BN bf16
@@ -59,17 +60,15 @@ struct Cfg {
     static constexpr int LPS = P_BLOCKS + Q_BLOCKS;    // DMA instructions per wave per stage
     static constexpr int EPI_BYTES = 8192;             // epilogue staging per wave and round
     static constexpr int EPI_ROWS = EPI_BYTES / 256;   // rows of 64 fp32 per staging round
+    static constexpr int NM = MI * NI;                 // MFMAs per wave and 16-k substep
+    static constexpr int NF = MI + NI;                 // fragments per wave and substep
 };
-using Big = Cfg<512, 256, 4>;   // GRAM, POLY
-using Pair = Cfg<256, 128, 3>;  // APPLY
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_tr;
 typedef __attribute__((address_space(3))) bf16x4_tr lds_bf16x4_t;
 
-// One LDS object per stage and operand: the compiler tracks DMA writes per
-// object, so reading one stage never waits on the DMA filling another.  Each
-// kernel is allocated only the objects it uses.
+// One LDS object per stage and operand (16 KB each); after the main loop the
+// epilogues reuse them as staging areas.
 __shared__ __attribute__((aligned(1024))) char lds_p0[16384];
 __shared__ __attribute__((aligned(1024))) char lds_p1[16384];
 __shared__ __attribute__((aligned(1024))) char lds_p2[16384];
@@ -78,9 +77,6 @@ __shared__ __attribute__((aligned(1024))) char lds_q0[16384];
 __shared__ __attribute__((aligned(1024))) char lds_q1[16384];
 __shared__ __attribute__((aligned(1024))) char lds_q2[16384];
 __shared__ __attribute__((aligned(1024))) char lds_q3[16384];
-__shared__ __attribute__((aligned(1024))) char lds_h0[8192];
-__shared__ __attribute__((aligned(1024))) char lds_h1[8192];
-__shared__ __attribute__((aligned(1024))) char lds_h2[8192];
 
 template <int S> __device__ __forceinline__ char *slot_p() {
     if constexpr (S == 0) return lds_p0;
@@ -88,32 +84,23 @@ template <int S> __device__ __forceinline__ char *slot_p() {
     else if constexpr (S == 2) return lds_p2;
     else return lds_p3;
 }
-template <class C, int S> __device__ __forceinline__ char *slot_q() {
-    if constexpr (C::Q_BYTES == 16384) {
-        if constexpr (S == 0) return lds_q0;
-        else if constexpr (S == 1) return lds_q1;
-        else if constexpr (S == 2) return lds_q2;
-        else return lds_q3;
-    } else {
-        static_assert(C::Q_BYTES == 8192 && S < 3, "Q slot");
-        if constexpr (S == 0) return lds_h0;
-        else if constexpr (S == 1) return lds_h1;
-        else return lds_h2;
-    }
+template <int S> __device__ __forceinline__ char *slot_q() {
+    if constexpr (S == 0) return lds_q0;
+    else if constexpr (S == 1) return lds_q1;
+    else if constexpr (S == 2) return lds_q2;
+    else return lds_q3;
 }
 
-// APPLY stages its epilogue through two areas per wave so the next round's
-// DMA overlaps this round's arithmetic and stores.  The first areas of all
-// waves lie in {p0, p1} and the second in {p2, h0, h1}: disjoint LDS
-// objects, so the compiler's tracking of LDS DMA makes a read of one area
-// wait only for the DMA that filled it.
-__device__ __forceinline__ char *epi_first(int wave) { return (wave < 2 ? lds_p0 : lds_p1) + (wave & 1) * 8192; }
-__device__ __forceinline__ char *epi_second(int wave) {
-    switch (wave) {
-        case 0: return lds_p2;
-        case 1: return lds_p2 + 8192;
-        case 2: return lds_h0;
-        default: return lds_h1;
+// Epilogue staging areas (8 KB each, inside the operand ring, free once every
+// wave has left the main loop): the first area of wave w lies in p(w/2), the
+// second in q(w/2).
+template <int WHICH> __device__ __forceinline__ char *epi_area(int wave) {
+    const int off = (wave & 1) * 8192;
+    switch (wave >> 1) {
+        case 0: return (WHICH ? lds_q0 : lds_p0) + off;
+        case 1: return (WHICH ? lds_q1 : lds_p1) + off;
+        case 2: return (WHICH ? lds_q2 : lds_p2) + off;
+        default: return (WHICH ? lds_q3 : lds_p3) + off;
     }
 }
 
@@ -138,6 +125,19 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// One global -> LDS DMA of 16 bytes per lane (global_load_lds_dwordx4): lane
+// i's 16 bytes at g land at LDS byte l + 16 i (l wave-uniform, passed in M0,
+// which is set in the same statement).  The instruction has no register
+// results.  It is issued from asm because the compiler, when it sees an
+// LDS-writing load, makes every later wait for an LDS read a wait for all of
+// them (lgkmcnt 0), which stalls the fragment pipeline; the kernels count
+// these loads themselves (wait_vmcnt) and fence LDS reads with barriers that
+// carry a memory clobber.
+__device__ __forceinline__ void dma16(const char *g, const char *l) {
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>(l)));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+
 // K-contiguous tile (rows x 64 bytes): 16-byte chunk c of row r lives at chunk
 // c ^ ((r >> 2) & 3), so 16 consecutive rows reading one chunk cover 16
 // distinct 16-byte bank groups.
@@ -154,200 +154,163 @@ template <class C> __device__ __forceinline__ int nc_offset(int krow, int byte) 
 // 64 banks.
 __device__ __forceinline__ int epi_offset(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
 
-// DMA of one stage of a K-contiguous tile: rows [0, ROWS) x bytes [kt*64,
-// kt*64 + 64) of `src` (row pitch ld) into `dst`.  Wave w fills BLOCKS
-// consecutive 1 KB blocks of 16 rows; lane i lands at block byte 16 i, i.e.
-// row i/4, swizzled chunk i%4.
-template <int BLOCKS>
-__device__ __forceinline__ void dma_kc(char *dst, const char *src, int64_t ld, int kt, int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < BLOCKS; ++j) {
-        const int blk = wave * BLOCKS + j;
-        const int row = blk * 16 + (lane >> 2);
-        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-        const char *g = src + row * ld + kt * 64 + chunk * 16;
-        __builtin_amdgcn_global_load_lds(g, (lds_void_t *)(dst + blk * 1024), 16, 0, 0);
-    }
-}
-
-// DMA of one stage of the B X operand: k-rows [kt*32, kt*32 + 32) x QROW bytes
-// of row-major X (`src` points at the tile's first column) into `dst`.  A 1 KB
-// block holds 1024/QROW consecutive k-rows; lane i lands at byte 16 i.
-template <class C>
-__device__ __forceinline__ void dma_nc(char *dst, const char *src, int64_t ld, int kt, int wave, int lane) {
-    constexpr int UNITS = C::QROW / 16;  // 16-byte units per k-row
-#pragma unroll
-    for (int j = 0; j < C::Q_BLOCKS; ++j) {
-        const int blk = wave * C::Q_BLOCKS + j;
-        const int krow = blk * (1024 / C::QROW) + lane / UNITS;
-        const int u = lane % UNITS;
-        const int byte = ((((u >> 2) ^ (krow & 3))) << 6) + ((u & 3) << 4);
-        const char *g = src + (static_cast<int64_t>(kt) * C::BK + krow) * ld + byte;
-        __builtin_amdgcn_global_load_lds(g, (lds_void_t *)(dst + blk * 1024), 16, 0, 0);
-    }
-}
-
-template <class C, int KIND, int S>
-__device__ __forceinline__ void issue_stage(const char *psrc, int64_t ld_p, const char *qsrc, int64_t ld_q, int kt,
-                                            int wave, int lane) {
-    dma_kc<C::P_BLOCKS>(slot_p<S>(), psrc, ld_p, kt, wave, lane);
-    if constexpr (KIND == APPLY)
-        dma_nc<C>(slot_q<C, S>(), qsrc, ld_q, kt, wave, lane);
-    else
-        dma_kc<C::Q_BLOCKS>(slot_q<C, S>(), qsrc, ld_q, kt, wave, lane);
-}
-
-// Fragments of one 16-k substep: MI A-fragments and NI B-fragments (8 bf16 =
-// 16 bytes each per lane).
-template <class C> struct Frags {
-    u32x4 a[C::MI];
-    u32x4 b[C::NI];
-};
-
-// Reads substep ks (0 or 1) of the stage in slot S.
-template <class C, int KIND, int S>
-__device__ __forceinline__ void read_frags(Frags<C> &f, int ks, int wm, int wn, int lane) {
-    const char *pl = slot_p<S>();
-    const char *ql = slot_q<C, S>();
-    const int chunk = 2 * ks + (lane >> 5);  // k = 8*chunk .. 8*chunk+7 of this stage
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi) {
-        const int row = wm * C::WM + mi * 32 + (lane & 31);
-        f.a[mi] = *reinterpret_cast<const u32x4 *>(pl + kc_offset(row, chunk));
-    }
-    if constexpr (KIND == APPLY) {
-        // Lane j of each 16-lane group supplies k-row kbase + j/4, columns
-        // n0 + 4(j%4) .. +3; lane i then holds X[kbase .. kbase+3][n0 + i].
-        const int grp = lane >> 4, j = lane & 15;
-#pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni) {
-            const int n0 = wn * C::WN + ni * 32 + 16 * (grp & 1);
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int krow = 16 * ks + 8 * (grp >> 1) + 4 * r + (j >> 2);
-                const int byte = (n0 + 4 * (j & 3)) * 2;
-                const bf16x4_tr t =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(ql + nc_offset<C>(krow, byte)));
-                const u32x2 tt = __builtin_bit_cast(u32x2, t);
-                f.b[ni][2 * r] = tt[0];
-                f.b[ni][2 * r + 1] = tt[1];
-            }
-        }
-    } else {
-#pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni) {
-            const int row = wn * C::WN + ni * 32 + (lane & 31);
-            f.b[ni] = *reinterpret_cast<const u32x4 *>(ql + kc_offset(row, chunk));
-        }
-    }
-}
-
-// acc[mi][ni] += A-fragment x B-fragment.  SWAP multiplies the operands the
-// other way round (the Q fragment as the MFMA's first operand), which leaves
-// the transposed 32 x 32 block in the accumulator: each lane then holds four
-// consecutive output columns of one output row, so the epilogue can move
-// 16 bytes per access.
-template <class C, bool SWAP>
-__device__ __forceinline__ void mma_frags(floatx16 (&acc)[C::MI][C::NI], const Frags<C> &f) {
-#pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni) {
-            if constexpr (SWAP)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.b[ni]),
-                                                                      __builtin_bit_cast(bf16x8, f.a[mi]),
-                                                                      acc[mi][ni], 0, 0, 0);
-            else
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[mi]),
-                                                                      __builtin_bit_cast(bf16x8, f.b[ni]),
-                                                                      acc[mi][ni], 0, 0, 0);
-        }
-}
-
 struct Src {
-    const char *p;
+    const char *p;  // P operand (output rows): K-contiguous rows of X, A or B
     int64_t ld_p;
-    const char *q;
+    const char *q;  // Q operand (output columns): K-contiguous rows, or X itself for APPLY
     int64_t ld_q;
 };
 
-// One pipeline step: stage kt (slot S) is consumed while up to WAIT/LPS later
-// stages may still be in flight.  With ISSUE the DMA of stage kt+STAGES-1
-// refills the slot stage kt-1 used: each wave waits for its own reads of that
-// slot to return (lgkmcnt 0) before the barrier, so after it no read of the
-// slot is outstanding, wherever the compiler placed the products.
-template <class C, int KIND, int S, int WAIT, bool ISSUE>
-__device__ __forceinline__ void pipeline_step(floatx16 (&acc)[C::MI][C::NI], const Src &src, int kt, int wave,
-                                              int wm, int wn, int lane) {
-    wait_lgkm0();
-    wait_vmcnt<WAIT>();
-    stage_barrier();
-    if constexpr (ISSUE)
-        issue_stage<C, KIND, (S + C::STAGES - 1) % C::STAGES>(src.p, src.ld_p, src.q, src.ld_q,
-                                                               kt + C::STAGES - 1, wave, lane);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        Frags<C> f;
-        read_frags<C, KIND, S>(f, ks, wm, wn, lane);
-        mma_frags<C, true>(acc, f);
+// DMA block j (0 <= j < LPS) of this wave for stage kt into slot S.  Blocks
+// [0, P_BLOCKS) fill the P slab: 1 KB block `blk` holds rows 16 blk .. +15 x
+// bytes [kt*64, kt*64 + 64); lane i lands at block byte 16 i, i.e. row i/4,
+// swizzled chunk i%4.  The rest fill the Q slab the same way, except for
+// APPLY, whose Q slab is k-rows [kt*32, kt*32 + 32) x QROW bytes of
+// row-major X: a block holds 1024/QROW consecutive k-rows.
+template <class C, int KIND, int S>
+__device__ __forceinline__ void dma_block(const Src &src, int kt, int j, int wave, int lane) {
+    if (j < C::P_BLOCKS) {
+        const int blk = wave * C::P_BLOCKS + j;
+        const int row = blk * 16 + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+        dma16(src.p + row * src.ld_p + kt * 64 + chunk * 16, slot_p<S>() + blk * 1024);
+    } else if constexpr (KIND == APPLY) {
+        constexpr int UNITS = C::QROW / 16;  // 16-byte units per k-row
+        const int blk = wave * C::Q_BLOCKS + (j - C::P_BLOCKS);
+        const int krow = blk * (1024 / C::QROW) + lane / UNITS;
+        const int u = lane % UNITS;
+        const int byte = ((((u >> 2) ^ (krow & 3))) << 6) + ((u & 3) << 4);
+        dma16(src.q + (static_cast<int64_t>(kt) * C::BK + krow) * src.ld_q + byte, slot_q<S>() + blk * 1024);
+    } else {
+        const int blk = wave * C::Q_BLOCKS + (j - C::P_BLOCKS);
+        const int row = blk * 16 + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+        dma16(src.q + row * src.ld_q + kt * 64 + chunk * 16, slot_q<S>() + blk * 1024);
     }
 }
 
-// 4-stage ring; nk is a multiple of 8.  Before step kt, stages kt, kt+1, kt+2
-// may be outstanding (2 x LPS newer loads allowed); the last steps drain.
+// Fragments of one 16-k substep: MI P-fragments and NI Q-fragments (8 bf16 =
+// 16 bytes each per lane).
+struct Frags {
+    u32x4 a[Cfg::MI];
+    u32x4 b[Cfg::NI];
+};
+
+// Reads fragment j of substep ks (0 or 1) of the stage in slot S, in the order
+// the products consume them: a0, b0 .. b(NI-1), a1 .. a(MI-1).
+template <class C, int KIND, int S>
+__device__ __forceinline__ void read_frag(Frags &f, int j, int ks, int wm, int wn, int lane) {
+    const bool is_a = j == 0 || j > C::NI;
+    const int idx = j == 0 ? 0 : (j <= C::NI ? j - 1 : j - C::NI);
+    const int chunk = 2 * ks + (lane >> 5);  // k = 8*chunk .. 8*chunk+7 of this stage
+    if (is_a) {
+        const int row = wm * C::WM + idx * 32 + (lane & 31);
+        f.a[idx] = *reinterpret_cast<const u32x4 *>(slot_p<S>() + kc_offset(row, chunk));
+    } else if constexpr (KIND == APPLY) {
+        // Lane jj of each 16-lane group supplies k-row kbase + jj/4, columns
+        // n0 + 4(jj%4) .. +3; lane i then holds X[kbase .. kbase+3][n0 + i].
+        const int grp = lane >> 4, jj = lane & 15;
+        const int n0 = wn * C::WN + idx * 32 + 16 * (grp & 1);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int krow = 16 * ks + 8 * (grp >> 1) + 4 * r + (jj >> 2);
+            const int byte = (n0 + 4 * (jj & 3)) * 2;
+            const bf16x4_tr t =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(slot_q<S>() + nc_offset<C>(krow, byte)));
+            const u32x2 tt = __builtin_bit_cast(u32x2, t);
+            f.b[idx][2 * r] = tt[0];
+            f.b[idx][2 * r + 1] = tt[1];
+        }
+    } else {
+        const int row = wn * C::WN + idx * 32 + (lane & 31);
+        f.b[idx] = *reinterpret_cast<const u32x4 *>(slot_q<S>() + kc_offset(row, chunk));
+    }
+}
+
+// Product i of a substep: acc[mi][ni] += with mi = i / NI, ni = i % NI.  The
+// operands are swapped (the Q fragment is the MFMA's first operand), which
+// leaves the transposed 32 x 32 block in the accumulator: each lane then holds
+// four consecutive output columns of one output row, so the epilogues move 16
+// bytes per access.
+template <class C>
+__device__ __forceinline__ void mma_one(floatx16 (&acc)[C::MI][C::NI], const Frags &f, int i) {
+    const int mi = i / C::NI, ni = i % C::NI;
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.b[ni]),
+                                                          __builtin_bit_cast(bf16x8, f.a[mi]), acc[mi][ni], 0, 0, 0);
+}
+
+// Stage kt, held in slot S (= kt mod 4).  Every product is followed by at
+// most one fragment read and one DMA, and a scheduling fence keeps that
+// order, so LDS reads and global->LDS copies proceed under the MFMAs.
+//   Part A: products of substep 0 (fa); reads of substep 1 (fb); DMA of the
+//           second half of stage kt+3 (slot (S+3) mod 4, released at the
+//           previous stage's barrier).
+//   Wait for this wave's DMA of stage kt+1 (WAIT newer loads may remain:
+//   stages kt+2 and kt+3) and for its own LDS reads, then the barrier: stage
+//   kt+1 has landed everywhere and no wave reads slot S any more.
+//   Part B: products of fb; reads of substep 0 of stage kt+1 into fa; DMA of
+//           the first half of stage kt+4 into slot S.
+// ISSUE_A / ISSUE_B drop the DMA past the last stage; LAST ends after Part A.
+template <class C, int KIND, int S, int WAIT, bool ISSUE_A, bool ISSUE_B, bool LAST>
+__device__ __forceinline__ void ring_stage(floatx16 (&acc)[C::MI][C::NI], const Src &src, int kt, int wave, int wm,
+                                           int wn, int lane, Frags &fa, Frags &fb) {
+    constexpr int H = C::LPS / 2, EVERY = C::NM / H;
+#pragma unroll
+    for (int i = 0; i < C::NM; ++i) {
+        mma_one<C>(acc, fa, i);
+        if (i < C::NF) read_frag<C, KIND, S>(fb, i, 1, wm, wn, lane);
+        if (ISSUE_A && i % EVERY == EVERY / 2) dma_block<C, KIND, (S + 3) % 4>(src, kt + 3, H + i / EVERY, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (LAST) {
+#pragma unroll
+        for (int i = 0; i < C::NM; ++i) mma_one<C>(acc, fb, i);
+    } else {
+        wait_lgkm0();
+        wait_vmcnt<WAIT>();
+        stage_barrier();
+#pragma unroll
+        for (int i = 0; i < C::NM; ++i) {
+            mma_one<C>(acc, fb, i);
+            if (i < C::NF) read_frag<C, KIND, (S + 1) % 4>(fa, i, 0, wm, wn, lane);
+            if (ISSUE_B && i % EVERY == EVERY / 2) dma_block<C, KIND, S>(src, kt + 4, i / EVERY, wave, lane);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// The K loop over nk stages (nk a multiple of 4, at least 8).  Stages 0..2 and
+// the first half of stage 3 are loaded up front; loads retire in issue
+// order, so vmcnt(2 LPS + LPS/2) leaves exactly those after stage 0 in flight.
 template <class C, int KIND>
-__device__ __forceinline__ void main_loop4(floatx16 (&acc)[C::MI][C::NI], const Src &src, int nk, int wave, int wm,
-                                           int wn, int lane) {
-    static_assert(C::STAGES == 4, "ring depth");
-    constexpr int W2 = 2 * C::LPS, W1 = C::LPS;
-    issue_stage<C, KIND, 0>(src.p, src.ld_p, src.q, src.ld_q, 0, wave, lane);
-    issue_stage<C, KIND, 1>(src.p, src.ld_p, src.q, src.ld_q, 1, wave, lane);
-    issue_stage<C, KIND, 2>(src.p, src.ld_p, src.q, src.ld_q, 2, wave, lane);
+__device__ __forceinline__ void main_loop(floatx16 (&acc)[C::MI][C::NI], const Src &src, int nk, int wave, int wm,
+                                          int wn, int lane) {
+    static_assert(C::STAGES == 4 && C::LPS % 2 == 0 && C::NM % (C::LPS / 2) == 0 && C::NF <= C::NM, "interleave");
+    constexpr int L = C::LPS, H = C::LPS / 2;
+#pragma unroll
+    for (int j = 0; j < L; ++j) dma_block<C, KIND, 0>(src, 0, j, wave, lane);
+#pragma unroll
+    for (int j = 0; j < L; ++j) dma_block<C, KIND, 1>(src, 1, j, wave, lane);
+#pragma unroll
+    for (int j = 0; j < L; ++j) dma_block<C, KIND, 2>(src, 2, j, wave, lane);
+#pragma unroll
+    for (int j = 0; j < H; ++j) dma_block<C, KIND, 3>(src, 3, j, wave, lane);
+    wait_vmcnt<2 * L + H>();
+    stage_barrier();
+    Frags fa, fb;
+#pragma unroll
+    for (int j = 0; j < C::NF; ++j) read_frag<C, KIND, 0>(fa, j, 0, wm, wn, lane);
     int kt = 0;
     for (; kt < nk - 4; kt += 4) {
-        pipeline_step<C, KIND, 0, W2, true>(acc, src, kt, wave, wm, wn, lane);
-        pipeline_step<C, KIND, 1, W2, true>(acc, src, kt + 1, wave, wm, wn, lane);
-        pipeline_step<C, KIND, 2, W2, true>(acc, src, kt + 2, wave, wm, wn, lane);
-        pipeline_step<C, KIND, 3, W2, true>(acc, src, kt + 3, wave, wm, wn, lane);
+        ring_stage<C, KIND, 0, 2 * L, true, true, false>(acc, src, kt, wave, wm, wn, lane, fa, fb);
+        ring_stage<C, KIND, 1, 2 * L, true, true, false>(acc, src, kt + 1, wave, wm, wn, lane, fa, fb);
+        ring_stage<C, KIND, 2, 2 * L, true, true, false>(acc, src, kt + 2, wave, wm, wn, lane, fa, fb);
+        ring_stage<C, KIND, 3, 2 * L, true, true, false>(acc, src, kt + 3, wave, wm, wn, lane, fa, fb);
     }
-    pipeline_step<C, KIND, 0, W2, true>(acc, src, kt, wave, wm, wn, lane);
-    pipeline_step<C, KIND, 1, W2, false>(acc, src, kt + 1, wave, wm, wn, lane);
-    pipeline_step<C, KIND, 2, W1, false>(acc, src, kt + 2, wave, wm, wn, lane);
-    pipeline_step<C, KIND, 3, 0, false>(acc, src, kt + 3, wave, wm, wn, lane);
-}
-
-// 3-stage ring; nk >= 8.  Stage kt lives in slot (kt + off) % 3 with off
-// chosen so the last two (draining) stages always sit in slots 0 and 1; the
-// nk-2 issuing steps are a prefix of 0..2 steps and whole groups of three.
-template <class C, int KIND>
-__device__ __forceinline__ void main_loop3(floatx16 (&acc)[C::MI][C::NI], const Src &src, int nk, int wave, int wm,
-                                           int wn, int lane) {
-    static_assert(C::STAGES == 3, "ring depth");
-    constexpr int W1 = C::LPS;
-    const int rest = (nk - 2) % 3;
-    int kt = 0;
-    if (rest == 0) {
-        issue_stage<C, KIND, 0>(src.p, src.ld_p, src.q, src.ld_q, 0, wave, lane);
-        issue_stage<C, KIND, 1>(src.p, src.ld_p, src.q, src.ld_q, 1, wave, lane);
-    } else if (rest == 1) {
-        issue_stage<C, KIND, 2>(src.p, src.ld_p, src.q, src.ld_q, 0, wave, lane);
-        issue_stage<C, KIND, 0>(src.p, src.ld_p, src.q, src.ld_q, 1, wave, lane);
-        pipeline_step<C, KIND, 2, W1, true>(acc, src, 0, wave, wm, wn, lane);
-        kt = 1;
-    } else {
-        issue_stage<C, KIND, 1>(src.p, src.ld_p, src.q, src.ld_q, 0, wave, lane);
-        issue_stage<C, KIND, 2>(src.p, src.ld_p, src.q, src.ld_q, 1, wave, lane);
-        pipeline_step<C, KIND, 1, W1, true>(acc, src, 0, wave, wm, wn, lane);
-        pipeline_step<C, KIND, 2, W1, true>(acc, src, 1, wave, wm, wn, lane);
-        kt = 2;
-    }
-    for (; kt < nk - 2; kt += 3) {
-        pipeline_step<C, KIND, 0, W1, true>(acc, src, kt, wave, wm, wn, lane);
-        pipeline_step<C, KIND, 1, W1, true>(acc, src, kt + 1, wave, wm, wn, lane);
-        pipeline_step<C, KIND, 2, W1, true>(acc, src, kt + 2, wave, wm, wn, lane);
-    }
-    pipeline_step<C, KIND, 0, W1, false>(acc, src, kt, wave, wm, wn, lane);
-    pipeline_step<C, KIND, 1, 0, false>(acc, src, kt + 1, wave, wm, wn, lane);
+    ring_stage<C, KIND, 0, 2 * L, true, false, false>(acc, src, kt, wave, wm, wn, lane, fa, fb);
+    ring_stage<C, KIND, 1, L, false, false, false>(acc, src, kt + 1, wave, wm, wn, lane, fa, fb);
+    ring_stage<C, KIND, 2, 0, false, false, false>(acc, src, kt + 2, wave, wm, wn, lane, fa, fb);
+    ring_stage<C, KIND, 3, 0, false, false, true>(acc, src, kt + 3, wave, wm, wn, lane, fa, fb);
 }
 
 // DMA of EPI_ROWS rows x 64 fp32 (256 bytes per row) starting at `src` (row
@@ -359,7 +322,7 @@ __device__ __forceinline__ void dma_epi(char *dst, const char *src, int64_t ld, 
     for (int t = 0; t < C::EPI_ROWS / 4; ++t) {
         const int row = 4 * t + (lane >> 4);
         const int chunk = (lane & 15) ^ (row & 15);
-        __builtin_amdgcn_global_load_lds(src + row * ld + chunk * 16, (lds_void_t *)(dst + t * 1024), 16, 0, 0);
+        dma16(src + row * ld + chunk * 16, dst + t * 1024);
     }
 }
 
@@ -373,7 +336,7 @@ __device__ __forceinline__ void dma_bf16_rows(char *dst, const char *src, int64_
     for (int t = 0; t < C::EPI_ROWS / 8; ++t) {
         const int row = 8 * t + (lane >> 3);
         const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-        __builtin_amdgcn_global_load_lds(src + row * ld + chunk * 16, (lds_void_t *)(dst + t * 1024), 16, 0, 0);
+        dma16(src + row * ld + chunk * 16, dst + t * 1024);
     }
 }
 __device__ __forceinline__ int pair_offset(int row, int col) {
@@ -389,19 +352,6 @@ __device__ __forceinline__ void tri_decode(int64_t t, int *ti, int *tj) {
 }
 
 // ------------------------------------------------------------------------ A, B
-
-// Epilogue staging areas of the 8-wave GRAM/POLY kernel (8 KB each, inside
-// the operand ring, free once every wave has left the main loop): the first
-// area of wave w lies in p(w/2), the second in q(w/2).
-template <int WHICH> __device__ __forceinline__ char *sym_area(int wave) {
-    const int off = (wave & 1) * 8192;
-    switch (wave >> 1) {
-        case 0: return (WHICH ? lds_q0 : lds_p0) + off;
-        case 1: return (WHICH ? lds_q1 : lds_p1) + off;
-        case 2: return (WHICH ? lds_q2 : lds_p2) + off;
-        default: return (WHICH ? lds_q3 : lds_p3) + off;
-    }
-}
 
 // Epilogue of GRAM and POLY.  The wave's 128 x 64 block is finished in four
 // rounds of 32 rows staged in LDS.  POLY first brings the matching rows of the
@@ -511,7 +461,7 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
 }
 
 template <class C, int KIND>
-__global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void ns_sym_kernel(Geom g, Work w, NsStep p,
+__global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep p,
                                                                           int64_t tiles_per_mat, int64_t nblocks) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -545,13 +495,13 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void ns_sym_kernel(Geom g
         for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-    main_loop4<C, KIND>(acc, src, static_cast<int>(kdim / C::BK), wave, wm, wn, lane);
+    main_loop<C, KIND>(acc, src, static_cast<int>(kdim / C::BK), wave, wm, wn, lane);
 
     // acc[mi][ni][4*c4 + q] holds output row wm*WM + mi*32 + lane%32, column
     // wn*WN + ni*32 + 8*c4 + 4*(lane/32) + q of the tile.
     wait_lgkm0();
     stage_barrier();  // every wave is done with the operand ring
-    char *const area[2] = {sym_area<0>(wave), sym_area<1>(wave)};
+    char *const area[2] = {epi_area<0>(wave), epi_area<1>(wave)};
     sym_epilogue<C, KIND>(acc, g, w, p, e, ti, tj, wm, wn, area, lane);
 }
 
@@ -618,10 +568,10 @@ __device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char
 // every vector-memory instruction retires in issue order, so the wait before
 // round h allows exactly the instructions issued after round h's DMA: round
 // h-1's stores and round h+1's DMA.
-__device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Pair::MI][Pair::NI], const Geom &g,
+__device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::MI][Cfg::NI], const Geom &g,
                                                     const Work &w, const NsStep &p, const ApplyTile &t,
                                                     char *const (&area)[2], int lane) {
-    using C = Pair;
+    using C = Cfg;
     constexpr int ROUNDS = C::WM / C::EPI_ROWS;
     constexpr int DMA_PER_ROUND = 2 * (C::EPI_ROWS / 8);
     constexpr int STORES_PER_ROUND = 2 * (C::EPI_ROWS / 4);
@@ -724,10 +674,10 @@ __device__ __forceinline__ void update_row4(const MatDesc &d, const Geom &g, con
 // layout already puts 32 consecutive X' rows, i.e. 32 consecutive elements of
 // a W row, in consecutive lanes.
 template <int PARAM_BF16>
-__device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Pair::MI][Pair::NI], const MatDesc &d,
+__device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Cfg::MI][Cfg::NI], const MatDesc &d,
                                                       const Geom &g, const Work &w, const NsStep &p,
                                                       const ApplyTile &t, char *reg, int lane) {
-    using C = Pair;
+    using C = Cfg;
     constexpr int ROUNDS = C::WM / C::EPI_ROWS;
     static_assert(C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
     const int64_t first = t.row0 * g.lp + t.col0;
@@ -769,9 +719,9 @@ __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Pair
 }
 
 template <int PARAM_BF16>
-__global__ __launch_bounds__(Pair::NT, 2) void ns_apply_kernel(const MatDesc *__restrict__ descs, Geom g, Work w,
+__global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__restrict__ descs, Geom g, Work w,
                                                                NsStep p, int64_t tiles_per_mat, int64_t nblocks) {
-    using C = Pair;
+    using C = Cfg;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int64_t L = xcd_swizzle(blockIdx.x, nblocks);
@@ -795,7 +745,7 @@ __global__ __launch_bounds__(Pair::NT, 2) void ns_apply_kernel(const MatDesc *__
         for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-    main_loop3<C, APPLY>(acc, src, static_cast<int>(g.sp / C::BK), wave, wm, wn, lane);
+    main_loop<C, APPLY>(acc, src, static_cast<int>(g.sp / C::BK), wave, wm, wn, lane);
 
     // Swapped product: acc[mi][ni][4*c4 + q] holds output row
     //   m = wm*WM + mi*32 + lane%32,  columns n = wn*WN + ni*32 + 8*c4 + 4*(lane/32) + q, q = 0..3
@@ -803,7 +753,7 @@ __global__ __launch_bounds__(Pair::NT, 2) void ns_apply_kernel(const MatDesc *__
     // rows, each wave loading its own slice with the DMA, then read back in
     // the accumulator layout.
     const ApplyTile t_{e, static_cast<int64_t>(ti) * C::BM + wm * C::WM, static_cast<int64_t>(tj) * C::BN + wn * C::WN};
-    char *const area[2] = {epi_first(wave), epi_second(wave)};
+    char *const area[2] = {epi_area<0>(wave), epi_area<1>(wave)};
     wait_lgkm0();
     stage_barrier();  // every wave is done with the operand ring
     if (p.final_update)
@@ -818,7 +768,7 @@ hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const 
                                 const NsStep &p, hipStream_t st) {
     using namespace bf16path;
     if (kind == GRAM || kind == POLY) {
-        using C = Big;
+        using C = Cfg;
         const int64_t nt = g.sp / C::BM;
         const int64_t tiles = nt * (nt + 1) / 2;
         const int64_t nblocks = tiles * nmat;
@@ -829,13 +779,13 @@ hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const 
             ns_sym_kernel<C, POLY><<<grid, block, 0, st>>>(g, w, p, tiles, nblocks);
         return hipGetLastError();
     }
-    const int64_t tiles = (g.sp / Pair::BM) * (g.lp / Pair::BN);
+    const int64_t tiles = (g.sp / Cfg::BM) * (g.lp / Cfg::BN);
     const int64_t nblocks = tiles * nmat;
     if (p.final_update && p.param_bf16)
-        hipLaunchKernelGGL(ns_apply_kernel<1>, dim3(static_cast<unsigned>(nblocks)), dim3(Pair::NT), 0, st, descs, g,
+        hipLaunchKernelGGL(ns_apply_kernel<1>, dim3(static_cast<unsigned>(nblocks)), dim3(Cfg::NT), 0, st, descs, g,
                            w, p, tiles, nblocks);
     else
-        hipLaunchKernelGGL(ns_apply_kernel<0>, dim3(static_cast<unsigned>(nblocks)), dim3(Pair::NT), 0, st, descs, g,
+        hipLaunchKernelGGL(ns_apply_kernel<0>, dim3(static_cast<unsigned>(nblocks)), dim3(Cfg::NT), 0, st, descs, g,
                            w, p, tiles, nblocks);
     return hipGetLastError();
 }
