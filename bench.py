@@ -62,6 +62,33 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": x.numel() * 4}), flush=True)
 
 
+def library_baseline(rows, cols, count):
+    """torch (hipBLASLt) bf16 batched products of the three Newton-Schulz
+    shapes over `count` matrices, dense and with contiguous operands: a
+    reference point for the fused kernels, not part of the Muon step."""
+    import torch
+    s, l = min(rows, cols), max(rows, cols)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = (torch.randn(count, s, l, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+    xt = x.transpose(1, 2).contiguous()
+    b = (torch.randn(count, s, s, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+    out = {}
+    for name, fn, flops in (("apply B@X", lambda: torch.bmm(b, x), 2.0 * count * s * s * l),
+                            ("gram X@X^T", lambda: torch.bmm(x, xt), 2.0 * count * s * s * l),
+                            ("poly B@B", lambda: torch.bmm(b, b), 2.0 * count * s * s * s)):
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(5):
+            fn()
+        t1.record()
+        t1.synchronize()
+        ms = t0.elapsed_time(t1) / 5
+        out[name] = {"ms": round(ms, 4), "dense_tflops": round(flops / ms / 1e9, 1)}
+    print(json.dumps({"library_bmm_bf16": out, "matrices": count, "shape": [s, l]}), flush=True)
+
+
 def cpu_baseline(rows, cols, count):
     """The oracle as it stands on one matrix of the batch; scaled to one step."""
     import numpy as np
@@ -92,9 +119,14 @@ def main():
     ap.add_argument("--experts", type=int, default=256)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB copy (reference for the HBM byte counters)")
+    ap.add_argument("--library-baseline", action="store_true",
+                    help="only time torch bf16 batched products of the same shapes (64 matrices)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.library_baseline:
+        library_baseline(2048, 7168, 64)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU work of a sharded "
