@@ -89,6 +89,36 @@ def library_baseline(rows, cols, count):
     print(json.dumps({"library_bmm_bf16": out, "matrices": count, "shape": [s, l]}), flush=True)
 
 
+def adamw_rate(ctx, torch, ms, stream, steps=5):
+    """The AdamW path on the 16B-MoE workload's embedding and head (two
+    102400 x 2048 fp32 tensors, 28 bytes per element per step), timed with the
+    library's per-launch events."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    tens = []
+    for _ in range(2):
+        shape = (102400, 2048)
+        p = torch.randn(shape, generator=gen, device="cuda") * 0.02
+        g = torch.randn(shape, generator=gen, device="cuda") * 1e-3
+        tens.append((p, g, torch.zeros_like(p), torch.zeros_like(p)))
+    descs = [ms.adamw_tensor(*t) for t in tens]
+    ctx.muon_adamw_step(descs, ms.adamw_hparams(step=1), stream)
+    torch.cuda.synchronize()
+    ctx.muon_profile_enable(True)
+    for i in range(steps):
+        ctx.muon_adamw_step(descs, ms.adamw_hparams(step=i + 2), stream)
+    torch.cuda.synchronize()
+    st = ctx.muon_profile_read()["adamw"]
+    ctx.muon_profile_enable(False)
+    gbs = st["bytes"] / st["total_ms"] / 1e6
+    log(f"  adamw              launches {st['launches']:5d}  avg {st['total_ms'] / st['launches']:9.4f} ms  "
+        f"{gbs:8.1f} GB/s")
+    del tens, descs
+    return {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "ms_per_step": round(st["total_ms"] / st["launches"], 4),
+            "workload": "embedding + head, 2 x 102400x2048 fp32, 28 B/elem"}
+
+
 def cpu_baseline(rows, cols, count):
     """The oracle as it stands on one matrix of the batch; scaled to one step."""
     import numpy as np
@@ -233,8 +263,10 @@ def main():
         "cpu_baseline": None,
         "pages_context": "NS adds ~5% training FLOPs (DeepSeek-V4 book ch. 6; no hardware given)",
     }
-    ctx.close()
     del grads, params, moms, mats
+    torch.cuda.empty_cache()
+    out["elementwise"]["adamw"] = adamw_rate(ctx, torch, ms, stream)
+    ctx.close()
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one matrix")
