@@ -43,15 +43,16 @@ struct Geom {
 //   xb_next + e*x_stride  where the current step writes X_hi: the product B X
 //                         reads whole column panels of X, so X_hi is
 //                         double-buffered
-//   xl      + e*x_stride  X_lo = bf16(X - X_hi), rewritten in place by the
-//                         tile that owns the elements (bf16 path)
+//   xl      + e*x_stride  X_lo, the 8-bit residual of X - X_hi (one byte per
+//                         element), rewritten in place by the tile that owns
+//                         the elements (bf16 path)
 //   af + e*a_stride       fp32 A = X X^T (sp x sp, lower-triangle tiles)
 //   ab + e*a_stride       A as MFMA operand (bf16 or fp32, both triangles)
 //   bb + e*a_stride       B = bA + cA^2 as MFMA operand (both triangles)
 // Newton-Schulz workspace of one chunk of same-shape matrices.  fp32 path: X
-// in xf / xf_next (fp32).  bf16 path: X as a pair of bf16 arrays, hi in
-// xb / xb_next (ping-pong: it is the operand every tile of the B X product
-// reads) and lo in xl (updated in place), xf == xf_next == nullptr.
+// in xf / xf_next (fp32).  bf16 path: X as hi (bf16) in xb / xb_next
+// (ping-pong: it is the operand every tile of the B X product reads) and the
+// 8-bit residual lo in xl (updated in place), xf == xf_next == nullptr.
 struct Work {
     float *xf;
     float *xf_next;
@@ -87,33 +88,54 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
-// A float kept as two bfloat16: hi = bf16(x), lo = bf16(x - hi).  x - hi is
-// exact in fp32 (hi is within half a bf16 ulp of x), so hi + lo carries x to
-// about 2^-17 relative, and hi + lo is exact in fp32.
-__device__ __forceinline__ void split_bf16(float x, uint16_t *hi, uint16_t *lo) {
+// A float kept as hi = bf16(x) and a signed 8-bit residual q:
+//   x ~= hi + q * 2^(e - 15),  e the exponent of hi,  q = rne((x - hi) 2^(15 - e))
+// clamped to [-128, 127].  x - hi is exact in fp32 and at most half a bf16
+// ulp (2^(e - 8)), so |q| <= 128 and the residual's rounding error is at most
+// 2^(e - 16), or 2^(e - 15) where q clamps: x is carried to 2^-15 relative
+// (2^-16 but for that clamp).  hi + q 2^(e - 15) spans at most 17 bits and is
+// exact in fp32.  Below 2^-111 (exponent field < 16) only hi's precision is
+// kept; infinite and NaN values are carried by hi alone.
+__device__ __forceinline__ uint32_t lo8_encode(float x, uint32_t hbits) {
+    // 2^(15 - e) from the exponent field, clamped to 16 .. 254: below 2^-111
+    // the residual is far under one step and rounds to 0; for infinite or NaN
+    // hi the residual is NaN, which converts to 0.
+    const uint32_t ex = min(max((hbits >> 7) & 0xffu, 16u), 254u);
+    const float t = (x - __uint_as_float(hbits << 16)) * __uint_as_float((269u - ex) << 23);  // exact
+    const int q = min(max(static_cast<int>(rintf(t)), -128), 127);
+    return static_cast<uint32_t>(q) & 0xffu;
+}
+// The residual of hi (hi's bits in the low 16 of hbits): q * 2^(e - 15), with
+// the exponent taken from hi's bits and capped at 2^127 so that infinite or
+// NaN hi (whose q is 0) gives 0.
+__device__ __forceinline__ float lo8_decode(uint32_t qbyte, uint32_t hbits) {
+    const float pow2e = __uint_as_float(min((hbits << 16) & 0x7f800000u, 0x7f000000u));
+    return static_cast<float>(static_cast<int8_t>(qbyte & 0xffu)) * 0x1p-15f * pow2e;
+}
+__device__ __forceinline__ void split_bf16(float x, uint16_t *hi, uint8_t *lo) {
     const uint16_t h = float_to_bf16_bits(x);
     *hi = h;
-    *lo = float_to_bf16_bits(x - bf16_bits_to_float(h));
+    *lo = static_cast<uint8_t>(lo8_encode(x, h));
 }
-__device__ __forceinline__ float join_bf16(uint16_t hi, uint16_t lo) {
-    return bf16_bits_to_float(hi) + bf16_bits_to_float(lo);
+__device__ __forceinline__ float join_bf16(uint16_t hi, uint8_t lo) {
+    return bf16_bits_to_float(hi) + lo8_decode(lo, hi);
 }
-// Four consecutive values: hi and lo as packed bf16 pairs.
-__device__ __forceinline__ void split_bf16x4(const floatx4 &v, u32x2 *hi, u32x2 *lo) {
-    u32x2 h, l;
+// Four consecutive values: hi as packed bf16 pairs, the residuals as four
+// bytes of one word (value k in byte k).
+__device__ __forceinline__ void split_bf16x4(const floatx4 &v, u32x2 *hi, uint32_t *lo) {
+    u32x2 h;
     h[0] = pack_bf16x2(v[0], v[1]);
     h[1] = pack_bf16x2(v[2], v[3]);
-    l[0] = pack_bf16x2(v[0] - __uint_as_float(h[0] << 16), v[1] - __uint_as_float(h[0] & 0xffff0000u));
-    l[1] = pack_bf16x2(v[2] - __uint_as_float(h[1] << 16), v[3] - __uint_as_float(h[1] & 0xffff0000u));
     *hi = h;
-    *lo = l;
+    *lo = lo8_encode(v[0], h[0] & 0xffffu) | (lo8_encode(v[1], h[0] >> 16) << 8) |
+          (lo8_encode(v[2], h[1] & 0xffffu) << 16) | (lo8_encode(v[3], h[1] >> 16) << 24);
 }
-__device__ __forceinline__ floatx4 join_bf16x4(const u32x2 &h, const u32x2 &l) {
+__device__ __forceinline__ floatx4 join_bf16x4(const u32x2 &h, uint32_t l) {
     floatx4 v;
-    v[0] = __uint_as_float(h[0] << 16) + __uint_as_float(l[0] << 16);
-    v[1] = __uint_as_float(h[0] & 0xffff0000u) + __uint_as_float(l[0] & 0xffff0000u);
-    v[2] = __uint_as_float(h[1] << 16) + __uint_as_float(l[1] << 16);
-    v[3] = __uint_as_float(h[1] & 0xffff0000u) + __uint_as_float(l[1] & 0xffff0000u);
+    v[0] = __uint_as_float(h[0] << 16) + lo8_decode(l, h[0]);
+    v[1] = __uint_as_float(h[0] & 0xffff0000u) + lo8_decode(l >> 8, h[0] >> 16);
+    v[2] = __uint_as_float(h[1] << 16) + lo8_decode(l >> 16, h[1]);
+    v[3] = __uint_as_float(h[1] & 0xffff0000u) + lo8_decode(l >> 24, h[1] >> 16);
     return v;
 }
 

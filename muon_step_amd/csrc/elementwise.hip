@@ -75,7 +75,7 @@ __device__ __forceinline__ double block_sum(double v, double *sh) {
 struct XView {
     const float *xf;  // fp32 path; nullptr on the bf16 path
     const uint16_t *xh;
-    const uint16_t *xl;
+    const uint8_t *xl;
     __device__ __forceinline__ float at(int64_t i) const { return xf ? xf[i] : join_bf16(xh[i], xl[i]); }
 };
 
@@ -84,7 +84,7 @@ __device__ __forceinline__ void store_n(const Work &w, int64_t i, float v) {
     if (w.xf)
         w.xf[i] = v;
     else
-        split_bf16(v, static_cast<uint16_t *>(w.xb) + i, static_cast<uint16_t *>(w.xl) + i);
+        split_bf16(v, static_cast<uint16_t *>(w.xb) + i, static_cast<uint8_t *>(w.xl) + i);
 }
 
 // ---------------------------------------------------------------------------
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void nesterov_rows_kernel(const MatDesc *__res
     float *__restrict__ mp = d.mom;
     float *__restrict__ xf = w.xf ? w.xf + e * w.x_stride : nullptr;  // fp32 path
     uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb) + e * w.x_stride;  // bf16 path
-    uint16_t *__restrict__ xl = static_cast<uint16_t *>(w.xl) + e * w.x_stride;
+    uint8_t *__restrict__ xl = static_cast<uint8_t *>(w.xl) + e * w.x_stride;
     const int64_t r0 = rb * rows_per_block;
     const int64_t r1 = min<int64_t>(g.rows, r0 + rows_per_block);
     const int64_t cols = g.cols;
@@ -140,10 +140,11 @@ __global__ __launch_bounds__(256) void nesterov_rows_kernel(const MatDesc *__res
             if (xf) {
                 *reinterpret_cast<floatx4 *>(xf + dst) = no;
             } else {
-                u32x2 h, l;
+                u32x2 h;
+                uint32_t l;
                 split_bf16x4(no, &h, &l);
                 *reinterpret_cast<u32x2 *>(xh + dst) = h;
-                *reinterpret_cast<u32x2 *>(xl + dst) = l;
+                *reinterpret_cast<uint32_t *>(xl + dst) = l;
             }
         }
     } else {
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(256) void nesterov_tile_kernel(const MatDesc *__res
     float *__restrict__ mp = d.mom;
     float *__restrict__ xf = w.xf ? w.xf + e * w.x_stride : nullptr;  // fp32 path
     uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb) + e * w.x_stride;  // bf16 path
-    uint16_t *__restrict__ xl = static_cast<uint16_t *>(w.xl) + e * w.x_stride;
+    uint8_t *__restrict__ xl = static_cast<uint8_t *>(w.xl) + e * w.x_stride;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     double acc = 0.0;
     for (int r = 0; r < 16; ++r) {
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc *__res
 }
 
 // X_0 = N * inv_norm over the padded sp x lp extent (zeros outside s x l), in
-// place: fp32 in xf, or the bf16 pair in (xb, xl).  The bf16 path runs it only
+// place: fp32 in xf, or the pair (bf16 hi in xb, 8-bit residual in xl).  The bf16 path runs it only
 // for an empty schedule; otherwise its first step applies inv_norm itself.
 __global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int blocks_per_mat, int rows_per_block) {
     const int64_t e = blockIdx.x / blocks_per_mat;
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int bloc
     const bool split = w.xf == nullptr;
     float *__restrict__ xf = split ? nullptr : w.xf + e * w.x_stride;
     uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb) + e * w.x_stride;
-    uint16_t *__restrict__ xl = static_cast<uint16_t *>(w.xl) + e * w.x_stride;
+    uint8_t *__restrict__ xl = static_cast<uint8_t *>(w.xl) + e * w.x_stride;
     const int64_t r0 = rb * rows_per_block;
     const int64_t r1 = min<int64_t>(g.sp, r0 + rows_per_block);
     const int64_t cv = g.lp / 4;
@@ -258,30 +259,31 @@ __global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int bloc
             floatx4 n;
             if (split) {
                 // entries past column l of the N pair are never written: mask them
-                n = join_bf16x4(*reinterpret_cast<const u32x2 *>(xh + off), *reinterpret_cast<const u32x2 *>(xl + off));
+                n = join_bf16x4(*reinterpret_cast<const u32x2 *>(xh + off), *reinterpret_cast<const uint32_t *>(xl + off));
             } else {
                 n = *reinterpret_cast<const floatx4 *>(xf + off);
             }
             for (int q = 0; q < 4; ++q) v[q] = (j + q < g.l) ? n[q] * inv : 0.0f;
         }
         if (split) {
-            u32x2 h, l;
+            u32x2 h;
+            uint32_t l;
             split_bf16x4(v, &h, &l);
             *reinterpret_cast<u32x2 *>(xh + off) = h;
-            *reinterpret_cast<u32x2 *>(xl + off) = l;
+            *reinterpret_cast<uint32_t *>(xl + off) = l;
         } else {
             *reinterpret_cast<floatx4 *>(xf + off) = v;
         }
     }
 }
 
-// Zeros the padding (outside s x l, inside sp x lp) of the bf16 pair (xb, xl)
+// Zeros the padding (outside s x l, inside sp x lp) of the pair (xb, xl)
 // that the momentum pass leaves untouched.  Block (e, i) handles padded row i.
 __global__ __launch_bounds__(256) void pad_zero_kernel(Geom g, Work w) {
     const int64_t e = blockIdx.x / g.sp;
     const int64_t i = blockIdx.x % g.sp;
     uint16_t *xh = static_cast<uint16_t *>(w.xb) + e * w.x_stride + i * g.lp;
-    uint16_t *xl = static_cast<uint16_t *>(w.xl) + e * w.x_stride + i * g.lp;
+    uint8_t *xl = static_cast<uint8_t *>(w.xl) + e * w.x_stride + i * g.lp;
     for (int64_t j = (i < g.s ? g.l : 0) + threadIdx.x; j < g.lp; j += 256) {
         xh[j] = 0;
         xl[j] = 0;
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(256) void update_from_work_kernel(const MatDesc *__
     const MatDesc d = descs[e];
     ParamT *__restrict__ pp = static_cast<ParamT *>(d.param);
     const XView xv_{w.xf ? w.xf + e * w.x_stride : nullptr, static_cast<const uint16_t *>(w.xb) + e * w.x_stride,
-                    static_cast<const uint16_t *>(w.xl) + e * w.x_stride};
+                    static_cast<const uint8_t *>(w.xl) + e * w.x_stride};
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     if (g.transposed) {
         // X row = W col
@@ -557,7 +559,7 @@ hipError_t launch_update_from_work(const MatDesc *descs, int nmat, const Geom &g
 hipError_t launch_export_x(const Geom &g, const Work &w, float *out, hipStream_t st) {
     const int tc = static_cast<int>((g.cols + 63) / 64);
     const int nb = static_cast<int>(((g.rows + 63) / 64) * tc);
-    const XView x{w.xf, static_cast<const uint16_t *>(w.xb), static_cast<const uint16_t *>(w.xl)};
+    const XView x{w.xf, static_cast<const uint16_t *>(w.xb), static_cast<const uint8_t *>(w.xl)};
     hipLaunchKernelGGL(export_x_kernel, dim3(nb), dim3(256), 0, st, g, x, out, tc);
     return hipGetLastError();
 }

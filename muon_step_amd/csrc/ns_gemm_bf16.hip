@@ -30,8 +30,8 @@
 // the operands swapped, so each lane's accumulators hold four consecutive
 // columns of one output row; every epilogue stages its block through LDS in
 // rounds of 32 rows and stores whole rows (GRAM/POLY also store the block's
-// columns as rows of the mirrored tile; APPLY moves 8 bytes per output
-// element: X_hi and X_lo in and out).  Block ids are renumbered so one
+// columns as rows of the mirrored tile; APPLY moves 6 bytes per output
+// element: X_hi and its 8-bit residual X_lo in and out).  Block ids are renumbered so one
 // matrix's tiles share an XCD (and its L2).
 #include "common.hpp"
 #include "kernels.hpp"
@@ -326,7 +326,7 @@ __device__ __forceinline__ void dma_epi(char *dst, const char *src, int64_t ld, 
     }
 }
 
-// DMA of EPI_ROWS rows x 64 bf16 (128 bytes per row, X_hi or X_lo) starting
+// DMA of EPI_ROWS rows x 64 bf16 (128 bytes per row, X_hi) starting
 // at `src` (row pitch ld bytes) into a staging area: instructions of 8 rows
 // each; lane i carries row i/8, chunk i%8 stored at chunk (i%8) ^ ((row/2)%8),
 // so 16 consecutive rows reading one chunk touch 16 distinct bank groups.
@@ -341,6 +341,23 @@ __device__ __forceinline__ void dma_bf16_rows(char *dst, const char *src, int64_
 }
 __device__ __forceinline__ int pair_offset(int row, int col) {
     return row * 128 + ((((col >> 3) ^ ((row >> 1) & 7))) << 4) + ((col & 7) << 1);
+}
+
+// DMA of EPI_ROWS rows x 64 residual bytes (64 bytes per row, X_lo) starting
+// at `src` (row pitch ld bytes) into a staging area: instructions of 16 rows
+// each; lane i carries row i/4, chunk i%4 stored at chunk (i%4) ^ ((row/4)%4),
+// so 16 consecutive rows reading one 4-byte word touch 16 distinct banks.
+template <class C>
+__device__ __forceinline__ void dma_lo8_rows(char *dst, const char *src, int64_t ld, int lane) {
+#pragma unroll
+    for (int t = 0; t < C::EPI_ROWS / 16; ++t) {
+        const int row = 16 * t + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+        dma16(src + row * ld + chunk * 16, dst + t * 1024);
+    }
+}
+__device__ __forceinline__ int lo8_offset(int row, int col) {
+    return row * 64 + ((((col >> 4) ^ ((row >> 2) & 3))) << 4) + (col & 15);
 }
 
 __device__ __forceinline__ void tri_decode(int64_t t, int *ti, int *tj) {
@@ -515,13 +532,14 @@ struct ApplyTile {
 };
 
 // Row lrow's four columns lcol .. lcol+3 of (a X + B X) * scale, with
-// X = X_hi + X_lo staged in `reg` (X_hi rows in the first PAIR_HALF bytes,
-// X_lo rows after).  scale is 1, or inv_norm when X still holds N.
+// X = X_hi + X_lo staged in `reg` (X_hi rows, 128 bytes each, in the first
+// PAIR_HALF bytes; X_lo rows, 64 bytes each, after).  scale is 1, or inv_norm
+// when X still holds N.
 constexpr int PAIR_HALF = 4096;
 __device__ __forceinline__ floatx4 apply_value(const floatx16 &acc, const char *reg, int lrow, int lcol, int c4,
                                                float a, float scale) {
     const u32x2 h = *reinterpret_cast<const u32x2 *>(reg + pair_offset(lrow, lcol));
-    const u32x2 l = *reinterpret_cast<const u32x2 *>(reg + PAIR_HALF + pair_offset(lrow, lcol));
+    const uint32_t l = *reinterpret_cast<const uint32_t *>(reg + PAIR_HALF + lo8_offset(lrow, lcol));
     const floatx4 x = join_bf16x4(h, l);
     floatx4 v;
 #pragma unroll
@@ -564,7 +582,8 @@ __device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char
 // rows, then read row-contiguously (16 lanes per row) so the stores move whole
 // rows.  Two staging areas: the DMA of round h+2 is issued once round h's
 // reads are done, so one round is always in flight.  Per round and lane:
-// 2*EPI_ROWS/8 DMA instructions and 2*EPI_ROWS/4 stores, unconditionally;
+// EPI_ROWS/8 + EPI_ROWS/16 DMA instructions (X_hi, X_lo) and 2*EPI_ROWS/4
+// stores, unconditionally;
 // every vector-memory instruction retires in issue order, so the wait before
 // round h allows exactly the instructions issued after round h's DMA: round
 // h-1's stores and round h+1's DMA.
@@ -573,20 +592,20 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::M
                                                     char *const (&area)[2], int lane) {
     using C = Cfg;
     constexpr int ROUNDS = C::WM / C::EPI_ROWS;
-    constexpr int DMA_PER_ROUND = 2 * (C::EPI_ROWS / 8);
+    constexpr int DMA_PER_ROUND = C::EPI_ROWS / 8 + C::EPI_ROWS / 16;
     constexpr int STORES_PER_ROUND = 2 * (C::EPI_ROWS / 4);
     static_assert(ROUNDS == 4 && C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
     static_assert(C::EPI_ROWS * 128 == PAIR_HALF, "X_hi and X_lo rows fill one staging area");
-    uint16_t *xl = static_cast<uint16_t *>(w.xl) + t.e * w.x_stride;
+    uint8_t *xl = static_cast<uint8_t *>(w.xl) + t.e * w.x_stride;
     uint16_t *xh_out = static_cast<uint16_t *>(w.xb_next) + t.e * w.x_stride;
     const int64_t first = t.row0 * g.lp + t.col0;
     const char *hi_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xb) + t.e * w.x_stride + first);
     const char *lo_in = reinterpret_cast<const char *>(xl + first);
-    const int64_t ld = g.lp * 2;
+    const int64_t ld = g.lp * 2, ld_lo = g.lp;
     const float scale = p.unnormalized ? w.inv_norm[t.e] : 1.0f;
     auto dma_round = [&](char *dst, int h) {
         dma_bf16_rows<C>(dst, hi_in + C::EPI_ROWS * h * ld, ld, lane);
-        dma_bf16_rows<C>(dst + PAIR_HALF, lo_in + C::EPI_ROWS * h * ld, ld, lane);
+        dma_lo8_rows<C>(dst + PAIR_HALF, lo_in + C::EPI_ROWS * h * ld_lo, ld_lo, lane);
     };
     dma_round(area[0], 0);
     dma_round(area[1], 1);
@@ -610,10 +629,11 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::M
             for (int q = 0; q < 4; ++q)
                 if (gi >= g.s || gj + q >= g.l) v[q] = 0.0f;
             const int64_t idx = gi * g.lp + gj;
-            u32x2 hi, lo;
+            u32x2 hi;
+            uint32_t lo;
             split_bf16x4(v, &hi, &lo);
             *reinterpret_cast<u32x2 *>(xh_out + idx) = hi;
-            *reinterpret_cast<u32x2 *>(xl + idx) = lo;
+            *reinterpret_cast<uint32_t *>(xl + idx) = lo;
         }
         if (h + 2 < ROUNDS) {
             wait_lgkm0();  // this round's LDS reads are done before the DMA refills the area
@@ -682,13 +702,13 @@ __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Cfg:
     static_assert(C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
     const int64_t first = t.row0 * g.lp + t.col0;
     const char *hi_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xb) + t.e * w.x_stride + first);
-    const char *lo_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xl) + t.e * w.x_stride + first);
-    const int64_t ld = g.lp * 2;
+    const char *lo_in = reinterpret_cast<const char *>(static_cast<const uint8_t *>(w.xl) + t.e * w.x_stride + first);
+    const int64_t ld = g.lp * 2, ld_lo = g.lp;
     const float scale = p.unnormalized ? w.inv_norm[t.e] : 1.0f;
 #pragma unroll
     for (int h = 0; h < ROUNDS; ++h) {
         dma_bf16_rows<C>(reg, hi_in + C::EPI_ROWS * h * ld, ld, lane);
-        dma_bf16_rows<C>(reg + PAIR_HALF, lo_in + C::EPI_ROWS * h * ld, ld, lane);
+        dma_lo8_rows<C>(reg + PAIR_HALF, lo_in + C::EPI_ROWS * h * ld_lo, ld_lo, lane);
         fenced_wait_vmcnt<0>();
         const int lrow = lane & 31;
         if (g.transposed) {

@@ -227,7 +227,7 @@ struct GroupPlan {
 // Bytes of NS workspace one matrix of geometry g needs.
 size_t per_matrix_bytes(const Geom &g, bool bf16) {
     const size_t x = static_cast<size_t>(g.sp * g.lp), a = static_cast<size_t>(g.sp * g.sp);
-    return bf16 ? (x * (4 + 2 + 2) + a * (4 + 2 + 2)) : (x * (4 + 4) + a * (4 + 4 + 4));
+    return bf16 ? (x * (2 + 2 + 1) + a * (4 + 2 + 2)) : (x * (4 + 4) + a * (4 + 4 + 4));
 }
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
@@ -242,11 +242,11 @@ Layout chunk_layout(const Geom &g, bool bf16, int64_t n) {
     Layout L{};
     size_t off = 0;
     if (bf16) {
-        // X as the bf16 pair: hi ping-pong + lo (in place); no fp32 X.
+        // X as hi (bf16, ping-pong) + its 8-bit residual lo (in place); no fp32 X.
         L.has_xf = false;
         L.xb0 = off; off = align_up(off + x * 2);
         L.xb1 = off; off = align_up(off + x * 2);
-        L.xl = off; off = align_up(off + x * 2);
+        L.xl = off; off = align_up(off + x * 1);
         L.af = off; off = align_up(off + a * 4);
         L.ab = off; off = align_up(off + a * 2);
         L.bb = off; off = align_up(off + a * 2);
@@ -521,13 +521,13 @@ void ns_work(int stage, const Geom &g, bool bf16, int n, bool ns_out, int psize,
             *bytes = s * s * es + s * (s + 1) / 2 * 4 + s * s * es;
             break;
         case ST_APPLY:
-            // B, X operand, then X_lo in and (X_hi, X_lo) out; fp32 path: X in, X out
+            // B, X operand, then X_lo in and (X_hi, X_lo) out (2 + 1 bytes); fp32 path: X in, X out
             *flops = 2 * s * s * l;
-            *bytes = s * s * es + s * l * es + (bf16 ? s * l * 6 : s * l * 8);
+            *bytes = s * s * es + s * l * es + (bf16 ? s * l * 4 : s * l * 8);
             break;
         default:  // ST_APPLY_UPDATE
             *flops = 2 * s * s * l;
-            *bytes = s * s * es + s * l * es + s * l * (bf16 ? 2 : 4) + s * l * 2.0 * psize + (ns_out ? s * l * 4 : 0);
+            *bytes = s * s * es + s * l * es + s * l * (bf16 ? 1 : 4) + s * l * 2.0 * psize + (ns_out ? s * l * 4 : 0);
             break;
     }
     *flops *= n;
@@ -547,10 +547,10 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
     const bool fold = bf16 && hp->num_ns_steps > 0;
     hipError_t e = hipSuccess;
     if (!fold) {
-        e = timed(ctx, ST_NORMALIZE, 0.0, xe * 8.0, st, [&] { return muon::launch_normalize(nmat, g, w, st); });
+        e = timed(ctx, ST_NORMALIZE, 0.0, xe * (bf16 ? 6.0 : 8.0), st, [&] { return muon::launch_normalize(nmat, g, w, st); });
     } else if (g.sp > g.s || g.lp > g.l) {
         const double pad = (static_cast<double>(g.sp) * g.lp - static_cast<double>(g.s) * g.l) * nmat;
-        e = timed(ctx, ST_NORMALIZE, 0.0, pad * 4.0, st, [&] { return muon::launch_pad_zero(nmat, g, w, st); });
+        e = timed(ctx, ST_NORMALIZE, 0.0, pad * 3.0, st, [&] { return muon::launch_pad_zero(nmat, g, w, st); });
     }
     if (e != hipSuccess) return hip_fail(ctx, e, "normalize launch");
     const int psize = param_bf16 ? 2 : 4;
@@ -743,7 +743,8 @@ muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count,
             Work w = chunk_work(ctx, gp.g, bf16, n, gp.bpm, count);
             const double elems = static_cast<double>(gp.g.rows) * gp.g.cols * n;
             const double gsz = gp.grad_dtype == MUON_BF16 ? 2.0 : 4.0;
-            hipError_t e = timed(ctx, ST_MOMENTUM, 0.0, elems * (gsz + 12.0), st, [&] {
+            // M read and written (8), N written: fp32 (4) or hi + residual (3)
+            hipError_t e = timed(ctx, ST_MOMENTUM, 0.0, elems * (gsz + (bf16 ? 11.0 : 12.0)), st, [&] {
                 return muon::launch_nesterov(dd, n, gp.g, w, mu, hp->nesterov, gp.grad_dtype == MUON_BF16, vec_ok,
                                              st);
             });
