@@ -252,7 +252,7 @@ def main():
         "data": "synthetic (seeded low-rank-plus-noise bf16 gradients, N(0,0.02) bf16 params, zero fp32 momentum)",
         "config": {"workload": "moe_256x2048x7168_bf16", "matrices": count, "shape": [rows, cols],
                    "ns_steps": 10, "schedule": "deepseekv4 8x(3.4445,-4.7750,2.0315)+2x(2,-1.5,0.5)",
-                   "ns_precision": "bf16 MFMA operands, fp32 accumulate, X kept as a bf16 (hi, lo) pair",
+                   "ns_precision": "bf16 MFMA operands, fp32 accumulate, X kept as bf16 hi + 8-bit residual",
                    "lr": 0.02, "momentum": 0.95, "weight_decay": 0.1, "gamma": 0.2},
         "ns_tflops": round(ns_tflops, 2),
         "ns_frac_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4),

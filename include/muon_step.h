@@ -58,9 +58,9 @@ typedef enum muon_dtype {
 
 /* Arithmetic of the Newton-Schulz products.
  * MUON_NS_BF16: bf16 MFMA operands, fp32 accumulation; between iterations X
- *               is kept as a pair of bf16 arrays hi + lo (hi = bf16(x),
- *               lo = bf16(x - hi): ~16 significant bits), hi being the MFMA
- *               operand (relative Frobenius error vs fp64 ~1e-2).
+ *               is kept as hi = bf16(x) plus an 8-bit residual of x - hi
+ *               (~16 significant bits), hi being the MFMA operand (relative
+ *               Frobenius error vs fp64 ~1e-2).
  *               Matrices whose smaller side is at most 16 use the fp32
  *               products instead (too few singular directions for the bf16
  *               rounding of X to average out; their cost is negligible).
