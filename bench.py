@@ -119,6 +119,78 @@ def adamw_rate(ctx, torch, ms, stream, steps=5):
             "workload": "embedding + head, 2 x 102400x2048 fp32, 28 B/elem"}
 
 
+def moe16b_step(args):
+    """Times the full synthetic 16B-MoE optimizer step (27 layers: 4 x 2048^2
+    attention matrices and 64 experts x (2048x1408 up, gate; 1408x2048 down),
+    Muon on all 5292 matrices in one call, then AdamW on the 102400x2048
+    embedding and head) and prints one JSON line of its own."""
+    import torch
+
+    import muon_step_amd as ms
+    import synth
+
+    wl = synth.WORKLOADS["moe16b_full_step"]
+    specs = list(wl.matrices)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.base_seed)
+    log(f"generating the 16B-MoE step: {len(specs)} Muon matrices + AdamW")
+    by_shape = {}
+    for i, sp in enumerate(specs):
+        by_shape.setdefault((sp.rows, sp.cols), []).append(i)
+    grads = [None] * len(specs)
+    for (rows, cols), ids in by_shape.items():
+        g = synth.spectral_grad_torch(rows, cols, len(ids), gen, "cuda")
+        for k, i in enumerate(ids):
+            grads[i] = g[k]
+    params = [(torch.randn(sp.rows, sp.cols, generator=gen, device="cuda") * synth.gen.PARAM_STD).to(torch.bfloat16)
+              for sp in specs]
+    moms = [torch.zeros(sp.rows, sp.cols, device="cuda") for sp in specs]
+    mats = [ms.matrix(params[i], grads[i], moms[i]) for i in range(len(specs))]
+    adamw_bufs = []  # the descriptors hold raw pointers: keep every tensor alive
+    for _, n in wl.adamw:
+        p = torch.randn(n, generator=gen, device="cuda") * synth.gen.PARAM_STD
+        adamw_bufs.append((p, torch.randn(n, generator=gen, device="cuda") * 1e-3, torch.zeros_like(p),
+                           torch.zeros_like(p)))
+    tensors = [ms.adamw_tensor(*b) for b in adamw_bufs]
+    hp = ms.make_hparams(lr=0.02, momentum=0.95, weight_decay=0.1, gamma=0.2, nesterov=True,
+                         ns_precision=ms.MUON_NS_BF16)
+    ctx = ms.Context(0, args.workspace_gib << 30)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        ctx.muon_step(mats, hp, stream)
+        ctx.muon_adamw_step(tensors, ms.adamw_hparams(step=i + 1), stream)
+
+    for i in range(args.warmup):
+        step(i)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    ctx.muon_profile_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    stages = ctx.muon_profile_read()
+    ctx.close()
+    ns_ms = sum(stages[k]["total_ms"] for k in NS_STAGES if k in stages)
+    ns_flops = sum(stages[k]["flops"] for k in NS_STAGES if k in stages)
+    breakdown = {k: round(v["total_ms"] / args.steps, 3) for k, v in stages.items()}
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; per stage (ms/step): {breakdown}")
+    print(json.dumps({
+        "metric": "16B-MoE optimizer step (Muon on 5292 matrices + AdamW on embedding and head)",
+        "value": round(1000.0 / ms_per_step, 4), "unit": "steps/s", "ms_per_step": round(ms_per_step, 3),
+        "steps": args.steps, "warmup": args.warmup, "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "moe16b_full_step", "muon_matrices": len(specs),
+                   "workspace_cap_gib": args.workspace_gib},
+        "ns_tflops": round(ns_flops / ns_ms / 1e9, 2) if ns_ms else None,
+        "ns_frac_bf16_peak": round(ns_flops / ns_ms / 1e9 / PEAK_BF16_TFLOPS, 4) if ns_ms else None,
+        "stage_ms_per_step": breakdown}), flush=True)
+
+
 def cpu_baseline(rows, cols, count):
     """The oracle as it stands on one matrix of the batch; scaled to one step."""
     import numpy as np
@@ -149,6 +221,10 @@ def main():
     ap.add_argument("--experts", type=int, default=256)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB copy (reference for the HBM byte counters)")
+    ap.add_argument("--workload", default="moe_256x2048x7168_bf16",
+                    choices=["moe_256x2048x7168_bf16", "moe16b"],
+                    help="moe16b: time the full 16B-MoE optimizer step instead (own JSON line)")
+    ap.add_argument("--workspace-gib", type=int, default=64, help="NS workspace cap for --workload moe16b")
     ap.add_argument("--library-baseline", action="store_true",
                     help="only time torch bf16 batched products of the same shapes (64 matrices)")
     args = ap.parse_args()
@@ -163,6 +239,9 @@ def main():
               "run is the same grouped kernel on that GPU's share of matrices); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "moe16b":
+        moe16b_step(args)
+        return
 
     import torch
 

@@ -31,8 +31,8 @@
 // columns of one output row; every epilogue stages its block through LDS in
 // rounds of 32 rows and stores whole rows (GRAM/POLY also store the block's
 // columns as rows of the mirrored tile; APPLY moves 6 bytes per output
-// element: X_hi and its 8-bit residual X_lo in and out).  Block ids are renumbered so one
-// matrix's tiles share an XCD (and its L2).
+// element: X_hi and its 8-bit residual X_lo in and out).  Block ids are
+// renumbered so one matrix's tiles share an XCD (and its L2).
 #include "common.hpp"
 #include "kernels.hpp"
 
