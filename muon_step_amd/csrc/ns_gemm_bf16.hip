@@ -18,11 +18,12 @@
 // Data movement.  All three products use 256 x 256 tiles, one workgroup of
 // 8 waves per CU (two per SIMD), each wave owning a 128 x 64 block computed
 // with v_mfma_f32_32x32x16_bf16 into fp32 accumulators.  Operand slabs of
-// 32 k are copied global -> LDS by the 16-byte-per-lane DMA
-// (global_load_lds_dwordx4) into a 4-stage ring (128 KB).  Within a stage
-// every product is followed by at most one fragment read for the next 16-k
-// substep and one DMA for a later stage, so LDS reads and copies run under
-// the MFMAs; one barrier per stage, between its two substeps.  The LDS
+// 64 k (one 128-byte line per row) are copied global -> LDS by the
+// 16-byte-per-lane DMA (global_load_lds_dwordx4) into a ring of two stages
+// (128 KB).  Every product is followed by at most one fragment read for the
+// next 16-k substep; the last of a stage's four substeps also refills the
+// slot just read with the stage after next, so LDS reads and copies run
+// under the MFMAs; one barrier per stage, before its last substep.  The LDS
 // layouts are XOR-swizzled so that every 16-lane phase of a fragment read
 // touches all 64 banks once.  The X operand of B X is stored as it lies in
 // memory (k rows, n contiguous) and read with ds_read_b64_tr_b16, which hands
@@ -43,17 +44,22 @@ enum Kind { GRAM = 0, POLY = 1, APPLY = 2 };
 
 // Tile geometry shared by the three products: 256 x 256 output tiles, 8
 // waves (two per SIMD, one workgroup per CU), each owning a 128 x 64 block,
-// and a ring of four 32-k stages.
+// and a ring of two 64-k stages (128 KB of LDS).  64 k of bf16 is one 128-byte
+// line per row, so every DMA instruction moves whole lines: DMA that moves
+// half lines (32-k stages) runs at half the rate through the L1 path.
 struct Cfg {
     static constexpr int NT = 512, NWAVES = NT / 64;
     static constexpr int BM = 256, BN = 256;
     static constexpr int WM = 128, WN = 64, MI = WM / 32, NI = WN / 32;
     static constexpr int WAVES_N = BN / WN, WAVES_M = BM / WM;
     static_assert(WAVES_N * WAVES_M == NWAVES, "wave grid");
-    static constexpr int STAGES = 4;
-    static constexpr int BK = 32;                      // k per stage
-    static constexpr int P_BYTES = BM * 64;            // 256 rows x 32 bf16
-    static constexpr int Q_BYTES = BN * 64;            // BN rows x 32 bf16, or 32 k-rows x BN bf16
+    static constexpr int STAGES = 2;
+    static constexpr int BK = 64;                      // k per stage
+    static constexpr int SUBSTEPS = BK / 16;           // 16-k MFMA substeps per stage
+    static constexpr int ROWB = BK * 2;                // bytes of one K-contiguous row per stage
+    static constexpr int P_BYTES = BM * ROWB;          // 256 rows x 64 bf16
+    static constexpr int Q_BYTES = BN * ROWB;          // BN rows x 64 bf16, or 64 k-rows x BN bf16
+    static constexpr int SLOT_BYTES = P_BYTES + Q_BYTES;
     static constexpr int QROW = BN * 2;                // bytes of one k-row of an N-contiguous Q tile
     static constexpr int P_BLOCKS = P_BYTES / 1024 / NWAVES;  // 1 KB DMA blocks per wave and stage
     static constexpr int Q_BLOCKS = Q_BYTES / 1024 / NWAVES;
@@ -67,41 +73,17 @@ struct Cfg {
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_tr;
 typedef __attribute__((address_space(3))) bf16x4_tr lds_bf16x4_t;
 
-// One LDS object per stage and operand (16 KB each); after the main loop the
-// epilogues reuse them as staging areas.
-__shared__ __attribute__((aligned(1024))) char lds_p0[16384];
-__shared__ __attribute__((aligned(1024))) char lds_p1[16384];
-__shared__ __attribute__((aligned(1024))) char lds_p2[16384];
-__shared__ __attribute__((aligned(1024))) char lds_p3[16384];
-__shared__ __attribute__((aligned(1024))) char lds_q0[16384];
-__shared__ __attribute__((aligned(1024))) char lds_q1[16384];
-__shared__ __attribute__((aligned(1024))) char lds_q2[16384];
-__shared__ __attribute__((aligned(1024))) char lds_q3[16384];
+// The operand ring: slot S holds the P slab, then the Q slab.  After the main
+// loop the epilogues reuse it as staging areas.
+__shared__ __attribute__((aligned(1024))) char lds_ring[Cfg::STAGES * Cfg::SLOT_BYTES];
 
-template <int S> __device__ __forceinline__ char *slot_p() {
-    if constexpr (S == 0) return lds_p0;
-    else if constexpr (S == 1) return lds_p1;
-    else if constexpr (S == 2) return lds_p2;
-    else return lds_p3;
-}
-template <int S> __device__ __forceinline__ char *slot_q() {
-    if constexpr (S == 0) return lds_q0;
-    else if constexpr (S == 1) return lds_q1;
-    else if constexpr (S == 2) return lds_q2;
-    else return lds_q3;
-}
+template <int S> __device__ __forceinline__ char *slot_p() { return lds_ring + S * Cfg::SLOT_BYTES; }
+template <int S> __device__ __forceinline__ char *slot_q() { return lds_ring + S * Cfg::SLOT_BYTES + Cfg::P_BYTES; }
 
-// Epilogue staging areas (8 KB each, inside the operand ring, free once every
-// wave has left the main loop): the first area of wave w lies in p(w/2), the
-// second in q(w/2).
+// Epilogue staging areas: two of 8 KB per wave, free once every wave has left
+// the main loop.
 template <int WHICH> __device__ __forceinline__ char *epi_area(int wave) {
-    const int off = (wave & 1) * 8192;
-    switch (wave >> 1) {
-        case 0: return (WHICH ? lds_q0 : lds_p0) + off;
-        case 1: return (WHICH ? lds_q1 : lds_p1) + off;
-        case 2: return (WHICH ? lds_q2 : lds_p2) + off;
-        default: return (WHICH ? lds_q3 : lds_p3) + off;
-    }
+    return lds_ring + wave * 2 * Cfg::EPI_BYTES + WHICH * Cfg::EPI_BYTES;
 }
 
 // s_waitcnt with vmcnt = N and the LDS/export counters left alone.
@@ -138,12 +120,12 @@ __device__ __forceinline__ void dma16(const char *g, const char *l) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
 
-// K-contiguous tile (rows x 64 bytes): 16-byte chunk c of row r lives at chunk
-// c ^ ((r >> 2) & 3), so 16 consecutive rows reading one chunk cover 16
+// K-contiguous tile (rows x 128 bytes): 16-byte chunk c of row r lives at
+// chunk c ^ ((r >> 1) & 7), so 16 consecutive rows reading one chunk cover 16
 // distinct 16-byte bank groups.
-__device__ __forceinline__ int kc_offset(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+__device__ __forceinline__ int kc_offset(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-// N-contiguous tile (32 k-rows x QROW bytes): 64-byte block b of k-row r lives
+// N-contiguous tile (64 k-rows x QROW bytes): 64-byte block b of k-row r lives
 // at block b ^ (r & 3), so four consecutive k-rows of one block cover 256 B.
 template <class C> __device__ __forceinline__ int nc_offset(int krow, int byte) {
     return krow * C::QROW + ((((byte >> 6) ^ (krow & 3))) << 6) + (byte & 63);
@@ -162,18 +144,19 @@ struct Src {
 };
 
 // DMA block j (0 <= j < LPS) of this wave for stage kt into slot S.  Blocks
-// [0, P_BLOCKS) fill the P slab: 1 KB block `blk` holds rows 16 blk .. +15 x
-// bytes [kt*64, kt*64 + 64); lane i lands at block byte 16 i, i.e. row i/4,
-// swizzled chunk i%4.  The rest fill the Q slab the same way, except for
-// APPLY, whose Q slab is k-rows [kt*32, kt*32 + 32) x QROW bytes of
-// row-major X: a block holds 1024/QROW consecutive k-rows.
+// [0, P_BLOCKS) fill the P slab: 1 KB block `blk` holds rows 8 blk .. +7 x
+// bytes [kt*128, kt*128 + 128); lane i lands at block byte 16 i, i.e. row
+// i/8, swizzled chunk i%8.  The rest fill the Q slab the same way, except for
+// APPLY, whose Q slab is k-rows [kt*64, kt*64 + 64) x QROW bytes of row-major
+// X: a block holds 1024/QROW consecutive k-rows.  Every instruction moves
+// whole 128-byte lines.
 template <class C, int KIND, int S>
 __device__ __forceinline__ void dma_block(const Src &src, int kt, int j, int wave, int lane) {
     if (j < C::P_BLOCKS) {
         const int blk = wave * C::P_BLOCKS + j;
-        const int row = blk * 16 + (lane >> 2);
-        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-        dma16(src.p + row * src.ld_p + kt * 64 + chunk * 16, slot_p<S>() + blk * 1024);
+        const int row = blk * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        dma16(src.p + row * src.ld_p + kt * C::ROWB + chunk * 16, slot_p<S>() + blk * 1024);
     } else if constexpr (KIND == APPLY) {
         constexpr int UNITS = C::QROW / 16;  // 16-byte units per k-row
         const int blk = wave * C::Q_BLOCKS + (j - C::P_BLOCKS);
@@ -183,9 +166,9 @@ __device__ __forceinline__ void dma_block(const Src &src, int kt, int j, int wav
         dma16(src.q + (static_cast<int64_t>(kt) * C::BK + krow) * src.ld_q + byte, slot_q<S>() + blk * 1024);
     } else {
         const int blk = wave * C::Q_BLOCKS + (j - C::P_BLOCKS);
-        const int row = blk * 16 + (lane >> 2);
-        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-        dma16(src.q + row * src.ld_q + kt * 64 + chunk * 16, slot_q<S>() + blk * 1024);
+        const int row = blk * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        dma16(src.q + row * src.ld_q + kt * C::ROWB + chunk * 16, slot_q<S>() + blk * 1024);
     }
 }
 
@@ -196,7 +179,7 @@ struct Frags {
     u32x4 b[Cfg::NI];
 };
 
-// Reads fragment j of substep ks (0 or 1) of the stage in slot S, in the order
+// Reads fragment j of substep ks (0 .. SUBSTEPS-1) of the stage in slot S, in the order
 // the products consume them: a0, b0 .. b(NI-1), a1 .. a(MI-1).
 template <class C, int KIND, int S>
 __device__ __forceinline__ void read_frag(Frags &f, int j, int ks, int wm, int wn, int lane) {
@@ -239,78 +222,72 @@ __device__ __forceinline__ void mma_one(floatx16 (&acc)[C::MI][C::NI], const Fra
                                                           __builtin_bit_cast(bf16x8, f.a[mi]), acc[mi][ni], 0, 0, 0);
 }
 
-// Stage kt, held in slot S (= kt mod 4).  Every product is followed by at
-// most one fragment read and one DMA, and a scheduling fence keeps that
-// order, so LDS reads and global->LDS copies proceed under the MFMAs.
-//   Part A: products of substep 0 (fa); reads of substep 1 (fb); DMA of the
-//           second half of stage kt+3 (slot (S+3) mod 4, released at the
-//           previous stage's barrier).
-//   Wait for this wave's DMA of stage kt+1 (WAIT newer loads may remain:
-//   stages kt+2 and kt+3) and for its own LDS reads, then the barrier: stage
-//   kt+1 has landed everywhere and no wave reads slot S any more.
-//   Part B: products of fb; reads of substep 0 of stage kt+1 into fa; DMA of
-//           the first half of stage kt+4 into slot S.
-// ISSUE_A / ISSUE_B drop the DMA past the last stage; LAST ends after Part A.
-template <class C, int KIND, int S, int WAIT, bool ISSUE_A, bool ISSUE_B, bool LAST>
-__device__ __forceinline__ void ring_stage(floatx16 (&acc)[C::MI][C::NI], const Src &src, int kt, int wave, int wm,
-                                           int wn, int lane, Frags &fa, Frags &fb) {
-    constexpr int H = C::LPS / 2, EVERY = C::NM / H;
+// Products of one substep (fragments f) with the reads of the next
+// substep's fragments (into g, from slot S, substep ks_next) interleaved one
+// per product; ISSUE_DMA spreads the LPS DMA blocks of stage kt_dma (into
+// slot S_DMA) over the products.  A scheduling fence after each product keeps
+// that order, so LDS reads and copies run under the MFMAs.
+template <class C, int KIND, int S_READ, bool READ, int S_DMA, bool ISSUE_DMA>
+__device__ __forceinline__ void substep(floatx16 (&acc)[C::MI][C::NI], const Frags &f, Frags &g, int ks_next,
+                                        const Src &src, int kt_dma, int wave, int wm, int wn, int lane) {
+    constexpr int EVERY = C::NM / C::LPS;
+    static_assert(EVERY >= 1 && C::NM % C::LPS == 0, "one DMA block per product slot");
 #pragma unroll
     for (int i = 0; i < C::NM; ++i) {
-        mma_one<C>(acc, fa, i);
-        if (i < C::NF) read_frag<C, KIND, S>(fb, i, 1, wm, wn, lane);
-        if (ISSUE_A && i % EVERY == EVERY / 2) dma_block<C, KIND, (S + 3) % 4>(src, kt + 3, H + i / EVERY, wave, lane);
+        mma_one<C>(acc, f, i);
+        if (READ && i < C::NF) read_frag<C, KIND, S_READ>(g, i, ks_next, wm, wn, lane);
+        if (ISSUE_DMA && i % EVERY == 0) dma_block<C, KIND, S_DMA>(src, kt_dma, i / EVERY, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (LAST) {
-#pragma unroll
-        for (int i = 0; i < C::NM; ++i) mma_one<C>(acc, fb, i);
-    } else {
-        wait_lgkm0();
-        wait_vmcnt<WAIT>();
-        stage_barrier();
-#pragma unroll
-        for (int i = 0; i < C::NM; ++i) {
-            mma_one<C>(acc, fb, i);
-            if (i < C::NF) read_frag<C, KIND, (S + 1) % 4>(fa, i, 0, wm, wn, lane);
-            if (ISSUE_B && i % EVERY == EVERY / 2) dma_block<C, KIND, S>(src, kt + 4, i / EVERY, wave, lane);
-            __builtin_amdgcn_sched_barrier(0);
-        }
     }
 }
 
-// The K loop over nk stages (nk a multiple of 4, at least 8).  Stages 0..2 and
-// the first half of stage 3 are loaded up front; loads retire in issue
-// order, so vmcnt(2 LPS + LPS/2) leaves exactly those after stage 0 in flight.
+// Stage kt, held in slot S (= kt mod 2), four 16-k substeps; fa holds the
+// first substep's fragments on entry.  After the third substep each wave
+// waits for its own DMA of stage kt+1 (the only loads in flight) and for its
+// LDS reads, then the barrier: stage kt+1 has landed everywhere and no wave
+// reads slot S any more, so the fourth substep refills it with stage kt+2
+// while reading stage kt+1's first fragments from the other slot.
+template <class C, int KIND, int S, bool ISSUE, bool LAST>
+__device__ __forceinline__ void ring_stage(floatx16 (&acc)[C::MI][C::NI], const Src &src, int kt, int wave, int wm,
+                                           int wn, int lane, Frags &fa, Frags &fb) {
+    static_assert(C::SUBSTEPS == 4, "four substeps per stage");
+    substep<C, KIND, S, true, S, false>(acc, fa, fb, 1, src, 0, wave, wm, wn, lane);
+    substep<C, KIND, S, true, S, false>(acc, fb, fa, 2, src, 0, wave, wm, wn, lane);
+    substep<C, KIND, S, true, S, false>(acc, fa, fb, 3, src, 0, wave, wm, wn, lane);
+    if constexpr (LAST) {
+        substep<C, KIND, S, false, S, false>(acc, fb, fa, 0, src, 0, wave, wm, wn, lane);
+    } else {
+        wait_lgkm0();
+        wait_vmcnt<0>();
+        stage_barrier();
+        substep<C, KIND, 1 - S, true, S, ISSUE>(acc, fb, fa, 0, src, kt + 2, wave, wm, wn, lane);
+    }
+}
+
+// The K loop over nk stages (nk even, at least 2): stages 0 and 1 are loaded
+// up front (loads retire in issue order, so vmcnt(LPS) leaves exactly stage
+// 1's in flight once stage 0 has landed).
 template <class C, int KIND>
 __device__ __forceinline__ void main_loop(floatx16 (&acc)[C::MI][C::NI], const Src &src, int nk, int wave, int wm,
                                           int wn, int lane) {
-    static_assert(C::STAGES == 4 && C::LPS % 2 == 0 && C::NM % (C::LPS / 2) == 0 && C::NF <= C::NM, "interleave");
-    constexpr int L = C::LPS, H = C::LPS / 2;
+    static_assert(C::STAGES == 2 && C::NF <= C::NM, "ring");
+    constexpr int L = C::LPS;
 #pragma unroll
     for (int j = 0; j < L; ++j) dma_block<C, KIND, 0>(src, 0, j, wave, lane);
 #pragma unroll
     for (int j = 0; j < L; ++j) dma_block<C, KIND, 1>(src, 1, j, wave, lane);
-#pragma unroll
-    for (int j = 0; j < L; ++j) dma_block<C, KIND, 2>(src, 2, j, wave, lane);
-#pragma unroll
-    for (int j = 0; j < H; ++j) dma_block<C, KIND, 3>(src, 3, j, wave, lane);
-    wait_vmcnt<2 * L + H>();
+    wait_vmcnt<L>();
     stage_barrier();
     Frags fa, fb;
 #pragma unroll
     for (int j = 0; j < C::NF; ++j) read_frag<C, KIND, 0>(fa, j, 0, wm, wn, lane);
     int kt = 0;
-    for (; kt < nk - 4; kt += 4) {
-        ring_stage<C, KIND, 0, 2 * L, true, true, false>(acc, src, kt, wave, wm, wn, lane, fa, fb);
-        ring_stage<C, KIND, 1, 2 * L, true, true, false>(acc, src, kt + 1, wave, wm, wn, lane, fa, fb);
-        ring_stage<C, KIND, 2, 2 * L, true, true, false>(acc, src, kt + 2, wave, wm, wn, lane, fa, fb);
-        ring_stage<C, KIND, 3, 2 * L, true, true, false>(acc, src, kt + 3, wave, wm, wn, lane, fa, fb);
+    for (; kt < nk - 2; kt += 2) {
+        ring_stage<C, KIND, 0, true, false>(acc, src, kt, wave, wm, wn, lane, fa, fb);
+        ring_stage<C, KIND, 1, true, false>(acc, src, kt + 1, wave, wm, wn, lane, fa, fb);
     }
-    ring_stage<C, KIND, 0, 2 * L, true, false, false>(acc, src, kt, wave, wm, wn, lane, fa, fb);
-    ring_stage<C, KIND, 1, L, false, false, false>(acc, src, kt + 1, wave, wm, wn, lane, fa, fb);
-    ring_stage<C, KIND, 2, 0, false, false, false>(acc, src, kt + 2, wave, wm, wn, lane, fa, fb);
-    ring_stage<C, KIND, 3, 0, false, false, true>(acc, src, kt + 3, wave, wm, wn, lane, fa, fb);
+    ring_stage<C, KIND, 0, false, false>(acc, src, kt, wave, wm, wn, lane, fa, fb);
+    ring_stage<C, KIND, 1, false, true>(acc, src, kt + 1, wave, wm, wn, lane, fa, fb);
 }
 
 // DMA of EPI_ROWS rows x 64 fp32 (256 bytes per row) starting at `src` (row
