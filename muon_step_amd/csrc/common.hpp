@@ -94,48 +94,99 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // ulp (2^(e - 8)), so |q| <= 128 and the residual's rounding error is at most
 // 2^(e - 16), or 2^(e - 15) where q clamps: x is carried to 2^-15 relative
 // (2^-16 but for that clamp).  hi + q 2^(e - 15) spans at most 17 bits and is
-// exact in fp32.  Below 2^-111 (exponent field < 16) only hi's precision is
-// kept; infinite and NaN values are carried by hi alone.
-__device__ __forceinline__ uint32_t lo8_encode(float x, uint32_t hbits) {
-    // 2^(15 - e) from the exponent field, clamped to 16 .. 254: below 2^-111
-    // the residual is far under one step and rounds to 0; for infinite or NaN
-    // hi the residual is NaN, which converts to 0.
-    const uint32_t ex = min(max((hbits >> 7) & 0xffu, 16u), 254u);
-    const float t = (x - __uint_as_float(hbits << 16)) * __uint_as_float((269u - ex) << 23);  // exact
-    const int q = min(max(static_cast<int>(rintf(t)), -128), 127);
-    return static_cast<uint32_t>(q) & 0xffu;
+// exact in fp32.
+//
+// The unit 2^(e - 15) is never formed.  The codec works against a reference
+// float m whose exponent is e + 8 and whose mantissa is 0.5 (plus, in the
+// paired form, a few low bits that change nothing): m sits mid-binade with
+// ulp 2^(e - 15), so the single rounding of m + (x - hi) rounds x - hi to a
+// multiple of the unit (to nearest, ties to even q) and leaves q as the
+// difference of the two bit patterns; decoding adds q to m's bits and
+// subtracts m, both exact.  e is capped at 119 (|hi| < 2^120; above that only
+// hi's precision is kept, and infinite or NaN hi absorbs any residual); below
+// 2^-126 the unit is still consistent, with hi's precision the limit.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+constexpr uint32_t LO8_REF_ADD = 0x04400000u;  // exponent + 8, mantissa 0.5
+constexpr uint32_t LO8_EXP_CAP = 246u << 23;    // exponent field 246 (e = 119)
+
+// Reference bits for one hi given as fp32 bits.
+__device__ __forceinline__ uint32_t lo8_ref(uint32_t hf_bits) {
+    return min(hf_bits & 0x7f800000u, LO8_EXP_CAP) + LO8_REF_ADD;
 }
-// The residual of hi (hi's bits in the low 16 of hbits): q * 2^(e - 15), with
-// the exponent taken from hi's bits and capped at 2^127 so that infinite or
-// NaN hi (whose q is 0) gives 0.
-__device__ __forceinline__ float lo8_decode(uint32_t qbyte, uint32_t hbits) {
-    const float pow2e = __uint_as_float(min((hbits << 16) & 0x7f800000u, 0x7f000000u));
-    return static_cast<float>(static_cast<int8_t>(qbyte & 0xffu)) * 0x1p-15f * pow2e;
+// Reference bits for the two bf16 of one packed pair (element 0 in the low
+// half).  m1 keeps element 0's capped exponent in its bits 14..7: mantissa
+// bits far below m's top bit that leave its binade, its ulp and its last bit
+// (hence ties) unchanged.
+__device__ __forceinline__ void lo8_ref2(uint32_t h2, uint32_t *m0, uint32_t *m1) {
+    const u16x2 cap = {static_cast<uint16_t>(LO8_EXP_CAP >> 16), static_cast<uint16_t>(LO8_EXP_CAP >> 16)};
+    const uint32_t eb = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, h2 & 0x7f807f80u), cap));
+    *m0 = (eb << 16) + LO8_REF_ADD;
+    *m1 = eb + LO8_REF_ADD;
+}
+// q of x against hi (as a float) and its reference bits.
+__device__ __forceinline__ int lo8_q(float x, float hf, uint32_t mb) {
+    const float t = (x - hf) + __uint_as_float(mb);  // x - hf exact; one rounding to the unit
+    return min(max(static_cast<int>(__float_as_uint(t) - mb), -128), 127);
+}
+// The residual q * 2^(e - 15) from q and the reference bits.
+__device__ __forceinline__ float lo8_value(int q, uint32_t mb) {
+    return __uint_as_float(mb + static_cast<uint32_t>(q)) - __uint_as_float(mb);
 }
 __device__ __forceinline__ void split_bf16(float x, uint16_t *hi, uint8_t *lo) {
     const uint16_t h = float_to_bf16_bits(x);
+    const uint32_t hb = static_cast<uint32_t>(h) << 16;
     *hi = h;
-    *lo = static_cast<uint8_t>(lo8_encode(x, h));
+    *lo = static_cast<uint8_t>(lo8_q(x, __uint_as_float(hb), lo8_ref(hb)) & 0xff);
 }
 __device__ __forceinline__ float join_bf16(uint16_t hi, uint8_t lo) {
-    return bf16_bits_to_float(hi) + lo8_decode(lo, hi);
+    const uint32_t hb = static_cast<uint32_t>(hi) << 16;
+    return __uint_as_float(hb) + lo8_value(static_cast<int8_t>(lo), lo8_ref(hb));
 }
 // Four consecutive values: hi as packed bf16 pairs, the residuals as four
-// bytes of one word (value k in byte k).
+// bytes of one word (value k in byte k).  BOUNDED: the caller guarantees
+// |x| < 2^120 or a non-finite hi (a Newton-Schulz iterate of a normalised
+// matrix), so the exponent cap is not needed: for infinite or NaN hi the
+// reference overflows, q is meaningless and the decode (which caps) adds a
+// finite residual to a non-finite hi.
+template <bool BOUNDED = false>
 __device__ __forceinline__ void split_bf16x4(const floatx4 &v, u32x2 *hi, uint32_t *lo) {
     u32x2 h;
     h[0] = pack_bf16x2(v[0], v[1]);
     h[1] = pack_bf16x2(v[2], v[3]);
+    // opaque to the optimiser, which would otherwise convert each value to
+    // bf16 a second time to get its float hi
+    asm volatile("" : "+v"(h[0]), "+v"(h[1]));
     *hi = h;
-    *lo = lo8_encode(v[0], h[0] & 0xffffu) | (lo8_encode(v[1], h[0] >> 16) << 8) |
-          (lo8_encode(v[2], h[1] & 0xffffu) << 16) | (lo8_encode(v[3], h[1] >> 16) << 24);
+    int q[4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        uint32_t m0, m1;
+        if (BOUNDED) {
+            const uint32_t eb = h[k] & 0x7f807f80u;
+            m0 = (eb << 16) + LO8_REF_ADD;
+            m1 = eb + LO8_REF_ADD;
+        } else {
+            lo8_ref2(h[k], &m0, &m1);
+        }
+        q[2 * k] = lo8_q(v[2 * k], __uint_as_float(h[k] << 16), m0);
+        q[2 * k + 1] = lo8_q(v[2 * k + 1], __uint_as_float(h[k] & 0xffff0000u), m1);
+    }
+    // v_perm_b32 picks bytes of {src0, src1} (src1 = bytes 0..3; 0x0c = zero)
+    const uint32_t p01 = __builtin_amdgcn_perm(static_cast<uint32_t>(q[1]), static_cast<uint32_t>(q[0]), 0x0c0c0400u);
+    const uint32_t p23 = __builtin_amdgcn_perm(static_cast<uint32_t>(q[3]), static_cast<uint32_t>(q[2]), 0x0c0c0400u);
+    *lo = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
 __device__ __forceinline__ floatx4 join_bf16x4(const u32x2 &h, uint32_t l) {
     floatx4 v;
-    v[0] = __uint_as_float(h[0] << 16) + lo8_decode(l, h[0]);
-    v[1] = __uint_as_float(h[0] & 0xffff0000u) + lo8_decode(l >> 8, h[0] >> 16);
-    v[2] = __uint_as_float(h[1] << 16) + lo8_decode(l >> 16, h[1]);
-    v[3] = __uint_as_float(h[1] & 0xffff0000u) + lo8_decode(l >> 24, h[1] >> 16);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        uint32_t m0, m1;
+        lo8_ref2(h[k], &m0, &m1);
+        const int q0 = static_cast<int8_t>((l >> (16 * k)) & 0xffu);
+        const int q1 = static_cast<int8_t>((l >> (16 * k + 8)) & 0xffu);
+        v[2 * k] = __uint_as_float(h[k] << 16) + lo8_value(q0, m0);
+        v[2 * k + 1] = __uint_as_float(h[k] & 0xffff0000u) + lo8_value(q1, m1);
+    }
     return v;
 }
 

@@ -350,7 +350,8 @@ __device__ __forceinline__ void tri_decode(int64_t t, int *ti, int *tj) {
 // Epilogue of GRAM and POLY.  The wave's 128 x 64 block is finished in four
 // rounds of 32 rows staged in LDS.  POLY first brings the matching rows of the
 // fp32 A by DMA (two areas, the next round in flight).  The values (GRAM: A,
-// times inv_norm^2 on the bf16 path's first step; POLY: b A + c A A) are
+// times inv_norm^2 on the bf16 path's first step; POLY: b A + c A A, times
+// inv_norm on that step, so that B X applies the normalisation of X) are
 // formed in the accumulator layout and written in place as fp32 rows; the
 // rows are stored whole (GRAM: fp32 A and its bf16 operand copy; POLY: bf16
 // B), and for an off-diagonal tile each column of the block is stored as 32
@@ -372,8 +373,11 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
     float *af = w.af + e * w.a_stride;
     uint16_t *dst = static_cast<uint16_t *>(KIND == GRAM ? w.ab : w.bb) + e * w.a_stride;
     const bool mirror = ti != tj;
-    // first step on the bf16 path: X holds N, so A = inv (N N^T) inv
-    const float scale = (KIND == GRAM && p.unnormalized) ? w.inv_norm[e] : 1.0f;
+    // first step on the bf16 path: X holds N, so A = inv^2 (N N^T) and the
+    // product B X is taken with B inv (X' = a inv N + (B inv) N)
+    const float inv = p.unnormalized ? w.inv_norm[e] : 1.0f;
+    const float gscale = inv * inv;
+    const float pb = p.b * inv, pc = p.c * inv;
     const char *a_in = reinterpret_cast<const char *>(af + row0 * ld + col0);
     if constexpr (KIND == POLY) {
         dma_epi<C>(area[0], a_in, ld * 4, lane);
@@ -399,11 +403,11 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
                 const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
                 if constexpr (KIND == GRAM) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) v[ni][c4][q] = (acc[h][ni][4 * c4 + q] * scale) * scale;
+                    for (int q = 0; q < 4; ++q) v[ni][c4][q] = acc[h][ni][4 * c4 + q] * gscale;
                 } else {
                     const floatx4 a4 = *reinterpret_cast<const floatx4 *>(reg + epi_offset(lrow, lcol >> 2));
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) v[ni][c4][q] = p.b * a4[q] + p.c * acc[h][ni][4 * c4 + q];
+                    for (int q = 0; q < 4; ++q) v[ni][c4][q] = __builtin_fmaf(pb, a4[q], pc * acc[h][ni][4 * c4 + q]);
                 }
             }
         asm volatile("" ::: "memory");
@@ -501,6 +505,24 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
 
 // --------------------------------------------------------------------- a X + B X
 
+// A wave-uniform value (the wave's own tile coordinates), moved to scalar
+// registers so that addresses built from it are too.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Global stores addressed as a scalar base plus a 32-bit per-lane offset
+// (the compiler builds a 64-bit vector address per store otherwise).  Plain
+// vector stores: they count in vmcnt like any other.
+__device__ __forceinline__ void store_saddr(char *base, uint32_t off, const u32x2 &v) {
+    asm volatile("global_store_dwordx2 %0, %1, %2" ::"v"(off), "v"(v), "s"(base) : "memory");
+}
+__device__ __forceinline__ void store_saddr(char *base, uint32_t off, uint32_t v) {
+    asm volatile("global_store_dword %0, %1, %2" ::"v"(off), "v"(v), "s"(base) : "memory");
+}
+
 // Output block of one wave in the apply epilogue.
 struct ApplyTile {
     int64_t e;     // matrix
@@ -508,19 +530,19 @@ struct ApplyTile {
     int64_t col0;  // first output column
 };
 
-// Row lrow's four columns lcol .. lcol+3 of (a X + B X) * scale, with
-// X = X_hi + X_lo staged in `reg` (X_hi rows, 128 bytes each, in the first
-// PAIR_HALF bytes; X_lo rows, 64 bytes each, after).  scale is 1, or inv_norm
-// when X still holds N.
+// Row lrow's four columns lcol .. lcol+3 of a X + B X, with X = X_hi + X_lo
+// staged in `reg` (X_hi rows, 128 bytes each, in the first PAIR_HALF bytes;
+// X_lo rows, 64 bytes each, after).  While X still holds N, `a` is a inv_norm
+// (and B was scaled by inv_norm when it was formed).
 constexpr int PAIR_HALF = 4096;
 __device__ __forceinline__ floatx4 apply_value(const floatx16 &acc, const char *reg, int lrow, int lcol, int c4,
-                                               float a, float scale) {
+                                               float a) {
     const u32x2 h = *reinterpret_cast<const u32x2 *>(reg + pair_offset(lrow, lcol));
     const uint32_t l = *reinterpret_cast<const uint32_t *>(reg + PAIR_HALF + lo8_offset(lrow, lcol));
     const floatx4 x = join_bf16x4(h, l);
     floatx4 v;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = (a * x[q] + acc[4 * c4 + q]) * scale;
+    for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(a, x[q], acc[4 * c4 + q]);
     return v;
 }
 
@@ -530,15 +552,14 @@ __device__ __forceinline__ floatx4 apply_value(const floatx16 &acc, const char *
 // one wave's LDS accesses execute in order, so no value is overwritten before
 // it is read.
 template <class C>
-__device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char *reg, float a, float scale,
-                                             int lane) {
+__device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char *reg, float a, int lane) {
     const int lrow = lane & 31;
     floatx4 v[C::NI][4];
 #pragma unroll
     for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
-            v[ni][c4] = apply_value(accm[ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, a, scale);
+            v[ni][c4] = apply_value(accm[ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, a);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int ni = 0; ni < C::NI; ++ni)
@@ -553,7 +574,9 @@ __device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char
 
 
 // Epilogue of an intermediate step: X' = a X + B X is written as the bf16 pair
-// (X'_hi to xb_next, X'_lo to xl in place; zero outside s x l).  Per round of
+// (X'_hi to xb_next, X'_lo to xl in place).  Outside s x l it is zero without
+// a mask: X is zero there, so are the padded rows and columns of A and B, and
+// with them every term of X'.  Per round of
 // EPI_ROWS rows the wave's X_hi and X_lo rows arrive in a staging area by DMA;
 // the values are formed in the accumulator layout and rewritten there as fp32
 // rows, then read row-contiguously (16 lanes per row) so the stores move whole
@@ -579,7 +602,13 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::M
     const char *hi_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xb) + t.e * w.x_stride + first);
     const char *lo_in = reinterpret_cast<const char *>(xl + first);
     const int64_t ld = g.lp * 2, ld_lo = g.lp;
-    const float scale = p.unnormalized ? w.inv_norm[t.e] : 1.0f;
+    const float a = p.unnormalized ? p.a * w.inv_norm[t.e] : p.a;
+    // Stores: a wave-uniform row base plus a per-lane 32-bit offset (lane
+    // (rr, chunk) owns columns 4 chunk .. +3 of row rr of each group of four).
+    const int rr = lane >> 4, chunk = lane & 15;
+    const uint32_t off_lo = static_cast<uint32_t>(rr * g.lp + 4 * chunk);
+    const uint32_t off_hi = 2 * off_lo;
+    const int64_t row0 = uniform64(t.row0), col0 = uniform64(t.col0);
     auto dma_round = [&](char *dst, int h) {
         dma_bf16_rows<C>(dst, hi_in + C::EPI_ROWS * h * ld, ld, lane);
         dma_lo8_rows<C>(dst + PAIR_HALF, lo_in + C::EPI_ROWS * h * ld_lo, ld_lo, lane);
@@ -595,22 +624,18 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::M
         else
             fenced_wait_vmcnt<STORES_PER_ROUND>();
         char *reg = area[h & 1];
-        stage_values<C>(acc[h], reg, p.a, scale, lane);
+        stage_values<C>(acc[h], reg, a, lane);
 #pragma unroll
         for (int r4 = 0; r4 < C::EPI_ROWS / 4; ++r4) {
-            const int lrow = 4 * r4 + (lane >> 4), chunk = lane & 15;
-            floatx4 v = *reinterpret_cast<const floatx4 *>(reg + epi_offset(lrow, chunk));
-            const int64_t gi = t.row0 + C::EPI_ROWS * h + lrow;
-            const int64_t gj = t.col0 + 4 * chunk;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (gi >= g.s || gj + q >= g.l) v[q] = 0.0f;
-            const int64_t idx = gi * g.lp + gj;
+            const floatx4 v = *reinterpret_cast<const floatx4 *>(reg + epi_offset(4 * r4 + rr, chunk));
+            const int64_t base = (row0 + C::EPI_ROWS * h + 4 * r4) * g.lp + col0;
+            char *ph = reinterpret_cast<char *>(xh_out + base);
+            char *pl = reinterpret_cast<char *>(xl + base);
             u32x2 hi;
             uint32_t lo;
-            split_bf16x4(v, &hi, &lo);
-            *reinterpret_cast<u32x2 *>(xh_out + idx) = hi;
-            *reinterpret_cast<uint32_t *>(xl + idx) = lo;
+            split_bf16x4<true>(v, &hi, &lo);  // |X'| <= ~1.2: X is normalised
+            store_saddr(ph, off_hi, hi);
+            store_saddr(pl, off_lo, lo);
         }
         if (h + 2 < ROUNDS) {
             wait_lgkm0();  // this round's LDS reads are done before the DMA refills the area
@@ -681,7 +706,7 @@ __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Cfg:
     const char *hi_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xb) + t.e * w.x_stride + first);
     const char *lo_in = reinterpret_cast<const char *>(static_cast<const uint8_t *>(w.xl) + t.e * w.x_stride + first);
     const int64_t ld = g.lp * 2, ld_lo = g.lp;
-    const float scale = p.unnormalized ? w.inv_norm[t.e] : 1.0f;
+    const float a = p.unnormalized ? p.a * w.inv_norm[t.e] : p.a;
 #pragma unroll
     for (int h = 0; h < ROUNDS; ++h) {
         dma_bf16_rows<C>(reg, hi_in + C::EPI_ROWS * h * ld, ld, lane);
@@ -695,11 +720,11 @@ __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Cfg:
 #pragma unroll
                 for (int c4 = 0; c4 < 4; ++c4) {
                     const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
-                    const floatx4 v = apply_value(acc[h][ni], reg, lrow, lcol, c4, p.a, scale);
+                    const floatx4 v = apply_value(acc[h][ni], reg, lrow, lcol, c4, a);
                     if (gi < g.s) update_row4<PARAM_BF16>(d, g, p, gi, t.col0 + lcol, v);
                 }
         } else {
-            stage_values<C>(acc[h], reg, p.a, scale, lane);
+            stage_values<C>(acc[h], reg, a, lane);
 #pragma unroll 4
             for (int r4 = 0; r4 < C::EPI_ROWS / 4; ++r4) {
                 const int rrow = 4 * r4 + (lane >> 4), chunk = lane & 15;
