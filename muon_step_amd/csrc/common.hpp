@@ -46,7 +46,8 @@ struct Geom {
 //   xl      + e*x_stride  X_lo, the 8-bit residual of X - X_hi (one byte per
 //                         element), rewritten in place by the tile that owns
 //                         the elements (bf16 path)
-//   af + e*a_stride       fp32 A = X X^T (sp x sp, lower-triangle tiles)
+//   af + e*a_stride       fp32 A = X X^T (sp x sp, lower-triangle tiles; fp32
+//                         path only, nullptr on the bf16 path)
 //   ab + e*a_stride       A as MFMA operand (bf16 or fp32, both triangles)
 //   bb + e*a_stride       B = bA + cA^2 as MFMA operand (both triangles)
 // Newton-Schulz workspace of one chunk of same-shape matrices.  fp32 path: X

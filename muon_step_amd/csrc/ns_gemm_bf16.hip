@@ -80,10 +80,13 @@ __shared__ __attribute__((aligned(1024))) char lds_ring[Cfg::STAGES * Cfg::SLOT_
 template <int S> __device__ __forceinline__ char *slot_p() { return lds_ring + S * Cfg::SLOT_BYTES; }
 template <int S> __device__ __forceinline__ char *slot_q() { return lds_ring + S * Cfg::SLOT_BYTES + Cfg::P_BYTES; }
 
-// Epilogue staging areas: two of 8 KB per wave, free once every wave has left
-// the main loop.
+// Epilogue staging areas: two of 8 KB per wave, area WHICH of every wave in
+// slot WHICH of the ring.  Slot 0 is free once the last stage (slot 1) has
+// begun, so the first round of an epilogue can be loaded under the last
+// stage's MFMAs; slot 1 once every wave has left the main loop.
 template <int WHICH> __device__ __forceinline__ char *epi_area(int wave) {
-    return lds_ring + wave * 2 * Cfg::EPI_BYTES + WHICH * Cfg::EPI_BYTES;
+    static_assert(Cfg::NWAVES * Cfg::EPI_BYTES == Cfg::SLOT_BYTES, "one slot per staging area");
+    return lds_ring + WHICH * Cfg::SLOT_BYTES + wave * Cfg::EPI_BYTES;
 }
 
 // s_waitcnt with vmcnt = N and the LDS/export counters left alone.
@@ -266,10 +269,12 @@ __device__ __forceinline__ void ring_stage(floatx16 (&acc)[C::MI][C::NI], const 
 
 // The K loop over nk stages (nk even, at least 2): stages 0 and 1 are loaded
 // up front (loads retire in issue order, so vmcnt(LPS) leaves exactly stage
-// 1's in flight once stage 0 has landed).
-template <class C, int KIND>
+// 1's in flight once stage 0 has landed).  pre_last() runs before the last
+// stage, when no wave reads slot 0 any more (every wave has passed the
+// barrier of stage nk-2): it may start loads into slot 0.
+template <class C, int KIND, class PreLast>
 __device__ __forceinline__ void main_loop(floatx16 (&acc)[C::MI][C::NI], const Src &src, int nk, int wave, int wm,
-                                          int wn, int lane) {
+                                          int wn, int lane, const PreLast &pre_last) {
     static_assert(C::STAGES == 2 && C::NF <= C::NM, "ring");
     constexpr int L = C::LPS;
 #pragma unroll
@@ -287,23 +292,11 @@ __device__ __forceinline__ void main_loop(floatx16 (&acc)[C::MI][C::NI], const S
         ring_stage<C, KIND, 1, true, false>(acc, src, kt + 1, wave, wm, wn, lane, fa, fb);
     }
     ring_stage<C, KIND, 0, false, false>(acc, src, kt, wave, wm, wn, lane, fa, fb);
+    pre_last();
     ring_stage<C, KIND, 1, false, true>(acc, src, kt + 1, wave, wm, wn, lane, fa, fb);
 }
 
-// DMA of EPI_ROWS rows x 64 fp32 (256 bytes per row) starting at `src` (row
-// pitch ld bytes) into a staging area: instructions of 4 rows each; lane i
-// lands at byte 16 i of its 1 KB block, i.e. row i/16, swizzled chunk i%16.
-template <class C>
-__device__ __forceinline__ void dma_epi(char *dst, const char *src, int64_t ld, int lane) {
-#pragma unroll
-    for (int t = 0; t < C::EPI_ROWS / 4; ++t) {
-        const int row = 4 * t + (lane >> 4);
-        const int chunk = (lane & 15) ^ (row & 15);
-        dma16(src + row * ld + chunk * 16, dst + t * 1024);
-    }
-}
-
-// DMA of EPI_ROWS rows x 64 bf16 (128 bytes per row, X_hi) starting
+// DMA of EPI_ROWS rows x 64 bf16 (128 bytes per row: X_hi, or A) starting
 // at `src` (row pitch ld bytes) into a staging area: instructions of 8 rows
 // each; lane i carries row i/8, chunk i%8 stored at chunk (i%8) ^ ((row/2)%8),
 // so 16 consecutive rows reading one chunk touch 16 distinct bank groups.
@@ -347,30 +340,38 @@ __device__ __forceinline__ void tri_decode(int64_t t, int *ti, int *tj) {
 
 // ------------------------------------------------------------------------ A, B
 
+// Rows of A that POLY's epilogue combines with the wave's block: the block
+// itself, bf16, row pitch sp.
+__device__ __forceinline__ const char *poly_a_rows(const Geom &g, const Work &w, int64_t e, int64_t row0,
+                                                   int64_t col0) {
+    return reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.ab) + e * w.a_stride + row0 * g.sp + col0);
+}
+
 // Epilogue of GRAM and POLY.  The wave's 128 x 64 block is finished in four
-// rounds of 32 rows staged in LDS.  POLY first brings the matching rows of the
-// fp32 A by DMA (two areas, the next round in flight).  The values (GRAM: A,
-// times inv_norm^2 on the bf16 path's first step; POLY: b A + c A A, times
+// rounds of 32 rows staged in LDS.  POLY brings the matching rows of the bf16
+// A by DMA (two areas, the next round in flight; round 0 was issued into
+// area 0 under the last stage of the main loop).  The values (GRAM:
+// A, times inv_norm^2 on the bf16 path's first step; POLY: b A + c A A, times
 // inv_norm on that step, so that B X applies the normalisation of X) are
 // formed in the accumulator layout and written in place as fp32 rows; the
-// rows are stored whole (GRAM: fp32 A and its bf16 operand copy; POLY: bf16
-// B), and for an off-diagonal tile each column of the block is stored as 32
-// consecutive bf16 of a row of the mirrored tile.  Vector-memory instructions
-// retire in issue order; the wait before POLY's round h allows what was issued
-// after round h's DMA: round h-1's stores (at least ROW_STORES) and round h+1's
-// DMA.
+// rows are stored whole as bf16 (GRAM: A; POLY: B), and for an off-diagonal
+// tile each column of the block is stored as 32 consecutive bf16 of a row of
+// the mirrored tile.  A exists only in bf16: the b A term of B taken from it
+// instead of an fp32 copy changes nothing measurable once B itself is rounded
+// to bf16.  Vector-memory instructions retire in issue order; the wait before
+// POLY's round h allows what was issued after round h's DMA: round h-1's
+// stores (at least ROW_STORES) and round h+1's DMA.
 template <class C, int KIND>
 __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI], const Geom &g, const Work &w,
                                              const NsStep &p, int64_t e, int ti, int tj, int wm, int wn,
                                              char *const (&area)[2], int lane) {
     constexpr int ROUNDS = C::WM / C::EPI_ROWS;
-    constexpr int DMA_PER_ROUND = C::EPI_ROWS / 4;
+    constexpr int DMA_PER_ROUND = C::EPI_ROWS / 8;
     constexpr int ROW_STORES = C::EPI_ROWS / 4;
     static_assert(ROUNDS == C::MI && C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
     const int64_t ld = g.sp;
     const int64_t row0 = static_cast<int64_t>(ti) * C::BM + wm * C::WM;
     const int64_t col0 = static_cast<int64_t>(tj) * C::BN + wn * C::WN;
-    float *af = w.af + e * w.a_stride;
     uint16_t *dst = static_cast<uint16_t *>(KIND == GRAM ? w.ab : w.bb) + e * w.a_stride;
     const bool mirror = ti != tj;
     // first step on the bf16 path: X holds N, so A = inv^2 (N N^T) and the
@@ -378,11 +379,8 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
     const float inv = p.unnormalized ? w.inv_norm[e] : 1.0f;
     const float gscale = inv * inv;
     const float pb = p.b * inv, pc = p.c * inv;
-    const char *a_in = reinterpret_cast<const char *>(af + row0 * ld + col0);
-    if constexpr (KIND == POLY) {
-        dma_epi<C>(area[0], a_in, ld * 4, lane);
-        dma_epi<C>(area[1], a_in + C::EPI_ROWS * ld * 4, ld * 4, lane);
-    }
+    const char *a_in = poly_a_rows(g, w, e, row0, col0);
+    if constexpr (KIND == POLY) dma_bf16_rows<C>(area[1], a_in + C::EPI_ROWS * ld * 2, ld * 2, lane);
     const int lrow = lane & 31;
 #pragma unroll
     for (int h = 0; h < ROUNDS; ++h) {
@@ -405,7 +403,9 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
 #pragma unroll
                     for (int q = 0; q < 4; ++q) v[ni][c4][q] = acc[h][ni][4 * c4 + q] * gscale;
                 } else {
-                    const floatx4 a4 = *reinterpret_cast<const floatx4 *>(reg + epi_offset(lrow, lcol >> 2));
+                    const u32x2 a2 = *reinterpret_cast<const u32x2 *>(reg + pair_offset(lrow, lcol));
+                    const float a4[4] = {__uint_as_float(a2[0] << 16), __uint_as_float(a2[0] & 0xffff0000u),
+                                         __uint_as_float(a2[1] << 16), __uint_as_float(a2[1] & 0xffff0000u)};
 #pragma unroll
                     for (int q = 0; q < 4; ++q) v[ni][c4][q] = __builtin_fmaf(pb, a4[q], pc * acc[h][ni][4 * c4 + q]);
                 }
@@ -426,7 +426,6 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
             const int rrow = 4 * r4 + (lane >> 4), chunk = lane & 15;
             const floatx4 x = *reinterpret_cast<const floatx4 *>(reg + epi_offset(rrow, chunk));
             const int64_t idx = (rbase + rrow) * ld + col0 + 4 * chunk;
-            if constexpr (KIND == GRAM) *reinterpret_cast<floatx4 *>(af + idx) = x;
             u32x2 pk;
             pk[0] = pack_bf16x2(x[0], x[1]);
             pk[1] = pack_bf16x2(x[2], x[3]);
@@ -452,7 +451,7 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
             if (h + 2 < ROUNDS) {
                 wait_lgkm0();  // this round's LDS reads are done before the DMA refills the area
                 asm volatile("" ::: "memory");
-                dma_epi<C>(reg, a_in + C::EPI_ROWS * (h + 2) * ld * 4, ld * 4, lane);
+                dma_bf16_rows<C>(reg, a_in + C::EPI_ROWS * (h + 2) * ld * 2, ld * 2, lane);
             }
         }
     }
@@ -493,7 +492,14 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
         for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-    main_loop<C, KIND>(acc, src, static_cast<int>(kdim / C::BK), wave, wm, wn, lane);
+    auto pre_last = [&] {
+        if constexpr (KIND == POLY)
+            dma_bf16_rows<C>(epi_area<0>(wave),
+                             poly_a_rows(g, w, e, static_cast<int64_t>(ti) * C::BM + wm * C::WM,
+                                         static_cast<int64_t>(tj) * C::BN + wn * C::WN),
+                             g.sp * 2, lane);
+    };
+    main_loop<C, KIND>(acc, src, static_cast<int>(kdim / C::BK), wave, wm, wn, lane, pre_last);
 
     // acc[mi][ni][4*c4 + q] holds output row wm*WM + mi*32 + lane%32, column
     // wn*WN + ni*32 + 8*c4 + 4*(lane/32) + q of the tile.
@@ -530,11 +536,29 @@ struct ApplyTile {
     int64_t col0;  // first output column
 };
 
+// First rows of X_hi (row pitch 2 lp bytes) and X_lo (pitch lp) of a wave's
+// output block, and the DMA of one round (EPI_ROWS rows of each) into a
+// staging area: X_hi rows in its first PAIR_HALF bytes, X_lo rows after.
+constexpr int PAIR_HALF = 4096;
+struct XRows {
+    const char *hi, *lo;
+    int64_t ld_hi, ld_lo;
+};
+__device__ __forceinline__ XRows x_rows(const Geom &g, const Work &w, const ApplyTile &t) {
+    const int64_t first = t.row0 * g.lp + t.col0;
+    return {reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xb) + t.e * w.x_stride + first),
+            reinterpret_cast<const char *>(static_cast<const uint8_t *>(w.xl) + t.e * w.x_stride + first), g.lp * 2,
+            g.lp};
+}
+__device__ __forceinline__ void dma_x_round(char *dst, const XRows &x, int h, int lane) {
+    dma_bf16_rows<Cfg>(dst, x.hi + Cfg::EPI_ROWS * h * x.ld_hi, x.ld_hi, lane);
+    dma_lo8_rows<Cfg>(dst + PAIR_HALF, x.lo + Cfg::EPI_ROWS * h * x.ld_lo, x.ld_lo, lane);
+}
+
 // Row lrow's four columns lcol .. lcol+3 of a X + B X, with X = X_hi + X_lo
 // staged in `reg` (X_hi rows, 128 bytes each, in the first PAIR_HALF bytes;
 // X_lo rows, 64 bytes each, after).  While X still holds N, `a` is a inv_norm
 // (and B was scaled by inv_norm when it was formed).
-constexpr int PAIR_HALF = 4096;
 __device__ __forceinline__ floatx4 apply_value(const floatx16 &acc, const char *reg, int lrow, int lcol, int c4,
                                                float a) {
     const u32x2 h = *reinterpret_cast<const u32x2 *>(reg + pair_offset(lrow, lcol));
@@ -580,7 +604,8 @@ __device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char
 // EPI_ROWS rows the wave's X_hi and X_lo rows arrive in a staging area by DMA;
 // the values are formed in the accumulator layout and rewritten there as fp32
 // rows, then read row-contiguously (16 lanes per row) so the stores move whole
-// rows.  Two staging areas: the DMA of round h+2 is issued once round h's
+// rows.  Two staging areas: round 0's DMA was issued under the last stage of
+// the main loop, round 1's on entry, and the DMA of round h+2 once round h's
 // reads are done, so one round is always in flight.  Per round and lane:
 // EPI_ROWS/8 + EPI_ROWS/16 DMA instructions (X_hi, X_lo) and 2*EPI_ROWS/4
 // stores, unconditionally;
@@ -598,10 +623,7 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::M
     static_assert(C::EPI_ROWS * 128 == PAIR_HALF, "X_hi and X_lo rows fill one staging area");
     uint8_t *xl = static_cast<uint8_t *>(w.xl) + t.e * w.x_stride;
     uint16_t *xh_out = static_cast<uint16_t *>(w.xb_next) + t.e * w.x_stride;
-    const int64_t first = t.row0 * g.lp + t.col0;
-    const char *hi_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xb) + t.e * w.x_stride + first);
-    const char *lo_in = reinterpret_cast<const char *>(xl + first);
-    const int64_t ld = g.lp * 2, ld_lo = g.lp;
+    const XRows x = x_rows(g, w, t);
     const float a = p.unnormalized ? p.a * w.inv_norm[t.e] : p.a;
     // Stores: a wave-uniform row base plus a per-lane 32-bit offset (lane
     // (rr, chunk) owns columns 4 chunk .. +3 of row rr of each group of four).
@@ -609,12 +631,7 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::M
     const uint32_t off_lo = static_cast<uint32_t>(rr * g.lp + 4 * chunk);
     const uint32_t off_hi = 2 * off_lo;
     const int64_t row0 = uniform64(t.row0), col0 = uniform64(t.col0);
-    auto dma_round = [&](char *dst, int h) {
-        dma_bf16_rows<C>(dst, hi_in + C::EPI_ROWS * h * ld, ld, lane);
-        dma_lo8_rows<C>(dst + PAIR_HALF, lo_in + C::EPI_ROWS * h * ld_lo, ld_lo, lane);
-    };
-    dma_round(area[0], 0);
-    dma_round(area[1], 1);
+    dma_x_round(area[1], x, 1, lane);
 #pragma unroll
     for (int h = 0; h < ROUNDS; ++h) {
         if (h == 0)
@@ -640,7 +657,7 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::M
         if (h + 2 < ROUNDS) {
             wait_lgkm0();  // this round's LDS reads are done before the DMA refills the area
             asm volatile("" ::: "memory");
-            dma_round(area[h & 1], h + 2);
+            dma_x_round(area[h & 1], x, h + 2, lane);
         }
     }
 }
@@ -690,28 +707,31 @@ __device__ __forceinline__ void update_row4(const MatDesc &d, const Geom &g, con
 }
 
 // Epilogue of the last step: W <- d W - s_scale X' (and O' = X' when asked),
-// orientation-aware.  One staging area, one round at a time.  For W in the
-// orientation of X' the values are rewritten as fp32 rows and the update walks
-// whole rows (16 lanes per 64-column row); for transposed W the accumulator
-// layout already puts 32 consecutive X' rows, i.e. 32 consecutive elements of
-// a W row, in consecutive lanes.
+// orientation-aware.  Two staging areas: round 0's X rows were requested under
+// the last stage of the main loop; round h+1's are requested as soon as round
+// h's have landed, so they arrive while round h is computed.  For W in the
+// orientation of X' the values are rewritten as fp32 rows and the update
+// walks whole rows (16 lanes per 64-column row); for transposed W the
+// accumulator layout already puts 32 consecutive X' rows, i.e. 32 consecutive
+// elements of a W row, in consecutive lanes.
 template <int PARAM_BF16>
 __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Cfg::MI][Cfg::NI], const MatDesc &d,
                                                       const Geom &g, const Work &w, const NsStep &p,
-                                                      const ApplyTile &t, char *reg, int lane) {
+                                                      const ApplyTile &t, char *const (&area)[2], int lane) {
     using C = Cfg;
     constexpr int ROUNDS = C::WM / C::EPI_ROWS;
     static_assert(C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
-    const int64_t first = t.row0 * g.lp + t.col0;
-    const char *hi_in = reinterpret_cast<const char *>(static_cast<const uint16_t *>(w.xb) + t.e * w.x_stride + first);
-    const char *lo_in = reinterpret_cast<const char *>(static_cast<const uint8_t *>(w.xl) + t.e * w.x_stride + first);
-    const int64_t ld = g.lp * 2, ld_lo = g.lp;
+    const XRows x = x_rows(g, w, t);
     const float a = p.unnormalized ? p.a * w.inv_norm[t.e] : p.a;
 #pragma unroll
     for (int h = 0; h < ROUNDS; ++h) {
-        dma_bf16_rows<C>(reg, hi_in + C::EPI_ROWS * h * ld, ld, lane);
-        dma_lo8_rows<C>(reg + PAIR_HALF, lo_in + C::EPI_ROWS * h * ld_lo, ld_lo, lane);
-        fenced_wait_vmcnt<0>();
+        char *reg = area[h & 1];
+        fenced_wait_vmcnt<0>();  // round h's rows (and round h-1's stores)
+        if (h + 1 < ROUNDS) {
+            // area (h+1)&1 was last read in round h-1, whose reads ended with it
+            dma_x_round(area[(h + 1) & 1], x, h + 1, lane);
+            asm volatile("" ::: "memory");
+        }
         const int lrow = lane & 31;
         if (g.transposed) {
             const int64_t gi = t.row0 + C::EPI_ROWS * h + lrow;
@@ -728,19 +748,20 @@ __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Cfg:
 #pragma unroll 4
             for (int r4 = 0; r4 < C::EPI_ROWS / 4; ++r4) {
                 const int rrow = 4 * r4 + (lane >> 4), chunk = lane & 15;
-                const floatx4 x = *reinterpret_cast<const floatx4 *>(reg + epi_offset(rrow, chunk));
+                const floatx4 xv = *reinterpret_cast<const floatx4 *>(reg + epi_offset(rrow, chunk));
                 const int64_t gi = t.row0 + C::EPI_ROWS * h + rrow;
-                if (gi < g.s) update_row4<PARAM_BF16>(d, g, p, gi, t.col0 + 4 * chunk, x);
+                if (gi < g.s) update_row4<PARAM_BF16>(d, g, p, gi, t.col0 + 4 * chunk, xv);
             }
         }
-        if (h + 1 < ROUNDS) {
-            wait_lgkm0();  // this round's LDS reads finish before the next DMA overwrites them
-            asm volatile("" ::: "memory");
-        }
+        wait_lgkm0();  // this round's LDS reads finish before a later DMA refills the area
+        asm volatile("" ::: "memory");
     }
 }
 
-template <int PARAM_BF16>
+// MODE 0: intermediate step (X' to the workspace); 1 / 2: last step with the
+// fused update of an fp32 / bf16 parameter.  One epilogue per instantiation
+// keeps each within the register file.
+template <int MODE>
 __global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__restrict__ descs, Geom g, Work w,
                                                                NsStep p, int64_t tiles_per_mat, int64_t nblocks) {
     using C = Cfg;
@@ -767,21 +788,26 @@ __global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__r
         for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-    main_loop<C, APPLY>(acc, src, static_cast<int>(g.sp / C::BK), wave, wm, wn, lane);
+    auto tile_of = [&] {
+        return ApplyTile{e, static_cast<int64_t>(ti) * C::BM + wm * C::WM,
+                         static_cast<int64_t>(tj) * C::BN + wn * C::WN};
+    };
+    auto pre_last = [&] { dma_x_round(epi_area<0>(wave), x_rows(g, w, tile_of()), 0, lane); };
+    main_loop<C, APPLY>(acc, src, static_cast<int>(g.sp / C::BK), wave, wm, wn, lane, pre_last);
+    const ApplyTile t_ = tile_of();
 
     // Swapped product: acc[mi][ni][4*c4 + q] holds output row
     //   m = wm*WM + mi*32 + lane%32,  columns n = wn*WN + ni*32 + 8*c4 + 4*(lane/32) + q, q = 0..3
-    // The fp32 X of the aX term is staged through LDS in rounds of EPI_ROWS
-    // rows, each wave loading its own slice with the DMA, then read back in
-    // the accumulator layout.
-    const ApplyTile t_{e, static_cast<int64_t>(ti) * C::BM + wm * C::WM, static_cast<int64_t>(tj) * C::BN + wn * C::WN};
+    // X_hi and X_lo of the aX term are staged through LDS in rounds of
+    // EPI_ROWS rows, each wave loading its own slice with the DMA, then read
+    // back in the accumulator layout.
     char *const area[2] = {epi_area<0>(wave), epi_area<1>(wave)};
     wait_lgkm0();
     stage_barrier();  // every wave is done with the operand ring
-    if (p.final_update)
-        apply_epilogue_update<PARAM_BF16>(acc, descs[e], g, w, p, t_, area[0], lane);
-    else
+    if constexpr (MODE == 0)
         apply_epilogue_next(acc, g, w, p, t_, area, lane);
+    else
+        apply_epilogue_update<MODE == 2>(acc, descs[e], g, w, p, t_, area, lane);
 }
 
 }  // namespace bf16path
@@ -803,12 +829,13 @@ hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const 
     }
     const int64_t tiles = (g.sp / Cfg::BM) * (g.lp / Cfg::BN);
     const int64_t nblocks = tiles * nmat;
-    if (p.final_update && p.param_bf16)
-        hipLaunchKernelGGL(ns_apply_kernel<1>, dim3(static_cast<unsigned>(nblocks)), dim3(Cfg::NT), 0, st, descs, g,
-                           w, p, tiles, nblocks);
+    const dim3 grid(static_cast<unsigned>(nblocks)), block(Cfg::NT);
+    if (!p.final_update)
+        ns_apply_kernel<0><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
+    else if (p.param_bf16)
+        ns_apply_kernel<2><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
     else
-        hipLaunchKernelGGL(ns_apply_kernel<0>, dim3(static_cast<unsigned>(nblocks)), dim3(Cfg::NT), 0, st, descs, g,
-                           w, p, tiles, nblocks);
+        ns_apply_kernel<1><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
     return hipGetLastError();
 }
 

@@ -227,7 +227,7 @@ struct GroupPlan {
 // Bytes of NS workspace one matrix of geometry g needs.
 size_t per_matrix_bytes(const Geom &g, bool bf16) {
     const size_t x = static_cast<size_t>(g.sp * g.lp), a = static_cast<size_t>(g.sp * g.sp);
-    return bf16 ? (x * (2 + 2 + 1) + a * (4 + 2 + 2)) : (x * (4 + 4) + a * (4 + 4 + 4));
+    return bf16 ? (x * (2 + 2 + 1) + a * (2 + 2)) : (x * (4 + 4) + a * (4 + 4 + 4));
 }
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
@@ -242,12 +242,13 @@ Layout chunk_layout(const Geom &g, bool bf16, int64_t n) {
     Layout L{};
     size_t off = 0;
     if (bf16) {
-        // X as hi (bf16, ping-pong) + its 8-bit residual lo (in place); no fp32 X.
+        // X as hi (bf16, ping-pong) + its 8-bit residual lo (in place); no fp32 X
+        // and no fp32 A (A lives in bf16 only).
         L.has_xf = false;
         L.xb0 = off; off = align_up(off + x * 2);
         L.xb1 = off; off = align_up(off + x * 2);
         L.xl = off; off = align_up(off + x * 1);
-        L.af = off; off = align_up(off + a * 4);
+        L.af = 0;
         L.ab = off; off = align_up(off + a * 2);
         L.bb = off; off = align_up(off + a * 2);
     } else {
@@ -487,7 +488,7 @@ Work chunk_work(muon_context *ctx, const Geom &g, bool bf16, int64_t n, int bpm,
     w.xb = bf16 ? static_cast<void *>(base + L.xb0) : nullptr;
     w.xb_next = bf16 ? static_cast<void *>(base + L.xb1) : nullptr;
     w.xl = bf16 ? static_cast<void *>(base + L.xl) : nullptr;
-    w.af = reinterpret_cast<float *>(base + L.af);
+    w.af = bf16 ? nullptr : reinterpret_cast<float *>(base + L.af);
     w.ab = base + L.ab;
     w.bb = base + L.bb;
     w.x_stride = g.sp * g.lp;
@@ -513,12 +514,13 @@ void ns_work(int stage, const Geom &g, bool bf16, int n, bool ns_out, int psize,
     const double s = static_cast<double>(g.s), l = static_cast<double>(g.l), es = bf16 ? 2.0 : 4.0;
     switch (stage) {
         case ST_GRAM:
+            // X read; A written (fp32 path: lower triangle in fp32 plus the operand copy)
             *flops = l * s * (s + 1);
-            *bytes = s * l * es + s * (s + 1) / 2 * 4 + s * s * es;
+            *bytes = s * l * es + (bf16 ? 0.0 : s * (s + 1) / 2 * 4) + s * s * es;
             break;
         case ST_POLY:
             *flops = s * s * (s + 1);
-            *bytes = s * s * es + s * (s + 1) / 2 * 4 + s * s * es;
+            *bytes = s * s * es + (bf16 ? 0.0 : s * (s + 1) / 2 * 4) + s * s * es;
             break;
         case ST_APPLY:
             // B, X operand, then X_lo in and (X_hi, X_lo) out (2 + 1 bytes); fp32 path: X in, X out

@@ -211,8 +211,8 @@ def test_workspace_bytes_moe_batch(lib):
     out = ctypes.c_size_t()
     assert lib.muon_workspace_bytes(arr, 256, ctypes.byref(hp), ctypes.byref(out)) == ms.MUON_OK
     x, a = 2048 * 7168, 2048 * 2048
-    # bf16 path: X as hi (two ping-pong bf16 copies) + its 8-bit residual lo; A fp32 + bf16; B bf16
-    ns = 256 * (x * (2 + 2 + 1) + a * (4 + 2 + 2))
+    # bf16 path: X as hi (two ping-pong bf16 copies) + its 8-bit residual lo; A bf16; B bf16
+    ns = 256 * (x * (2 + 2 + 1) + a * (2 + 2))
     assert ns <= out.value <= ns + 64 * 1024 * 1024
 
 
