@@ -191,6 +191,13 @@ __device__ __forceinline__ floatx4 join_bf16x4(const u32x2 &h, uint32_t l) {
     return v;
 }
 
+// Pointers read from descriptor tables are generic to the compiler, which
+// then addresses them with flat instructions (which also count as LDS
+// accesses in lgkmcnt).  Every such pointer here points to device memory.
+template <class T> __device__ __forceinline__ __attribute__((address_space(1))) T *as_global(T *p) {
+    return (__attribute__((address_space(1))) T *)p;
+}
+
 // Blocks whose ids the hardware spreads round-robin over the 8 XCDs are
 // renumbered so that consecutive logical ids run on the same XCD (and share
 // its L2).  Bijective on [0, nblocks).

@@ -109,24 +109,26 @@ __global__ __launch_bounds__(256) void nesterov_rows_kernel(const MatDesc *__res
     const int64_t cols = g.cols;
     double acc = 0.0;
     if (VEC) {
-        const int64_t cv = cols / 4;
-        const int64_t total = (r1 - r0) * cv;
-        for (int64_t t = threadIdx.x; t < total; t += 256) {
-            const int64_t i = r0 + t / cv;
-            const int64_t j = (t % cv) * 4;
+        // a block covers at most 65536 / 4 vectors: 32-bit index arithmetic
+        const int cv = static_cast<int>(cols / 4);
+        const int total = static_cast<int>((r1 - r0) * cv);
+        for (int t = threadIdx.x; t < total; t += 256) {
+            const int ii = t / cv;
+            const int64_t i = r0 + ii;
+            const int64_t j = 4 * static_cast<int64_t>(t - ii * cv);
             const int64_t src = i * cols + j;
             float gv[4];
             if constexpr (sizeof(GradT) == 2) {
-                const u32x2 raw = *reinterpret_cast<const u32x2 *>(gp + src);
+                const u32x2 raw = *as_global(reinterpret_cast<const u32x2 *>(gp + src));
                 gv[0] = __uint_as_float(raw[0] << 16);
                 gv[1] = __uint_as_float(raw[0] & 0xffff0000u);
                 gv[2] = __uint_as_float(raw[1] << 16);
                 gv[3] = __uint_as_float(raw[1] & 0xffff0000u);
             } else {
-                const floatx4 raw = *reinterpret_cast<const floatx4 *>(gp + src);
+                const floatx4 raw = *as_global(reinterpret_cast<const floatx4 *>(gp + src));
                 gv[0] = raw[0]; gv[1] = raw[1]; gv[2] = raw[2]; gv[3] = raw[3];
             }
-            floatx4 m = *reinterpret_cast<const floatx4 *>(mp + src);
+            floatx4 m = *as_global(reinterpret_cast<const floatx4 *>(mp + src));
             floatx4 mo, no;
             for (int q = 0; q < 4; ++q) {
                 const float m1 = mu * m[q] + gv[q];
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256) void nesterov_rows_kernel(const MatDesc *__res
                 no[q] = n;
                 acc += static_cast<double>(n) * static_cast<double>(n);
             }
-            *reinterpret_cast<floatx4 *>(mp + src) = mo;
+            *as_global(reinterpret_cast<floatx4 *>(mp + src)) = mo;
             const int64_t dst = i * g.lp + j;
             if (xf) {
                 *reinterpret_cast<floatx4 *>(xf + dst) = no;
@@ -422,10 +424,10 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamwDesc *__restrict_
                        reinterpret_cast<uintptr_t>(d.m) | reinterpret_cast<uintptr_t>(d.v)) & 15) == 0;
     const int64_t i = base + threadIdx.x * 4;
     if (vec && i + 4 <= d.numel) {
-        floatx4 p = *reinterpret_cast<const floatx4 *>(d.param + i);
-        const floatx4 gg = *reinterpret_cast<const floatx4 *>(d.grad + i);
-        floatx4 m = *reinterpret_cast<const floatx4 *>(d.m + i);
-        floatx4 v = *reinterpret_cast<const floatx4 *>(d.v + i);
+        floatx4 p = *as_global(reinterpret_cast<const floatx4 *>(d.param + i));
+        const floatx4 gg = *as_global(reinterpret_cast<const floatx4 *>(d.grad + i));
+        floatx4 m = *as_global(reinterpret_cast<const floatx4 *>(d.m + i));
+        floatx4 v = *as_global(reinterpret_cast<const floatx4 *>(d.v + i));
         for (int q = 0; q < 4; ++q) {
             const float p1 = k.decay * p[q];
             const float m1 = k.beta1 * m[q] + k.one_minus_beta1 * gg[q];
@@ -437,9 +439,9 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamwDesc *__restrict_
             m[q] = m1;
             v[q] = v1;
         }
-        *reinterpret_cast<floatx4 *>(d.param + i) = p;
-        *reinterpret_cast<floatx4 *>(d.m + i) = m;
-        *reinterpret_cast<floatx4 *>(d.v + i) = v;
+        *as_global(reinterpret_cast<floatx4 *>(d.param + i)) = p;
+        *as_global(reinterpret_cast<floatx4 *>(d.m + i)) = m;
+        *as_global(reinterpret_cast<floatx4 *>(d.v + i)) = v;
     } else {
         for (int q = 0; q < 4; ++q) {
             const int64_t ii = i + q;

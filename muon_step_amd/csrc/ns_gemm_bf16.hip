@@ -671,23 +671,23 @@ __device__ __forceinline__ void update_row4(const MatDesc &d, const Geom &g, con
     if (!g.transposed && (g.cols % 4 == 0) && gj + 3 < g.l) {
         const int64_t widx = gi * g.cols + gj;
         if (PARAM_BF16) {
-            uint16_t *pp = static_cast<uint16_t *>(d.param) + widx;
-            const u32x2 wv = *reinterpret_cast<const u32x2 *>(pp);
+            auto *pp = as_global(reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(d.param) + widx));
+            const u32x2 wv = *pp;
             u32x2 o;
             o[0] = pack_bf16x2(p.dscale * __uint_as_float(wv[0] << 16) - p.sscale * v[0],
                                p.dscale * __uint_as_float(wv[0] & 0xffff0000u) - p.sscale * v[1]);
             o[1] = pack_bf16x2(p.dscale * __uint_as_float(wv[1] << 16) - p.sscale * v[2],
                                p.dscale * __uint_as_float(wv[1] & 0xffff0000u) - p.sscale * v[3]);
-            *reinterpret_cast<u32x2 *>(pp) = o;
+            *pp = o;
         } else {
-            float *pp = static_cast<float *>(d.param) + widx;
-            const floatx4 wv = *reinterpret_cast<const floatx4 *>(pp);
+            auto *pp = as_global(reinterpret_cast<floatx4 *>(static_cast<float *>(d.param) + widx));
+            const floatx4 wv = *pp;
             floatx4 o;
 #pragma unroll
             for (int q = 0; q < 4; ++q) o[q] = p.dscale * wv[q] - p.sscale * v[q];
-            *reinterpret_cast<floatx4 *>(pp) = o;
+            *pp = o;
         }
-        if (d.ns_out) *reinterpret_cast<floatx4 *>(d.ns_out + widx) = v;
+        if (d.ns_out) *as_global(reinterpret_cast<floatx4 *>(d.ns_out + widx)) = v;
         return;
     }
 #pragma unroll
@@ -695,14 +695,14 @@ __device__ __forceinline__ void update_row4(const MatDesc &d, const Geom &g, con
         if (gj + q >= g.l) continue;
         const int64_t widx = g.transposed ? ((gj + q) * g.cols + gi) : (gi * g.cols + gj + q);
         if (PARAM_BF16) {
-            uint16_t *pp = static_cast<uint16_t *>(d.param);
+            auto *pp = as_global(static_cast<uint16_t *>(d.param));
             const float wv = bf16_bits_to_float(pp[widx]);
             pp[widx] = float_to_bf16_bits(p.dscale * wv - p.sscale * v[q]);
         } else {
-            float *pp = static_cast<float *>(d.param);
+            auto *pp = as_global(static_cast<float *>(d.param));
             pp[widx] = p.dscale * pp[widx] - p.sscale * v[q];
         }
-        if (d.ns_out) d.ns_out[widx] = v[q];
+        if (d.ns_out) as_global(d.ns_out)[widx] = v[q];
     }
 }
 
