@@ -107,6 +107,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // hi's precision is kept, and infinite or NaN hi absorbs any residual); below
 // 2^-126 the unit is still consistent, with hi's precision the limit.
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t s16x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t LO8_REF_ADD = 0x04400000u;  // exponent + 8, mantissa 0.5
 constexpr uint32_t LO8_EXP_CAP = 246u << 23;    // exponent field 246 (e = 119)
 
@@ -158,17 +159,31 @@ __device__ __forceinline__ void split_bf16x4(const floatx4 &v, u32x2 *hi, uint32
     // bf16 a second time to get its float hi
     asm volatile("" : "+v"(h[0]), "+v"(h[1]));
     *hi = h;
+    if (BOUNDED) {
+        // References with clear low halves: the low 16 bits of the rounded
+        // sum are then q itself (|q| <= 128 never borrows across bit 16), two
+        // of them gather into one register and one packed min clamps both
+        // (q >= -128 always holds).
+        u32x2 qq;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const uint32_t m0 = ((h[k] & 0x7f80u) << 16) + LO8_REF_ADD;
+            const uint32_t m1 = (h[k] & 0x7f800000u) + LO8_REF_ADD;
+            const float t0 = (v[2 * k] - __uint_as_float(h[k] << 16)) + __uint_as_float(m0);
+            const float t1 = (v[2 * k + 1] - __uint_as_float(h[k] & 0xffff0000u)) + __uint_as_float(m1);
+            // v_perm_b32 picks bytes of {src0, src1} (src1 = bytes 0..3)
+            const uint32_t g = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x05040100u);
+            const s16x2 c = {127, 127};
+            qq[k] = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(s16x2, g), c));
+        }
+        *lo = __builtin_amdgcn_perm(qq[1], qq[0], 0x06040200u);
+        return;
+    }
     int q[4];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         uint32_t m0, m1;
-        if (BOUNDED) {
-            const uint32_t eb = h[k] & 0x7f807f80u;
-            m0 = (eb << 16) + LO8_REF_ADD;
-            m1 = eb + LO8_REF_ADD;
-        } else {
-            lo8_ref2(h[k], &m0, &m1);
-        }
+        lo8_ref2(h[k], &m0, &m1);
         q[2 * k] = lo8_q(v[2 * k], __uint_as_float(h[k] << 16), m0);
         q[2 * k + 1] = lo8_q(v[2 * k + 1], __uint_as_float(h[k] & 0xffff0000u), m1);
     }
