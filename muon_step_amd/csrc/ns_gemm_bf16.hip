@@ -139,6 +139,13 @@ template <class C> __device__ __forceinline__ int nc_offset(int krow, int byte) 
 // 64 banks.
 __device__ __forceinline__ int epi_offset(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
 
+// Length of a K loop over a padded dimension of true length n: the padding
+// beyond n is zero and adds nothing, so the loop stops at the first multiple
+// of two 64-k stages (the loop runs stages in pairs) at or after n.
+__device__ __forceinline__ int64_t k_extent(int64_t n, int64_t padded) {
+    return min(padded, (n + 2 * Cfg::BK - 1) / (2 * Cfg::BK) * (2 * Cfg::BK));
+}
+
 struct Src {
     const char *p;  // P operand (output rows): K-contiguous rows of X, A or B
     int64_t ld_p;
@@ -474,13 +481,13 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
     if (KIND == GRAM) {
         const char *x = static_cast<const char *>(w.xb) + e * w.x_stride * 2;
         src.ld_p = src.ld_q = g.lp * 2;
-        kdim = g.lp;
+        kdim = k_extent(g.l, g.lp);
         src.p = x + static_cast<int64_t>(ti) * C::BM * src.ld_p;
         src.q = x + static_cast<int64_t>(tj) * C::BN * src.ld_q;
     } else {
         const char *a = static_cast<const char *>(w.ab) + e * w.a_stride * 2;
         src.ld_p = src.ld_q = g.sp * 2;
-        kdim = g.sp;
+        kdim = k_extent(g.s, g.sp);
         src.p = a + static_cast<int64_t>(ti) * C::BM * src.ld_p;
         src.q = a + static_cast<int64_t>(tj) * C::BN * src.ld_q;
     }
@@ -793,7 +800,7 @@ __global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__r
                          static_cast<int64_t>(tj) * C::BN + wn * C::WN};
     };
     auto pre_last = [&] { dma_x_round(epi_area<0>(wave), x_rows(g, w, tile_of()), 0, lane); };
-    main_loop<C, APPLY>(acc, src, static_cast<int>(g.sp / C::BK), wave, wm, wn, lane, pre_last);
+    main_loop<C, APPLY>(acc, src, static_cast<int>(k_extent(g.s, g.sp) / C::BK), wave, wm, wn, lane, pre_last);
     const ApplyTile t_ = tile_of();
 
     // Swapped product: acc[mi][ni][4*c4 + q] holds output row
