@@ -68,6 +68,16 @@ struct Cfg {
     static constexpr int EPI_ROWS = EPI_BYTES / 256;   // rows of 64 fp32 per staging round
     static constexpr int NM = MI * NI;                 // MFMAs per wave and 16-k substep
     static constexpr int NF = MI + NI;                 // fragments per wave and substep
+    static constexpr bool MFMA = true;                 // the wave's products are issued
+};
+
+// The K loop of a GRAM or POLY wave whose 128 output rows all lie in the zero
+// padding beyond s (last tile row when s is not a multiple of 256): it keeps its
+// share of the copies, reads and barriers but issues no products (its
+// accumulators stay zero, which is their value), so the other wave on its
+// SIMD has the matrix core to itself.
+struct CfgIdle : Cfg {
+    static constexpr bool MFMA = false;
 };
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_tr;
@@ -244,7 +254,7 @@ __device__ __forceinline__ void substep(floatx16 (&acc)[C::MI][C::NI], const Fra
     static_assert(EVERY >= 1 && C::NM % C::LPS == 0, "one DMA block per product slot");
 #pragma unroll
     for (int i = 0; i < C::NM; ++i) {
-        mma_one<C>(acc, f, i);
+        if constexpr (C::MFMA) mma_one<C>(acc, f, i);
         if (READ && i < C::NF) read_frag<C, KIND, S_READ>(g, i, ks_next, wm, wn, lane);
         if (ISSUE_DMA && i % EVERY == 0) dma_block<C, KIND, S_DMA>(src, kt_dma, i / EVERY, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
@@ -506,7 +516,11 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
                                          static_cast<int64_t>(tj) * C::BN + wn * C::WN),
                              g.sp * 2, lane);
     };
-    main_loop<C, KIND>(acc, src, static_cast<int>(kdim / C::BK), wave, wm, wn, lane, pre_last);
+    const int nk = static_cast<int>(kdim / C::BK);
+    if (__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(ti) * C::BM + wm * C::WM >= g.s)))
+        main_loop<CfgIdle, KIND>(acc, src, nk, wave, wm, wn, lane, pre_last);
+    else
+        main_loop<C, KIND>(acc, src, nk, wave, wm, wn, lane, pre_last);
 
     // acc[mi][ni][4*c4 + q] holds output row wm*WM + mi*32 + lane%32, column
     // wn*WN + ni*32 + 8*c4 + 4*(lane/32) + q of the tile.
