@@ -69,6 +69,7 @@ struct Cfg {
     static constexpr int NM = MI * NI;                 // MFMAs per wave and 16-k substep
     static constexpr int NF = MI + NI;                 // fragments per wave and substep
     static constexpr bool MFMA = true;                 // the wave's products are issued
+    static constexpr bool DIAG = false;                // products selected by Src::mmask
 };
 
 // The K loop of a GRAM or POLY wave whose 128 output rows all lie in the zero
@@ -78,6 +79,19 @@ struct Cfg {
 // SIMD has the matrix core to itself.
 struct CfgIdle : Cfg {
     static constexpr bool MFMA = false;
+};
+
+// The K loop of a diagonal tile of GRAM or POLY: only the 32 x 32 blocks on
+// and below the diagonal (36 of 64) are needed, the rest is their mirror.  The
+// waves take their 128 x 64 blocks in a permuted order and issue only the
+// needed products (Src::mmask), so that the two waves sharing a SIMD (w and
+// w + 4) hold 8 + 0, 8 + 0, 7 + 3 and 7 + 3 products per substep instead of
+// 8 + 8.
+struct CfgDiag : Cfg {
+    static constexpr bool DIAG = true;
+    // wave w -> (wm, wn): (1,0) (1,1) (0,0) (1,2) (0,2) (0,3) (0,1) (1,3)
+    static constexpr uint32_t WM_OF = 0x8Bu;    // bit w
+    static constexpr uint32_t WN_OF = 0xDE84u;  // bits 2w, 2w+1
 };
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_tr;
@@ -161,6 +175,7 @@ struct Src {
     int64_t ld_p;
     const char *q;  // Q operand (output columns): K-contiguous rows, or X itself for APPLY
     int64_t ld_q;
+    uint32_t mmask;  // C::DIAG: bit i set = product i of each substep is needed (wave-uniform)
 };
 
 // DMA block j (0 <= j < LPS) of this wave for stage kt into slot S.  Blocks
@@ -254,7 +269,11 @@ __device__ __forceinline__ void substep(floatx16 (&acc)[C::MI][C::NI], const Fra
     static_assert(EVERY >= 1 && C::NM % C::LPS == 0, "one DMA block per product slot");
 #pragma unroll
     for (int i = 0; i < C::NM; ++i) {
-        if constexpr (C::MFMA) mma_one<C>(acc, f, i);
+        if constexpr (C::DIAG) {
+            if (src.mmask & (1u << i)) mma_one<C>(acc, f, i);
+        } else if constexpr (C::MFMA) {
+            mma_one<C>(acc, f, i);
+        }
         if (READ && i < C::NF) read_frag<C, KIND, S_READ>(g, i, ks_next, wm, wn, lane);
         if (ISSUE_DMA && i % EVERY == 0) dma_block<C, KIND, S_DMA>(src, kt_dma, i / EVERY, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
@@ -390,7 +409,10 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
     const int64_t row0 = static_cast<int64_t>(ti) * C::BM + wm * C::WM;
     const int64_t col0 = static_cast<int64_t>(tj) * C::BN + wn * C::WN;
     uint16_t *dst = static_cast<uint16_t *>(KIND == GRAM ? w.ab : w.bb) + e * w.a_stride;
-    const bool mirror = ti != tj;
+    // Off-diagonal tiles store every block and its mirror.  Diagonal tiles
+    // computed only the 32 x 32 blocks on and below the diagonal (block row >=
+    // block column): they store those and mirror the ones strictly below it.
+    const bool diag = ti == tj;
     // first step on the bf16 path: X holds N, so A = inv^2 (N N^T) and the
     // product B X is taken with B inv (X' = a inv N + (B inv) N)
     const float inv = p.unnormalized ? w.inv_norm[e] : 1.0f;
@@ -403,13 +425,20 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
     for (int h = 0; h < ROUNDS; ++h) {
         char *reg = area[h & 1];
         if constexpr (KIND == POLY) {
+            // a diagonal tile's round may issue no stores: there only round
+            // h+1's DMA may stay in flight
             if (h == 0)
+                fenced_wait_vmcnt<DMA_PER_ROUND>();
+            else if (h + 1 < ROUNDS && diag)
                 fenced_wait_vmcnt<DMA_PER_ROUND>();
             else if (h + 1 < ROUNDS)
                 fenced_wait_vmcnt<ROW_STORES + DMA_PER_ROUND>();
+            else if (diag)
+                fenced_wait_vmcnt<0>();
             else
                 fenced_wait_vmcnt<ROW_STORES>();
         }
+        const int brow = wm * C::MI + h;  // block row of this round (32-row blocks of the tile)
         floatx4 v[C::NI][4];
 #pragma unroll
         for (int ni = 0; ni < C::NI; ++ni)
@@ -446,13 +475,14 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
             u32x2 pk;
             pk[0] = pack_bf16x2(x[0], x[1]);
             pk[1] = pack_bf16x2(x[2], x[3]);
-            *reinterpret_cast<u32x2 *>(dst + idx) = pk;
+            if (!diag || brow >= wn * C::NI + (chunk >> 3)) *reinterpret_cast<u32x2 *>(dst + idx) = pk;
         }
-        if (mirror) {
+        {
             // column c of the block -> row col0 + c of the mirrored tile; lane
             // (c, part) moves rows 8*part .. 8*part+7 of the round
 #pragma unroll
             for (int t = 0; t < C::WN / 16; ++t) {
+                if (diag && brow <= wn * C::NI + t / 2) continue;  // columns 16t.. lie in block wn*NI + t/2
                 const int c = 16 * t + (lane >> 2), part = lane & 3;
                 float f[8];
 #pragma unroll
@@ -478,15 +508,25 @@ template <class C, int KIND>
 __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep p,
                                                                           int64_t tiles_per_mat, int64_t nblocks) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int64_t L = xcd_swizzle(blockIdx.x, nblocks);
     const int64_t e = L / tiles_per_mat;
     int ti, tj;
     tri_decode(L % tiles_per_mat, &ti, &tj);
+    const bool diag = ti == tj;
+    const int wm = diag ? static_cast<int>((CfgDiag::WM_OF >> wave) & 1) : wave / C::WAVES_N;
+    const int wn = diag ? static_cast<int>((CfgDiag::WN_OF >> (2 * wave)) & 3) : wave % C::WAVES_N;
 
     // P supplies output rows (tile ti), Q output columns (tile tj); both are
     // rows of X (GRAM) or of the symmetric A (POLY), K-contiguous.
     Src src;
+    {
+        // product i = (mi, ni) covers block row wm*MI + mi, block column wn*NI + ni
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < C::NM; ++i)
+            if (wm * C::MI + i / C::NI >= wn * C::NI + i % C::NI) m |= 1u << i;
+        src.mmask = __builtin_amdgcn_readfirstlane(m);
+    }
     int64_t kdim;
     if (KIND == GRAM) {
         const char *x = static_cast<const char *>(w.xb) + e * w.x_stride * 2;
@@ -517,7 +557,9 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
                              g.sp * 2, lane);
     };
     const int nk = static_cast<int>(kdim / C::BK);
-    if (__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(ti) * C::BM + wm * C::WM >= g.s)))
+    if (diag)
+        main_loop<CfgDiag, KIND>(acc, src, nk, wave, wm, wn, lane, pre_last);
+    else if (__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(ti) * C::BM + wm * C::WM >= g.s)))
         main_loop<CfgIdle, KIND>(acc, src, nk, wave, wm, wn, lane, pre_last);
     else
         main_loop<C, KIND>(acc, src, nk, wave, wm, wn, lane, pre_last);
