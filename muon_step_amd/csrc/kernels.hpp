@@ -51,6 +51,9 @@ struct NsStep {
     // bf16 path, first step: the workspace X holds N itself; the Gram is
     // scaled by inv_norm^2 and a X + B X by inv_norm (X_0 = N inv_norm).
     int unnormalized;
+    // bf16 path, last step: W rows may be staged through LDS (no transpose,
+    // s and l multiples of 256, every parameter 16-byte aligned).
+    int w_staged;
 };
 
 // kind: 0 = A = X X^T, 1 = B = bA + cA^2, 2 = X <- aX + BX (or the fused update).

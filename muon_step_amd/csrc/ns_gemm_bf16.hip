@@ -100,6 +100,8 @@ typedef __attribute__((address_space(3))) bf16x4_tr lds_bf16x4_t;
 // The operand ring: slot S holds the P slab, then the Q slab.  After the main
 // loop the epilogues reuse it as staging areas.
 __shared__ __attribute__((aligned(1024))) char lds_ring[Cfg::STAGES * Cfg::SLOT_BYTES];
+// The fused update's W rows, two halves of a round per wave (bf16 parameters).
+__shared__ __attribute__((aligned(1024))) char lds_wbuf[Cfg::NWAVES * 4096];
 
 template <int S> __device__ __forceinline__ char *slot_p() { return lds_ring + S * Cfg::SLOT_BYTES; }
 template <int S> __device__ __forceinline__ char *slot_q() { return lds_ring + S * Cfg::SLOT_BYTES + Cfg::P_BYTES; }
@@ -821,9 +823,90 @@ __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Cfg:
     }
 }
 
+// DMA of 16 rows x 64 bf16 of W (row pitch ld bytes) into 2 KB of LDS, plain
+// rows of 128 bytes: lane i of instruction t carries row 8t + i/8, chunk i%8.
+__device__ __forceinline__ void dma_w_half(char *dst, const char *src, int64_t ld, int lane) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) dma16(src + (8 * t + (lane >> 3)) * ld + (lane & 7) * 16, dst + t * 1024);
+}
+
+// The fused update for a bf16 W in the orientation of X', on a wave block that
+// lies wholly inside W with 16-byte aligned rows (every block, by the launch
+// condition).  W is read once, straight
+// from HBM, so its rows are brought by DMA into the wave's 4 KB of lds_wbuf a
+// half round ahead (16 rows each): W(0) on entry, W(h+1)'s first half once
+// round h's first half has used its buffer, its second half likewise.  The
+// X rows come through the staging areas as in the other epilogues (round 0
+// requested under the last K stage).  Per round the vector-memory stream is
+// X(h+1) [6], the first half's stores [4, or 8 with O'], W(h+1) first half
+// [2], the second half's stores, W(h+1) second half [2]; since they retire in
+// issue order the waits below allow exactly the instructions issued after the
+// one awaited (more when O' is stored, which only waits longer).
+__device__ __forceinline__ void apply_epilogue_update_staged(const floatx16 (&acc)[Cfg::MI][Cfg::NI],
+                                                             const MatDesc &d, const Geom &g, const Work &w,
+                                                             const NsStep &p, const ApplyTile &t,
+                                                             char *const (&area)[2], char *wb, int lane) {
+    using C = Cfg;
+    constexpr int ROUNDS = C::WM / C::EPI_ROWS;
+    static_assert(ROUNDS == 4 && C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
+    const XRows x = x_rows(g, w, t);
+    const float a = p.unnormalized ? p.a * w.inv_norm[t.e] : p.a;
+    uint16_t *const wrow0 = static_cast<uint16_t *>(d.param) + t.row0 * g.cols + t.col0;
+    const char *const wsrc = reinterpret_cast<const char *>(wrow0);
+    const int64_t wld = g.cols * 2;
+    dma_w_half(wb, wsrc, wld, lane);
+    dma_w_half(wb + 2048, wsrc + 16 * wld, wld, lane);
+    const int rr = lane >> 4, chunk = lane & 15;
+#pragma unroll
+    for (int h = 0; h < ROUNDS; ++h) {
+        char *reg = area[h & 1];
+        if (h == 0)
+            fenced_wait_vmcnt<2>();  // X(0), W(0) first half
+        else
+            fenced_wait_vmcnt<6>();  // X(h), W(h) first half
+        if (h + 1 < ROUNDS) {
+            dma_x_round(area[(h + 1) & 1], x, h + 1, lane);  // its area was last read in round h-1
+            asm volatile("" ::: "memory");
+        }
+        stage_values<C>(acc[h], reg, a, lane);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            if (half == 1) {
+                if (h + 1 < ROUNDS)
+                    fenced_wait_vmcnt<12>();  // W(h) second half
+                else
+                    fenced_wait_vmcnt<4>();
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int rrow = 16 * half + 4 * k + rr;
+                const floatx4 xv = *reinterpret_cast<const floatx4 *>(reg + epi_offset(rrow, chunk));
+                const u32x2 w2 = *reinterpret_cast<const u32x2 *>(wb + half * 2048 + (rrow - 16 * half) * 128 + chunk * 8);
+                u32x2 o;
+                o[0] = pack_bf16x2(p.dscale * __uint_as_float(w2[0] << 16) - p.sscale * xv[0],
+                                   p.dscale * __uint_as_float(w2[0] & 0xffff0000u) - p.sscale * xv[1]);
+                o[1] = pack_bf16x2(p.dscale * __uint_as_float(w2[1] << 16) - p.sscale * xv[2],
+                                   p.dscale * __uint_as_float(w2[1] & 0xffff0000u) - p.sscale * xv[3]);
+                const int64_t widx = (C::EPI_ROWS * h + rrow) * g.cols + 4 * chunk;
+                *as_global(reinterpret_cast<u32x2 *>(wrow0 + widx)) = o;
+                if (d.ns_out)
+                    *as_global(reinterpret_cast<floatx4 *>(d.ns_out + (t.row0 * g.cols + t.col0) + widx)) = xv;
+            }
+            wait_lgkm0();  // this half's LDS reads are done before its buffer is refilled
+            asm volatile("" ::: "memory");
+            if (h + 1 < ROUNDS) {
+                dma_w_half(wb + half * 2048, wsrc + (C::EPI_ROWS * (h + 1) + 16 * half) * wld, wld, lane);
+                asm volatile("" ::: "memory");
+            }
+        }
+    }
+}
+
 // MODE 0: intermediate step (X' to the workspace); 1 / 2: last step with the
-// fused update of an fp32 / bf16 parameter.  One epilogue per instantiation
-// keeps each within the register file.
+// fused update of an fp32 / bf16 parameter; 3: the same for a bf16 parameter
+// through apply_epilogue_update_staged (NsStep::w_staged: no transpose, s and
+// l multiples of 256, 16-byte aligned parameters).  One epilogue per
+// instantiation keeps each within the register file.
 template <int MODE>
 __global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__restrict__ descs, Geom g, Work w,
                                                                NsStep p, int64_t tiles_per_mat, int64_t nblocks) {
@@ -869,6 +952,8 @@ __global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__r
     stage_barrier();  // every wave is done with the operand ring
     if constexpr (MODE == 0)
         apply_epilogue_next(acc, g, w, p, t_, area, lane);
+    else if constexpr (MODE == 3)
+        apply_epilogue_update_staged(acc, descs[e], g, w, p, t_, area, lds_wbuf + wave * 4096, lane);
     else
         apply_epilogue_update<MODE == 2>(acc, descs[e], g, w, p, t_, area, lane);
 }
@@ -895,6 +980,8 @@ hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const 
     const dim3 grid(static_cast<unsigned>(nblocks)), block(Cfg::NT);
     if (!p.final_update)
         ns_apply_kernel<0><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
+    else if (p.param_bf16 && p.w_staged)
+        ns_apply_kernel<3><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
     else if (p.param_bf16)
         ns_apply_kernel<2><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
     else

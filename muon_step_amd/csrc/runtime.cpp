@@ -542,7 +542,7 @@ void ns_work(int stage, const Geom &g, bool bf16, int n, bool ns_out, int psize,
 // meaningful when !update.
 muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom &g, Work &w, bool bf16,
                    const muon_hparams *hp, bool update, int param_bf16, bool any_ns_out, float d, float s,
-                   hipStream_t st) {
+                   hipStream_t st, bool params_aligned16 = false) {
     const double xe = static_cast<double>(g.s) * g.l * nmat;
     // bf16 path with a schedule: X stays N and the first step applies 1/||N||
     // (only the padding needs zeros); otherwise a normalisation pass.
@@ -566,6 +566,7 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
         p.dscale = d;
         p.sscale = s;
         p.unnormalized = (fold && it == 0) ? 1 : 0;
+        p.w_staged = (param_bf16 && params_aligned16 && !g.transposed && g.s % muon::kTile == 0 && g.l % muon::kTile == 0) ? 1 : 0;
         for (int kind = 0; kind < 3; ++kind) {
             const int stage = kind == 0 ? ST_GRAM : kind == 1 ? ST_POLY : (p.final_update ? ST_APPLY_UPDATE : ST_APPLY);
             double fl = 0, by = 0;
@@ -735,10 +736,11 @@ muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count,
         for (int64_t c0 = 0; c0 < n_all; c0 += gp.chunk) {
             const int n = static_cast<int>(std::min<int64_t>(gp.chunk, n_all - c0));
             const MatDesc *dd = ddev + pos + c0;
-            bool vec_ok = true;
+            bool vec_ok = true, params_aligned = true;
             for (int k = 0; k < n; ++k) {
                 const muon_matrix &m = mats[gp.members[c0 + k]];
                 vec_ok = vec_ok && aligned16(m.momentum) && aligned16(m.grad);
+                params_aligned = params_aligned && aligned16(m.param);
             }
             bool any_out = false;
             for (int k = 0; k < n; ++k) any_out = any_out || mats[gp.members[c0 + k]].ns_out != nullptr;
@@ -754,7 +756,8 @@ muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count,
             e = timed(ctx, ST_FINALIZE, 0.0, static_cast<double>(n) * gp.bpm * 8.0, st,
                       [&] { return muon::launch_norm_finalize(dd, n, w, gp.bpm, st); });
             if (e != hipSuccess) return hip_fail(ctx, e, "norm launch");
-            s = run_ns(ctx, dd, n, gp.g, w, bf16, hp, true, gp.param_dtype == MUON_BF16, any_out, d, sc, st);
+            s = run_ns(ctx, dd, n, gp.g, w, bf16, hp, true, gp.param_dtype == MUON_BF16, any_out, d, sc, st,
+                       params_aligned);
             if (s != MUON_OK) return s;
         }
         pos += static_cast<size_t>(n_all);

@@ -149,11 +149,13 @@ def _run_step(ctx, torch_mod, specs, precision, seed, lr=0.02, wd=0.1, gamma=0.2
 @pytest.mark.parametrize("precision", ["bf16", "f32"])
 def test_step_mixed_group(ctx, torch_mod, precision):
     """Several shapes and dtype combinations in one call: grouped launches, ragged tiles,
-    transposed matrices, bf16/fp32 params and grads."""
+    transposed matrices, bf16/fp32 params and grads (256 x 512 bf16: the fused update
+    that stages W through LDS)."""
     S = synth.MatrixSpec
     specs = [S(96, 300, "bf16", "bf16"), S(96, 300, "bf16", "bf16"), S(300, 96, "bf16", "bf16"),
              S(260, 260, "f32", "f32", law="gauss"), S(64, 128, "f32", "bf16"), S(128, 64, "bf16", "f32"),
-             S(96, 300, "bf16", "bf16", prefill_momentum=True), S(5, 3, "f32", "f32", law="gauss")]
+             S(96, 300, "bf16", "bf16", prefill_momentum=True), S(5, 3, "f32", "f32", law="gauss"),
+             S(256, 512, "bf16", "bf16"), S(256, 512, "bf16", "bf16"), S(512, 256, "bf16", "bf16")]
     say(f"step mixed group {precision}")
     _run_step(ctx, torch_mod, specs, precision, seed=21)
 
