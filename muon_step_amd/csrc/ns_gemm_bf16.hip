@@ -6,11 +6,12 @@
 // launch each:
 //
 //   GRAM  : A = X X^T         s x s, K = l.  Only lower-triangle tiles are
-//                             computed (A is symmetric); each is written to
-//                             A (fp32) and, mirrored, to the bf16 operand copy.
-//   POLY  : B = b A + c A A   s x s, K = s.  A A is symmetric too: lower tiles
-//                             only, written mirrored.  Row i of A serves as
-//                             column i, so both operands are K-contiguous.
+//                             computed (A is symmetric), and of a diagonal
+//                             tile only the blocks on and below its diagonal;
+//                             A is written in bf16, with the mirror.
+//   POLY  : B = b A + c A A   s x s, K = s.  A A is symmetric too: the same
+//                             triangle, written mirrored.  Row i of A serves
+//                             as column i, so both operands are K-contiguous.
 //   APPLY : X' = a X + B X    s x l, K = s.  The aX term is added in fp32 from
 //                             X = X_hi + X_lo.  The last step instead
 //                             writes W <- d W - s_scale X' (and O'_t).
@@ -32,8 +33,10 @@
 // columns of one output row; every epilogue stages its block through LDS in
 // rounds of 32 rows and stores whole rows (GRAM/POLY also store the block's
 // columns as rows of the mirrored tile; APPLY moves 6 bytes per output
-// element: X_hi and its 8-bit residual X_lo in and out).  Block ids are
-// renumbered so one matrix's tiles share an XCD (and its L2).
+// element: X_hi and its 8-bit residual X_lo in and out; the fused update of
+// a bf16 W brings W's rows by DMA too).  K loops stop at the true length
+// rounded to 128 (the padding is zero).  Block ids are renumbered so one
+// matrix's tiles share an XCD (and its L2).
 #include "common.hpp"
 #include "kernels.hpp"
 
