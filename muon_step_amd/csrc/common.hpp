@@ -192,12 +192,21 @@ __device__ __forceinline__ void split_bf16x4(const floatx4 &v, u32x2 *hi, uint32
     const uint32_t p23 = __builtin_amdgcn_perm(static_cast<uint32_t>(q[3]), static_cast<uint32_t>(q[2]), 0x0c0c0400u);
     *lo = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
 }
+// BOUNDED: the values were written by split_bf16x4<true> (|x| < 2^120 or a
+// non-finite hi), so the exponent cap is not needed either.
+template <bool BOUNDED = false>
 __device__ __forceinline__ floatx4 join_bf16x4(const u32x2 &h, uint32_t l) {
     floatx4 v;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         uint32_t m0, m1;
-        lo8_ref2(h[k], &m0, &m1);
+        if (BOUNDED) {
+            const uint32_t eb = h[k] & 0x7f807f80u;
+            m0 = (eb << 16) + LO8_REF_ADD;
+            m1 = eb + LO8_REF_ADD;
+        } else {
+            lo8_ref2(h[k], &m0, &m1);
+        }
         const int q0 = static_cast<int8_t>((l >> (16 * k)) & 0xffu);
         const int q1 = static_cast<int8_t>((l >> (16 * k + 8)) & 0xffu);
         v[2 * k] = __uint_as_float(h[k] << 16) + lo8_value(q0, m0);

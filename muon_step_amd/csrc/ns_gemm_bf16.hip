@@ -627,11 +627,12 @@ __device__ __forceinline__ void dma_x_round(char *dst, const XRows &x, int h, in
 // staged in `reg` (X_hi rows, 128 bytes each, in the first PAIR_HALF bytes;
 // X_lo rows, 64 bytes each, after).  While X still holds N, `a` is a inv_norm
 // (and B was scaled by inv_norm when it was formed).
+template <bool BOUNDED = false>
 __device__ __forceinline__ floatx4 apply_value(const floatx16 &acc, const char *reg, int lrow, int lcol, int c4,
                                                float a) {
     const u32x2 h = *reinterpret_cast<const u32x2 *>(reg + pair_offset(lrow, lcol));
     const uint32_t l = *reinterpret_cast<const uint32_t *>(reg + PAIR_HALF + lo8_offset(lrow, lcol));
-    const floatx4 x = join_bf16x4(h, l);
+    const floatx4 x = join_bf16x4<BOUNDED>(h, l);
     floatx4 v;
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(a, x[q], acc[4 * c4 + q]);
@@ -643,7 +644,7 @@ __device__ __forceinline__ floatx4 apply_value(const floatx16 &acc, const char *
 // for the row-contiguous pass.  All of the lane's reads precede its writes, and
 // one wave's LDS accesses execute in order, so no value is overwritten before
 // it is read.
-template <class C>
+template <class C, bool BOUNDED = false>
 __device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char *reg, float a, int lane) {
     const int lrow = lane & 31;
     floatx4 v[C::NI][4];
@@ -651,7 +652,7 @@ __device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char
     for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
-            v[ni][c4] = apply_value(accm[ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, a);
+            v[ni][c4] = apply_value<BOUNDED>(accm[ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, a);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int ni = 0; ni < C::NI; ++ni)
@@ -680,6 +681,7 @@ __device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char
 // every vector-memory instruction retires in issue order, so the wait before
 // round h allows exactly the instructions issued after round h's DMA: round
 // h-1's stores and round h+1's DMA.
+template <bool BOUNDED>
 __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::MI][Cfg::NI], const Geom &g,
                                                     const Work &w, const NsStep &p, const ApplyTile &t,
                                                     char *const (&area)[2], int lane) {
@@ -709,7 +711,7 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::M
         else
             fenced_wait_vmcnt<STORES_PER_ROUND>();
         char *reg = area[h & 1];
-        stage_values<C>(acc[h], reg, a, lane);
+        stage_values<C, BOUNDED>(acc[h], reg, a, lane);
 #pragma unroll
         for (int r4 = 0; r4 < C::EPI_ROWS / 4; ++r4) {
             const floatx4 v = *reinterpret_cast<const floatx4 *>(reg + epi_offset(4 * r4 + rr, chunk));
@@ -905,7 +907,9 @@ __device__ __forceinline__ void apply_epilogue_update_staged(const floatx16 (&ac
     }
 }
 
-// MODE 0: intermediate step (X' to the workspace); 1 / 2: last step with the
+// MODE 0: intermediate step (X' to the workspace); 4: the same after the first
+// step, where X is a Newton-Schulz iterate (|X| <= ~1.2), so its residual
+// decodes without the exponent cap; 1 / 2: last step with the
 // fused update of an fp32 / bf16 parameter; 3: the same for a bf16 parameter
 // through apply_epilogue_update_staged (NsStep::w_staged: no transpose, s and
 // l multiples of 256, 16-byte aligned parameters).  One epilogue per
@@ -953,8 +957,8 @@ __global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__r
     char *const area[2] = {epi_area<0>(wave), epi_area<1>(wave)};
     wait_lgkm0();
     stage_barrier();  // every wave is done with the operand ring
-    if constexpr (MODE == 0)
-        apply_epilogue_next(acc, g, w, p, t_, area, lane);
+    if constexpr (MODE == 0 || MODE == 4)
+        apply_epilogue_next<MODE == 4>(acc, g, w, p, t_, area, lane);
     else if constexpr (MODE == 3)
         apply_epilogue_update_staged(acc, descs[e], g, w, p, t_, area, lds_wbuf + wave * 4096, lane);
     else
@@ -981,7 +985,9 @@ hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const 
     const int64_t tiles = (g.sp / Cfg::BM) * (g.lp / Cfg::BN);
     const int64_t nblocks = tiles * nmat;
     const dim3 grid(static_cast<unsigned>(nblocks)), block(Cfg::NT);
-    if (!p.final_update)
+    if (!p.final_update && !p.unnormalized)
+        ns_apply_kernel<4><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
+    else if (!p.final_update)
         ns_apply_kernel<0><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
     else if (p.param_bf16 && p.w_staged)
         ns_apply_kernel<3><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
