@@ -837,7 +837,7 @@ __device__ __forceinline__ void dma_w_half(char *dst, const char *src, int64_t l
 
 // The fused update for a bf16 W in the orientation of X', on a wave block that
 // lies wholly inside W with 16-byte aligned rows (every block, by the launch
-// condition).  W is read once, straight
+// condition), after the first step (X is a bounded iterate).  W is read once, straight
 // from HBM, so its rows are brought by DMA into the wave's 4 KB of lds_wbuf a
 // half round ahead (16 rows each): W(0) on entry, W(h+1)'s first half once
 // round h's first half has used its buffer, its second half likewise.  The
@@ -873,7 +873,7 @@ __device__ __forceinline__ void apply_epilogue_update_staged(const floatx16 (&ac
             dma_x_round(area[(h + 1) & 1], x, h + 1, lane);  // its area was last read in round h-1
             asm volatile("" ::: "memory");
         }
-        stage_values<C>(acc[h], reg, a, lane);
+        stage_values<C, true>(acc[h], reg, a, lane);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             if (half == 1) {
@@ -911,8 +911,8 @@ __device__ __forceinline__ void apply_epilogue_update_staged(const floatx16 (&ac
 // step, where X is a Newton-Schulz iterate (|X| <= ~1.2), so its residual
 // decodes without the exponent cap; 1 / 2: last step with the
 // fused update of an fp32 / bf16 parameter; 3: the same for a bf16 parameter
-// through apply_epilogue_update_staged (NsStep::w_staged: no transpose, s and
-// l multiples of 256, 16-byte aligned parameters).  One epilogue per
+// through apply_epilogue_update_staged after the first step (NsStep::w_staged:
+// no transpose, s and l multiples of 256, 16-byte aligned parameters).  One epilogue per
 // instantiation keeps each within the register file.
 template <int MODE>
 __global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__restrict__ descs, Geom g, Work w,
@@ -989,7 +989,7 @@ hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const 
         ns_apply_kernel<4><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
     else if (!p.final_update)
         ns_apply_kernel<0><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
-    else if (p.param_bf16 && p.w_staged)
+    else if (p.param_bf16 && p.w_staged && !p.unnormalized)
         ns_apply_kernel<3><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
     else if (p.param_bf16)
         ns_apply_kernel<2><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
