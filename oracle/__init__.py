@@ -34,6 +34,8 @@ from .muon import (  # noqa: F401
     newton_schulz,
     orthogonalized_update,
     muon_scalars_f32,
+    unit_rms_factor,
+    update_scale,
     apply_update_f32,
     muon_step,
     ns_flops_algorithmic,

@@ -97,29 +97,63 @@ def orthogonalized_update(n_mat, gamma, schedule=DEEPSEEK_V4_SCHEDULE):
     return newton_schulz(n_mat, schedule) * (math.sqrt(max(rows, cols)) * gamma)
 
 
-def muon_scalars_f32(lr, weight_decay, gamma, rows, cols):
+def unit_rms_factor(x, gamma):
+    """Scale of the unit-RMS mode: O = X * gamma / RMS(X), RMS(X) = ||X||_F / sqrt(n m).
+
+    The deep-dive page's Megatron-Bridge recipe (muon_scale_mode
+    "unit_rms_norm" with muon_extra_scale_factor 0.2, and the remark below it
+    that contrasts it with V4's sqrt(max) rule) divides the update by its own
+    RMS and multiplies by the extra factor; gamma plays that factor here.
+    X = 0 has no RMS to divide by: the factor is 0 (a decay-only update, as
+    for ||N|| = 0).  Computed in float64 from the values given.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    ss = float(np.sum(x * x))
+    if ss == 0.0:
+        return 0.0
+    return gamma * math.sqrt(float(rows) * float(cols)) / math.sqrt(ss)
+
+
+def update_scale(x, gamma, scale_mode="sqrt_max"):
+    """The factor O_t / O'_t: sqrt(max(n, m)) * gamma (V4, Algorithm 1) or the
+    unit-RMS factor of `unit_rms_factor`."""
+    rows, cols = np.shape(x)
+    if scale_mode == "sqrt_max":
+        return math.sqrt(max(rows, cols)) * gamma
+    if scale_mode == "unit_rms":
+        return unit_rms_factor(x, gamma)
+    raise ValueError(f"unknown scale mode {scale_mode!r}")
+
+
+def muon_scalars_f32(lr, weight_decay, gamma, rows, cols, x32=None, scale_mode="sqrt_max"):
     """Host scalars of the decay + update: (d, s) as float32.
 
-    d = 1 - lr*wd and s = lr * gamma * sqrt(max(rows, cols)), each computed in
-    float64 and rounded once to float32.
+    d = 1 - lr*wd and s = lr * gamma * sqrt(max(rows, cols)) (unit-RMS mode:
+    s = lr * unit_rms_factor(x32, gamma), which needs the float32 X), each
+    computed in float64 and rounded once to float32.
     """
     d = np.float32(1.0 - lr * weight_decay)
-    s = np.float32(lr * gamma * math.sqrt(float(max(rows, cols))))
+    if scale_mode == "unit_rms":
+        s = np.float32(lr * unit_rms_factor(x32, gamma))
+    else:
+        s = np.float32(lr * gamma * math.sqrt(float(max(rows, cols))))
     return d, s
 
 
-def apply_update_f32(w, x32, lr, weight_decay, gamma, param_bf16):
-    """W_t = (1 - lr*wd) W_{t-1} - lr * gamma * sqrt(max) * X, float32 ops.
+def apply_update_f32(w, x32, lr, weight_decay, gamma, param_bf16, scale_mode="sqrt_max"):
+    """W_t = (1 - lr*wd) W_{t-1} - lr * scale * X, float32 ops.
 
     w: parameter values as float32 (bfloat16 values widened exactly when
     param_bf16).  x32: the float32 orthogonalised update O'_t (unscaled).
+    scale = sqrt(max) * gamma, or gamma / RMS(x32) in the unit-RMS mode.
     Computes fl(fl(d*w) - fl(s*x)); rounds the result to bfloat16 (RNE) when
     the parameter is bfloat16.
     """
     w = np.asarray(w, dtype=np.float32)
     x32 = np.asarray(x32, dtype=np.float32)
     rows, cols = w.shape
-    d, s = muon_scalars_f32(lr, weight_decay, gamma, rows, cols)
+    d, s = muon_scalars_f32(lr, weight_decay, gamma, rows, cols, x32, scale_mode)
     out = (d * w) - (s * x32)
     out = out.astype(np.float32)
     if param_bf16:
@@ -128,22 +162,24 @@ def apply_update_f32(w, x32, lr, weight_decay, gamma, param_bf16):
 
 
 def muon_step(w, g, m, lr=0.02, momentum=0.95, weight_decay=0.1, gamma=0.2,
-              nesterov=True, schedule=DEEPSEEK_V4_SCHEDULE, param_bf16=False):
+              nesterov=True, schedule=DEEPSEEK_V4_SCHEDULE, param_bf16=False, scale_mode="sqrt_max"):
     """One full Muon step on one matrix.
 
     Returns a dict with
       m_new : float32 M_t (bit-exact target)
       n     : float32 N_t (the NS input)
       x     : float64 O'_t (NS output, unscaled)
-      o     : float64 O_t = O'_t * sqrt(max) * gamma (the parity object)
+      o     : float64 O_t = O'_t * scale (the parity object); scale is
+              sqrt(max) * gamma, or gamma / RMS(O'_t) when scale_mode is
+              "unit_rms"
       w_new : float32 W_t computed from fl32(O'_t) (bfloat16-rounded if the
               parameter is bfloat16)
     """
     m_new, n = nesterov_momentum_f32(m, g, momentum, nesterov)
     x = newton_schulz(n, schedule)
     rows, cols = np.shape(w)
-    o = x * (math.sqrt(max(rows, cols)) * gamma)
-    w_new = apply_update_f32(w, x.astype(np.float32), lr, weight_decay, gamma, param_bf16)
+    o = x * update_scale(x, gamma, scale_mode)
+    w_new = apply_update_f32(w, x.astype(np.float32), lr, weight_decay, gamma, param_bf16, scale_mode)
     return {"m_new": m_new, "n": n, "x": x, "o": o, "w_new": w_new}
 
 

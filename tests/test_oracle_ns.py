@@ -247,6 +247,64 @@ def test_frobenius_norm_is_sqrt_min_and_rms_is_gamma():
         assert abs(rms / 0.2 - 1.0) < 2.2e-3
 
 
+def test_unit_rms_mode_rms_is_gamma_for_any_x():
+    """Unit-RMS mode (the deep-dive page's Megatron-Bridge recipe): O = X * gamma / RMS(X)
+    has RMS exactly gamma whatever X is, orthogonal or not; RMS here is the plain mean of
+    squares over all n*m entries."""
+    for rows, cols in [(3, 7), (7, 3), (16, 16), (40, 9)]:
+        x = _rng(rows + 31 * cols).standard_normal((rows, cols)) * 3.7
+        o = x * oracle.update_scale(x, 0.2, "unit_rms")
+        rms = math.sqrt(sum(float(v) ** 2 for v in o.ravel()) / (rows * cols))
+        assert abs(rms - 0.2) < 1e-13
+
+
+def test_unit_rms_mode_equals_sqrt_max_on_orthogonal_x():
+    """For X with orthonormal columns (or rows), ||X||_F = sqrt(min(n, m)), so the unit-RMS
+    factor gamma * sqrt(n m) / ||X|| is exactly gamma * sqrt(max(n, m)): the two scale modes
+    agree on an exact polar factor (the deep-dive page's remark that they are equivalent in
+    theory)."""
+    for rows, cols in [(12, 5), (5, 12), (9, 9)]:
+        q, _ = np.linalg.qr(_rng(rows * cols).standard_normal((max(rows, cols), min(rows, cols))))
+        x = q if rows >= cols else q.T
+        assert x.shape == (rows, cols)
+        got = oracle.update_scale(x, 0.18, "unit_rms")
+        assert abs(got / (0.18 * math.sqrt(max(rows, cols))) - 1.0) < 1e-13
+
+
+def test_unit_rms_mode_zero_and_worked_scalars():
+    """X = 0 gives a zero factor (decay-only update); a 2 x 2 case by hand:
+    X = diag(3, 4) has ||X|| = 5 and RMS 5/2, so with gamma = 0.25 the factor is 0.1,
+    and with lr = 0.5 the update scalar s is fl32(0.05)."""
+    assert oracle.update_scale(np.zeros((4, 6)), 0.2, "unit_rms") == 0.0
+    x = np.array([[3.0, 0.0], [0.0, 4.0]], dtype=np.float32)
+    assert abs(oracle.update_scale(x, 0.25, "unit_rms") - 0.1) < 1e-15
+    d, s = oracle.muon_scalars_f32(0.5, 0.2, 0.25, 2, 2, x, "unit_rms")
+    assert d == np.float32(0.9) and s == np.float32(0.05)
+    w = np.array([[1.0, 2.0], [-1.0, 0.5]], dtype=np.float32)
+    got = oracle.apply_update_f32(w, x, 0.5, 0.2, 0.25, False, "unit_rms")
+    want = np.array([[np.float32(0.9) * np.float32(1.0) - np.float32(0.05) * np.float32(3.0),
+                      np.float32(0.9) * np.float32(2.0)],
+                     [np.float32(0.9) * np.float32(-1.0),
+                      np.float32(0.9) * np.float32(0.5) - np.float32(0.05) * np.float32(4.0)]], dtype=np.float32)
+    assert np.array_equal(got, want)
+    with pytest.raises(ValueError):
+        oracle.update_scale(x, 0.2, "bogus")
+
+
+def test_unit_rms_mode_close_to_sqrt_max_after_ns():
+    """After the hybrid schedule the singular values sit within the pages' band around 1, so
+    the two modes' O differ by the factor sqrt(min)/||O'|| within 2.2e-3."""
+    for rows, cols in [(64, 128), (128, 64)]:
+        rng = _rng(7 * rows + cols)
+        w, g, m = (rng.standard_normal((rows, cols)).astype(np.float32) for _ in range(3))
+        a = oracle.muon_step(w, g, m)
+        b = oracle.muon_step(w, g, m, scale_mode="unit_rms")
+        assert np.array_equal(a["x"], b["x"])
+        ratio = np.linalg.norm(b["o"]) / np.linalg.norm(a["o"])
+        assert abs(ratio - math.sqrt(min(rows, cols)) / np.linalg.norm(a["x"])) < 1e-12
+        assert abs(ratio - 1.0) < 2.2e-3
+
+
 # --------------------------------------------------------------- the independent polar route
 
 
