@@ -191,7 +191,7 @@ def moe16b_step(args):
         "stage_ms_per_step": breakdown}), flush=True)
 
 
-def cpu_baseline(rows, cols, count):
+def cpu_baseline(rows, cols, count, scale_mode="sqrt_max"):
     """The oracle as it stands on one matrix of the batch; scaled to one step."""
     import numpy as np
 
@@ -205,7 +205,7 @@ def cpu_baseline(rows, cols, count):
     wl = synth.Workload("moe_256x2048x7168_bf16", 4, (synth.MatrixSpec(rows, cols),))
     inp = synth.matrix_inputs(wl, 0)
     t0 = time.perf_counter()
-    oracle.muon_step(inp["w"], inp["g"], inp["m"], param_bf16=True)
+    oracle.muon_step(inp["w"], inp["g"], inp["m"], param_bf16=True, scale_mode=scale_mode)
     dt = time.perf_counter() - t0
     return {"value": 1.0 / (dt * count), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
             "sample": f"1 of {count} matrices ({rows}x{cols}), full oracle step (fp32 bookkeeping, fp64 "
@@ -225,6 +225,8 @@ def main():
                     choices=["moe_256x2048x7168_bf16", "moe16b"],
                     help="moe16b: time the full 16B-MoE optimizer step instead (own JSON line)")
     ap.add_argument("--workspace-gib", type=int, default=64, help="NS workspace cap for --workload moe16b")
+    ap.add_argument("--scale-mode", default="sqrt_max", choices=["sqrt_max", "unit_rms"],
+                    help="update scale: sqrt(max(n,m))*gamma (DeepSeek-V4) or the unit-RMS mode")
     ap.add_argument("--library-baseline", action="store_true",
                     help="only time torch bf16 batched products of the same shapes (64 matrices)")
     args = ap.parse_args()
@@ -260,7 +262,8 @@ def main():
     torch.cuda.synchronize()
     mats = [ms.matrix(params[e], grads[e], moms[e]) for e in range(count)]
     hp = ms.make_hparams(lr=0.02, momentum=0.95, weight_decay=0.1, gamma=0.2, nesterov=True,
-                         ns_precision=ms.MUON_NS_BF16)
+                         ns_precision=ms.MUON_NS_BF16,
+                         scale_mode=ms.MUON_SCALE_UNIT_RMS if args.scale_mode == "unit_rms" else ms.MUON_SCALE_SQRT_MAX)
     ctx = ms.Context(0)
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
@@ -311,7 +314,7 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "bytes_per_launch": dom["bytes"] / dom["launches"], "avg_launch_ms": round(avg_ms, 4)}
     elementwise = {}
-    for k in ("momentum_nesterov", "normalize"):
+    for k in ("momentum_nesterov", "normalize", "unit_rms", "update"):
         if k in stages and stages[k]["total_ms"]:
             gbs = stages[k]["bytes"] / stages[k]["total_ms"] / 1e6
             elementwise[k] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
@@ -332,7 +335,8 @@ def main():
         "config": {"workload": "moe_256x2048x7168_bf16", "matrices": count, "shape": [rows, cols],
                    "ns_steps": 10, "schedule": "deepseekv4 8x(3.4445,-4.7750,2.0315)+2x(2,-1.5,0.5)",
                    "ns_precision": "bf16 MFMA operands, fp32 accumulate, X kept as bf16 hi + 8-bit residual",
-                   "lr": 0.02, "momentum": 0.95, "weight_decay": 0.1, "gamma": 0.2},
+                   "lr": 0.02, "momentum": 0.95, "weight_decay": 0.1, "gamma": 0.2,
+                   "scale_mode": args.scale_mode},
         "ns_tflops": round(ns_tflops, 2),
         "ns_frac_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4),
         "ns_dense_equivalent_tflops": round(dense_flops_step * args.steps / ns_ms / 1e9, 2) if ns_ms else None,
@@ -349,7 +353,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one matrix")
-        out["cpu_baseline"] = cpu_baseline(rows, cols, count)
+        out["cpu_baseline"] = cpu_baseline(rows, cols, count, args.scale_mode)
     print(json.dumps(out), flush=True)
 
 

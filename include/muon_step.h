@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MUON_STEP_ABI_VERSION 1
+#define MUON_STEP_ABI_VERSION 2
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -66,6 +66,21 @@ typedef enum muon_dtype {
  *               rounding of X to average out; their cost is negligible).
  * MUON_NS_F32:  fp32 MFMA operands and accumulation (error vs fp64 ~1e-6). */
 typedef enum muon_ns_precision { MUON_NS_BF16 = 0, MUON_NS_F32 = 1 } muon_ns_precision;
+
+/* How the orthogonalised update O'_t (n x m) is scaled into O_t.
+ * MUON_SCALE_SQRT_MAX: O_t = O'_t * sqrt(max(n, m)) * gamma, the shape rule of
+ *                      DeepSeek-V4's Algorithm 1 (the deep-dive page, "V4 的
+ *                      完整更新公式，逐行拆解" and "更新尺度").
+ * MUON_SCALE_UNIT_RMS: O_t = O'_t * gamma / RMS(O'_t), RMS(X) = ||X||_F /
+ *                      sqrt(n m): the update divided by its own RMS, then
+ *                      multiplied by gamma as the extra scale factor (the
+ *                      deep-dive page's Megatron-Bridge recipe,
+ *                      muon_scale_mode "unit_rms_norm" with
+ *                      muon_extra_scale_factor 0.2).  ||O'_t|| is reduced on
+ *                      the device in fp64 from the fp32 values of O'_t;
+ *                      O'_t = 0 gives a zero scale (decay-only update).  Costs
+ *                      one extra read of X and an unfused update pass. */
+typedef enum muon_scale_mode { MUON_SCALE_SQRT_MAX = 0, MUON_SCALE_UNIT_RMS = 1 } muon_scale_mode;
 
 /* One Newton-Schulz step X <- a X + b (X X^T) X + c (X X^T)^2 X
  * (DeepSeek-V4 book ch. 6, section 3).  Passed to kernels as fp32. */
@@ -104,6 +119,7 @@ typedef struct muon_matrix {
  *   num_ns_steps  0..64.  0 means X = N / ||N||_F with no iteration.
  *   nesterov      1: NS input mu*M_t + G_t;  0: NS input M_t.
  *   ns_precision  muon_ns_precision.
+ *   scale_mode    muon_scale_mode (other values: INVALID_ARGUMENT).
  * lr, momentum, weight_decay and gamma must be finite. */
 typedef struct muon_hparams {
     double lr;
@@ -114,7 +130,7 @@ typedef struct muon_hparams {
     int32_t num_ns_steps;
     int32_t nesterov;
     int32_t ns_precision;
-    int32_t reserved; /* must be 0 */
+    int32_t scale_mode; /* muon_scale_mode */
 } muon_hparams;
 
 /* One tensor handed to muon_adamw_step: numel contiguous fp32 elements each
@@ -213,16 +229,18 @@ muon_status muon_adamw_step(muon_context *ctx, const muon_adamw_tensor *ts, int6
 
 /* Normalisation + Newton-Schulz only: x_out (device fp32 rows x cols)
  * receives NS(n_in / ||n_in||_F) for the device fp32 rows x cols input n_in,
- * with hp's schedule and precision (lr, momentum, weight_decay, gamma and
- * nesterov are ignored).  n_in and x_out must not overlap. */
+ * with hp's schedule and precision (lr, momentum, weight_decay, gamma,
+ * nesterov and scale_mode are ignored).  n_in and x_out must not overlap. */
 muon_status muon_ns_only(muon_context *ctx, const float *n_in, float *x_out, int64_t rows,
                          int64_t cols, const muon_hparams *hp, void *hip_stream);
 
 /* Decay + update given an orthogonalised update x (device fp32 rows x cols,
  * the unscaled O'_t):  param <- fl(fl(d * param) - fl(s * x)) with
- * d = fl32(1 - lr*wd), s = fl32(lr * gamma * sqrt(max(rows, cols))), rounded
- * to bf16 (nearest even) when param_dtype is MUON_BF16.  Exactly the
- * arithmetic muon_step's last stage performs. */
+ * d = fl32(1 - lr*wd), s = fl32(lr * gamma * sqrt(max(rows, cols))) (unit-RMS
+ * mode: s = fl32(lr * (gamma * sqrt(rows * cols) / ||x||_F)), 0 for x = 0,
+ * ||x||^2 summed on the device in fp64), rounded to bf16 (nearest even) when
+ * param_dtype is MUON_BF16.  Exactly the arithmetic muon_step's last stage
+ * performs. */
 muon_status muon_apply_update(muon_context *ctx, void *param, int32_t param_dtype, const float *x,
                               int64_t rows, int64_t cols, const muon_hparams *hp,
                               void *hip_stream);

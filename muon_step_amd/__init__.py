@@ -25,6 +25,8 @@ MUON_F32 = 0
 MUON_BF16 = 1
 MUON_NS_BF16 = 0
 MUON_NS_F32 = 1
+MUON_SCALE_SQRT_MAX = 0
+MUON_SCALE_UNIT_RMS = 1
 
 # Names every build of the library exports (the functions include/muon_step.h declares).
 EXPORTS = (
@@ -56,7 +58,7 @@ class muon_hparams(ctypes.Structure):
                 ("weight_decay", ctypes.c_double), ("gamma", ctypes.c_double),
                 ("schedule", ctypes.POINTER(muon_ns_coeff)), ("num_ns_steps", ctypes.c_int32),
                 ("nesterov", ctypes.c_int32), ("ns_precision", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("scale_mode", ctypes.c_int32)]
 
 
 class muon_adamw_tensor(ctypes.Structure):
@@ -133,7 +135,7 @@ def schedule(name="deepseekv4"):
 
 
 def make_hparams(lr=0.02, momentum=0.95, weight_decay=0.1, gamma=0.2, nesterov=True,
-                 coeffs=None, ns_precision=MUON_NS_BF16):
+                 coeffs=None, ns_precision=MUON_NS_BF16, scale_mode=MUON_SCALE_SQRT_MAX):
     """Builds a muon_hparams; `coeffs` defaults to the DeepSeek-V4 hybrid schedule.
     The returned object keeps its schedule array alive."""
     if coeffs is None:
@@ -141,7 +143,7 @@ def make_hparams(lr=0.02, momentum=0.95, weight_decay=0.1, gamma=0.2, nesterov=T
     arr = (muon_ns_coeff * max(1, len(coeffs)))(*[muon_ns_coeff(*c) for c in coeffs])
     hp = muon_hparams(lr, momentum, weight_decay, gamma,
                       ctypes.cast(arr, ctypes.POINTER(muon_ns_coeff)) if coeffs else None,
-                      len(coeffs), 1 if nesterov else 0, ns_precision, 0)
+                      len(coeffs), 1 if nesterov else 0, ns_precision, scale_mode)
     hp._keep = arr
     return hp
 

@@ -69,6 +69,7 @@ struct Work {
     double *nrm2;         // per chunk matrix
     float *inv_norm;      // per chunk matrix: 1/||N||_F (0 when ||N|| == 0)
     double *call_nrm2;    // per call matrix (indexed by MatDesc::call_index)
+    const float *uscale;  // per chunk matrix update scale s (unit-RMS mode), else nullptr
 };
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {

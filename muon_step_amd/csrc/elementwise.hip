@@ -297,7 +297,9 @@ __global__ __launch_bounds__(256) void pad_zero_kernel(Geom g, Work w) {
 template <typename ParamT>
 __global__ __launch_bounds__(256) void update_plain_kernel(ParamT *__restrict__ p,
                                                            const float *__restrict__ x, int64_t n,
-                                                           float dscale, float sscale) {
+                                                           float dscale, float sscale,
+                                                           const float *__restrict__ s_dev) {
+    if (s_dev) sscale = *s_dev;
     for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
         const float wv = load_val<ParamT>(p, i);
         const float r = dscale * wv - sscale * x[i];
@@ -321,6 +323,7 @@ __global__ __launch_bounds__(256) void update_from_work_kernel(const MatDesc *__
     ParamT *__restrict__ pp = static_cast<ParamT *>(d.param);
     const XView xv_{w.xf ? w.xf + e * w.x_stride : nullptr, static_cast<const uint16_t *>(w.xb) + e * w.x_stride,
                     static_cast<const uint8_t *>(w.xl) + e * w.x_stride};
+    if (w.uscale) sscale = w.uscale[e];
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     if (g.transposed) {
         // X row = W col
@@ -342,6 +345,68 @@ __global__ __launch_bounds__(256) void update_from_work_kernel(const MatDesc *__
             if (d.ns_out) d.ns_out[dst] = xv;
         }
     }
+}
+
+// Unit-RMS mode, first pass: per-block fp64 sums of X^2 over the valid s x l
+// region of each matrix (rows b, b + blocks_per_mat, ...).  The square of an
+// fp32 value is exact in fp64, so only the order of the additions differs
+// from a serial sum.  The bf16 pair (hi, residual) is read 8 columns at a
+// time (16 + 8 bytes) when the row length allows it.
+__global__ __launch_bounds__(256) void x_sumsq_kernel(Geom g, Work w, const float *__restrict__ x_override,
+                                                      int blocks_per_mat) {
+    __shared__ double sh[4];
+    const int64_t e = blockIdx.x / blocks_per_mat;
+    const int b = static_cast<int>(blockIdx.x % blocks_per_mat);
+    double acc = 0.0;
+    const float *xf = x_override ? x_override : (w.xf ? w.xf + e * w.x_stride : nullptr);
+    if (xf) {
+        for (int64_t r = b; r < g.s; r += blocks_per_mat)
+            for (int64_t c = threadIdx.x; c < g.l; c += 256) {
+                const double v = xf[r * g.lp + c];
+                acc += v * v;
+            }
+    } else {
+        const uint16_t *xh = static_cast<const uint16_t *>(w.xb) + e * w.x_stride;
+        const uint8_t *xl = static_cast<const uint8_t *>(w.xl) + e * w.x_stride;
+        const bool vec = (g.l % 8 == 0) && (g.lp % 8 == 0) && (w.x_stride % 8 == 0);
+        for (int64_t r = b; r < g.s; r += blocks_per_mat) {
+            const int64_t row = r * g.lp;
+            if (vec) {
+                for (int64_t c = 8 * threadIdx.x; c < g.l; c += 8 * 256) {
+                    const uint4 h = *reinterpret_cast<const uint4 *>(xh + row + c);
+                    const uint2 l = *reinterpret_cast<const uint2 *>(xl + row + c);
+                    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+                    const uint32_t lw[2] = {l.x, l.y};
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const uint16_t hk = static_cast<uint16_t>(hw[k >> 1] >> (16 * (k & 1)));
+                        const uint8_t lk = static_cast<uint8_t>(lw[k >> 2] >> (8 * (k & 3)));
+                        const double v = join_bf16(hk, lk);
+                        acc += v * v;
+                    }
+                }
+            } else {
+                for (int64_t c = threadIdx.x; c < g.l; c += 256) {
+                    const double v = join_bf16(xh[row + c], xl[row + c]);
+                    acc += v * v;
+                }
+            }
+        }
+    }
+    const double t = block_sum<256>(acc, sh);
+    if (threadIdx.x == 0) w.partials[e * blocks_per_mat + b] = t;
+}
+
+// Unit-RMS mode, second pass: s_e = fl32(lr * (gsq / sqrt(sum X^2))),
+// gsq = gamma * sqrt(rows * cols); a zero X gives s_e = 0.
+__global__ __launch_bounds__(256) void unit_rms_finalize_kernel(Work w, int blocks_per_mat, double lr, double gsq,
+                                                                float *__restrict__ out) {
+    __shared__ double sh[4];
+    const int64_t e = blockIdx.x;
+    double acc = 0.0;
+    for (int b = threadIdx.x; b < blocks_per_mat; b += 256) acc += w.partials[e * blocks_per_mat + b];
+    const double ss = block_sum<256>(acc, sh);
+    if (threadIdx.x == 0) out[e] = (ss == 0.0) ? 0.0f : static_cast<float>(lr * (gsq / sqrt(ss)));
 }
 
 // Copy of the workspace X into a plain rows x cols output (muon_ns_only).
@@ -533,16 +598,25 @@ hipError_t launch_pad_zero(int nmat, const Geom &g, const Work &w, hipStream_t s
     return hipGetLastError();
 }
 hipError_t launch_update_plain(void *param, int param_bf16, const float *x, int64_t n, float d,
-                               float s, hipStream_t st) {
+                               float s, const float *s_dev, hipStream_t st) {
     int64_t nb = (n + 255) / 256;
     if (nb > 65536) nb = 65536;
     if (nb < 1) nb = 1;
     if (param_bf16)
         hipLaunchKernelGGL(update_plain_kernel<uint16_t>, dim3(static_cast<unsigned>(nb)), dim3(256), 0, st,
-                           static_cast<uint16_t *>(param), x, n, d, s);
+                           static_cast<uint16_t *>(param), x, n, d, s, s_dev);
     else
         hipLaunchKernelGGL(update_plain_kernel<float>, dim3(static_cast<unsigned>(nb)), dim3(256), 0, st,
-                           static_cast<float *>(param), x, n, d, s);
+                           static_cast<float *>(param), x, n, d, s, s_dev);
+    return hipGetLastError();
+}
+
+hipError_t launch_unit_rms_scale(int nmat, const Geom &g, const Work &w, const float *x_override,
+                                 int blocks_per_mat, double lr, double gsq, float *out, hipStream_t st) {
+    hipLaunchKernelGGL(x_sumsq_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(blocks_per_mat) * nmat)),
+                       dim3(256), 0, st, g, w, x_override, blocks_per_mat);
+    hipLaunchKernelGGL(unit_rms_finalize_kernel, dim3(static_cast<unsigned>(nmat)), dim3(256), 0, st, w,
+                       blocks_per_mat, lr, gsq, out);
     return hipGetLastError();
 }
 

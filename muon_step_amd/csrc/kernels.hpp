@@ -25,8 +25,15 @@ hipError_t launch_import_n(const float *n_in, const Geom &g, const Work &w, hipS
 int import_n_blocks(const Geom &g);
 hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, hipStream_t st);
 hipError_t launch_pad_zero(int nmat, const Geom &g, const Work &w, hipStream_t st);
+// s_dev, when non-null, is a device float read in place of s.
 hipError_t launch_update_plain(void *param, int param_bf16, const float *x, int64_t n, float d,
-                               float s, hipStream_t st);
+                               float s, const float *s_dev, hipStream_t st);
+// Unit-RMS scale: out[e] = fl32(lr * (gsq / ||X_e||_F)), gsq = gamma * sqrt(rows * cols),
+// 0 when X_e = 0; ||X_e||^2 summed in fp64 over the valid s x l region of
+// workspace X (x_override, when non-null, is one plain fp32 s x l matrix with
+// pitch g.lp instead).  Uses w.partials[0 .. nmat * blocks_per_mat).
+hipError_t launch_unit_rms_scale(int nmat, const Geom &g, const Work &w, const float *x_override,
+                                 int blocks_per_mat, double lr, double gsq, float *out, hipStream_t st);
 hipError_t launch_update_from_work(const MatDesc *descs, int nmat, const Geom &g, const Work &w,
                                    int param_bf16, float d, float s, hipStream_t st);
 hipError_t launch_export_x(const Geom &g, const Work &w, float *out, hipStream_t st);

@@ -98,7 +98,10 @@ muon_status check_hparams(const muon_hparams *hp, char *msg, size_t cap) {
         set_msg(msg, cap, "unknown ns_precision %d", hp->ns_precision);
         return MUON_ERR_INVALID_ARGUMENT;
     }
-    if (hp->reserved != 0) { set_msg(msg, cap, "reserved must be 0"); return MUON_ERR_INVALID_ARGUMENT; }
+    if (hp->scale_mode != MUON_SCALE_SQRT_MAX && hp->scale_mode != MUON_SCALE_UNIT_RMS) {
+        set_msg(msg, cap, "unknown scale_mode %d", hp->scale_mode);
+        return MUON_ERR_INVALID_ARGUMENT;
+    }
     return MUON_OK;
 }
 
@@ -381,10 +384,11 @@ muon_status hip_fail(muon_context *ctx, hipError_t e, const char *where) {
 
 enum Stage {
     ST_MOMENTUM = 0, ST_FINALIZE, ST_NORMALIZE, ST_GRAM, ST_POLY, ST_APPLY, ST_APPLY_UPDATE, ST_UPDATE,
-    ST_ADAMW, ST_IMPORT, ST_EXPORT, ST_COUNT
+    ST_ADAMW, ST_IMPORT, ST_EXPORT, ST_UNIT_RMS, ST_COUNT
 };
 const char *const kStageNames[ST_COUNT] = {"momentum_nesterov", "norm_finalize", "normalize", "gram", "poly",
-                                           "apply", "apply_update", "update", "adamw", "import", "export"};
+                                           "apply", "apply_update", "update", "adamw", "import", "export",
+                                           "unit_rms"};
 
 hipError_t take_event(muon_context *ctx, hipEvent_t *ev) {
     if (ctx->ev_used == ctx->ev_pool.size()) {
@@ -539,10 +543,14 @@ void ns_work(int stage, const Geom &g, bool bf16, int n, bool ns_out, int psize,
 // Runs normalisation + the NS schedule (+ the fused update when `update`) on
 // one chunk whose first stage already wrote X = N and the norms.  Returns the
 // workspace view holding the final X in xf (fp32 path) or xb + xl (bf16 path),
-// meaningful when !update.
+// meaningful when !update.  In the unit-RMS scale mode the last step writes X
+// like the others; ||X||^2 per matrix is then reduced (partial_bpm partial
+// sums per matrix fit in w.partials) into a per-matrix scale, and a separate
+// pass applies the decay + update.
 muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom &g, Work &w, bool bf16,
                    const muon_hparams *hp, bool update, int param_bf16, bool any_ns_out, float d, float s,
-                   hipStream_t st, bool params_aligned16 = false) {
+                   hipStream_t st, bool params_aligned16 = false, int partial_bpm = 0) {
+    const bool unit_rms = update && hp->scale_mode == MUON_SCALE_UNIT_RMS;
     const double xe = static_cast<double>(g.s) * g.l * nmat;
     // bf16 path with a schedule: X stays N and the first step applies 1/||N||
     // (only the padding needs zeros); otherwise a normalisation pass.
@@ -561,7 +569,7 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
         p.a = static_cast<float>(hp->schedule[it].a);
         p.b = static_cast<float>(hp->schedule[it].b);
         p.c = static_cast<float>(hp->schedule[it].c);
-        p.final_update = (update && it == hp->num_ns_steps - 1) ? 1 : 0;
+        p.final_update = (update && !unit_rms && it == hp->num_ns_steps - 1) ? 1 : 0;
         p.param_bf16 = param_bf16;
         p.dscale = d;
         p.sscale = s;
@@ -578,8 +586,17 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
         std::swap(w.xf, w.xf_next);
         std::swap(w.xb, w.xb_next);
     }
-    if (update && hp->num_ns_steps == 0) {
-        const double by = xe * (4.0 + 2.0 * psize + (any_ns_out ? 4.0 : 0.0));
+    if (unit_rms) {
+        const int nbx = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(partial_bpm, g.s)));
+        const double gsq = hp->gamma * std::sqrt(static_cast<double>(g.rows) * static_cast<double>(g.cols));
+        e = timed(ctx, ST_UNIT_RMS, 0.0, xe * (bf16 ? 3.0 : 4.0), st, [&] {
+            return muon::launch_unit_rms_scale(nmat, g, w, nullptr, nbx, hp->lr, gsq, w.inv_norm, st);
+        });
+        if (e != hipSuccess) return hip_fail(ctx, e, "unit-RMS norm launch");
+        w.uscale = w.inv_norm;
+    }
+    if (update && (hp->num_ns_steps == 0 || unit_rms)) {
+        const double by = xe * ((bf16 ? 3.0 : 4.0) + 2.0 * psize + (any_ns_out ? 4.0 : 0.0));
         e = timed(ctx, ST_UPDATE, 0.0, by, st,
                   [&] { return muon::launch_update_from_work(descs, nmat, g, w, param_bf16, d, s, st); });
         if (e != hipSuccess) return hip_fail(ctx, e, "update launch");
@@ -757,7 +774,7 @@ muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count,
                       [&] { return muon::launch_norm_finalize(dd, n, w, gp.bpm, st); });
             if (e != hipSuccess) return hip_fail(ctx, e, "norm launch");
             s = run_ns(ctx, dd, n, gp.g, w, bf16, hp, true, gp.param_dtype == MUON_BF16, any_out, d, sc, st,
-                       params_aligned);
+                       params_aligned, gp.bpm);
             if (s != MUON_OK) return s;
         }
         pos += static_cast<size_t>(n_all);
@@ -832,8 +849,29 @@ muon_status muon_apply_update(muon_context *ctx, void *param, int32_t param_dtyp
     DeviceGuard guard(ctx->device);
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const double by = static_cast<double>(rows) * cols * (4.0 + 2.0 * dtype_size(param_dtype));
-    hipError_t e = timed(ctx, ST_UPDATE, 0.0, by, st, [&] {
-        return muon::launch_update_plain(param, param_dtype == MUON_BF16, x, rows * cols, d, sc, st);
+    const float *s_dev = nullptr;
+    hipError_t e = hipSuccess;
+    if (hp->scale_mode == MUON_SCALE_UNIT_RMS) {
+        // ||x||^2 over the plain rows x cols matrix: rows reduced in up to 1024
+        // blocks, the scale written after the partial sums.
+        const int nbx = static_cast<int>(std::min<int64_t>(rows, 1024));
+        const size_t part = align_up(static_cast<size_t>(nbx) * sizeof(double));
+        if ((s = ensure(ctx, ctx->tabs, part + sizeof(float), "norm tables")) != MUON_OK) return s;
+        Geom g{};
+        g.rows = g.s = g.sp = rows;
+        g.cols = g.l = g.lp = cols;
+        Work w{};
+        w.partials = static_cast<double *>(ctx->tabs.p);
+        float *sd = reinterpret_cast<float *>(static_cast<char *>(ctx->tabs.p) + part);
+        const double gsq = hp->gamma * std::sqrt(static_cast<double>(rows) * static_cast<double>(cols));
+        e = timed(ctx, ST_UNIT_RMS, 0.0, static_cast<double>(rows) * cols * 4.0, st, [&] {
+            return muon::launch_unit_rms_scale(1, g, w, x, nbx, hp->lr, gsq, sd, st);
+        });
+        if (e != hipSuccess) return hip_fail(ctx, e, "unit-RMS norm launch");
+        s_dev = sd;
+    }
+    e = timed(ctx, ST_UPDATE, 0.0, by, st, [&] {
+        return muon::launch_update_plain(param, param_dtype == MUON_BF16, x, rows * cols, d, sc, s_dev, st);
     });
     if (e != hipSuccess) return hip_fail(ctx, e, "update launch");
     ctx->err.clear();

@@ -154,6 +154,16 @@ def apply_update_f32(w, x32, lr, weight_decay, gamma, param_bf16, scale_mode="sq
     x32 = np.asarray(x32, dtype=np.float32)
     rows, cols = w.shape
     d, s = muon_scalars_f32(lr, weight_decay, gamma, rows, cols, x32, scale_mode)
+    return apply_update_ds_f32(w, x32, d, s, param_bf16)
+
+
+def apply_update_ds_f32(w, x32, d, s, param_bf16):
+    """fl(fl(d*w) - fl(s*x)) in float32 for given float32 scalars d and s, rounded
+    to bfloat16 (RNE) when the parameter is bfloat16 (the decay + update step of
+    Algorithm 1 with its scalars already formed)."""
+    w = np.asarray(w, dtype=np.float32)
+    x32 = np.asarray(x32, dtype=np.float32)
+    d, s = np.float32(d), np.float32(s)
     out = (d * w) - (s * x32)
     out = out.astype(np.float32)
     if param_bf16:

@@ -61,7 +61,7 @@ int main(void) {
   printf("muon_ns_coeff %zu\n", sizeof(muon_ns_coeff));
   F(muon_matrix, rows) F(muon_matrix, param_dtype) F(muon_matrix, grad_dtype) F(muon_matrix, ns_out)
   F(muon_hparams, schedule) F(muon_hparams, num_ns_steps) F(muon_hparams, ns_precision)
-  F(muon_hparams, reserved) F(muon_adamw_tensor, numel) F(muon_adamw_tensor, grad_dtype)
+  F(muon_hparams, scale_mode) F(muon_adamw_tensor, numel) F(muon_adamw_tensor, grad_dtype)
   F(muon_adamw_hparams, step)
   printf("muon_stage_stats %zu\n", sizeof(muon_stage_stats));
   F(muon_stage_stats, launches) F(muon_stage_stats, total_ms) F(muon_stage_stats, bytes)
@@ -131,7 +131,7 @@ def test_valid_step_args(lib):
 
 @pytest.mark.parametrize("case", [
     "null_param", "null_grad", "null_mom", "rows0", "cols_neg", "dtype", "steps_neg", "steps_big",
-    "sched_null", "lr_nan", "gamma_inf", "nesterov2", "precision", "reserved", "coeff_nan",
+    "sched_null", "lr_nan", "gamma_inf", "nesterov2", "precision", "scale_mode", "coeff_nan",
     "grad_aliases_param", "mom_aliases_param", "two_mats_share_param", "ns_out_aliases_grad",
     "null_hparams",
 ])
@@ -152,7 +152,7 @@ def test_invalid_step_args(lib, case):
     elif case == "gamma_inf": hp.gamma = math.inf
     elif case == "nesterov2": hp.nesterov = 2
     elif case == "precision": hp.ns_precision = 5
-    elif case == "reserved": hp.reserved = 1
+    elif case == "scale_mode": hp.scale_mode = 2
     elif case == "coeff_nan": hp._keep[3].b = math.nan
     elif case == "grad_aliases_param": m.grad = m.param + 16
     elif case == "mom_aliases_param": m.momentum = m.param + 64 * 128 * 2 - 4

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import (BF16_TOL, F32_TOL, assert_bitexact, rel_fro, say, scale_of, to_dev, to_np)
+from gpu_util import (BF16_TOL, F32_TOL, assert_bitexact, rel_fro, say, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -101,7 +101,7 @@ def test_ns_only_zero_steps_is_normalisation(ctx, torch_mod, precision):
 
 
 def _run_step(ctx, torch_mod, specs, precision, seed, lr=0.02, wd=0.1, gamma=0.2, mu=0.95, nesterov=True,
-              coeffs=None, zero_grad=False):
+              coeffs=None, zero_grad=False, scale_mode="sqrt_max"):
     """Runs muon_step on freshly generated matrices and checks every matrix against the oracle."""
     ms = _ms()
     wl = synth.Workload("t", seed, tuple(specs))
@@ -120,7 +120,8 @@ def _run_step(ctx, torch_mod, specs, precision, seed, lr=0.02, wd=0.1, gamma=0.2
         dev.append((p, g, m, o))
         mats.append(ms.matrix(p, g, m, o))
     hp = ms.make_hparams(lr=lr, momentum=mu, weight_decay=wd, gamma=gamma, nesterov=nesterov, coeffs=coeffs,
-                         ns_precision=ms.MUON_NS_BF16 if precision == "bf16" else ms.MUON_NS_F32)
+                         ns_precision=ms.MUON_NS_BF16 if precision == "bf16" else ms.MUON_NS_F32,
+                         scale_mode=ms.MUON_SCALE_UNIT_RMS if scale_mode == "unit_rms" else ms.MUON_SCALE_SQRT_MAX)
     ctx.muon_step(mats, hp)
     torch_mod.cuda.synchronize()
     sched = tuple(tuple(c) for c in (coeffs if coeffs is not None else ms.schedule("deepseekv4")))
@@ -138,10 +139,12 @@ def _run_step(ctx, torch_mod, specs, precision, seed, lr=0.02, wd=0.1, gamma=0.2
         if zero_grad:
             assert not np.any(x_gpu)
         else:
-            err = rel_fro(x_gpu * scale_of(sp.rows, sp.cols, gamma), x_ref * scale_of(sp.rows, sp.cols, gamma))
+            err = rel_fro(x_gpu * oracle.update_scale(x_gpu, gamma, scale_mode),
+                          x_ref * oracle.update_scale(x_ref, gamma, scale_mode))
             say(f"  matrix {i} {sp.rows}x{sp.cols} p={sp.param_dtype} g={sp.grad_dtype}: O rel err {err:.3e}")
             assert err <= tol
-        w_ref = oracle.apply_update_f32(inp["w"], x_gpu, lr, wd, gamma, sp.param_dtype == "bf16")
+        # unit-RMS mode: s from ||fl32 X||, summed in fp64 in another order on the device
+        w_ref = oracle.apply_update_f32(inp["w"], x_gpu, lr, wd, gamma, sp.param_dtype == "bf16", scale_mode)
         assert_bitexact(to_np(p), w_ref, f"param of matrix {i}")
     return host, dev
 
@@ -158,6 +161,31 @@ def test_step_mixed_group(ctx, torch_mod, precision):
              S(256, 512, "bf16", "bf16"), S(256, 512, "bf16", "bf16"), S(512, 256, "bf16", "bf16")]
     say(f"step mixed group {precision}")
     _run_step(ctx, torch_mod, specs, precision, seed=21)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_step_unit_rms_mode(ctx, torch_mod, precision):
+    """The unit-RMS scale mode (Megatron-Bridge recipe): the last step writes X, ||X|| is
+    reduced per matrix, and the update runs as a separate pass with a per-matrix scale.
+    Grouped, ragged and transposed shapes, both parameter dtypes, the gamma = 0.2 extra
+    factor."""
+    S = synth.MatrixSpec
+    specs = [S(96, 300, "bf16", "bf16"), S(96, 300, "bf16", "bf16"), S(300, 96, "bf16", "bf16"),
+             S(260, 260, "f32", "f32", law="gauss"), S(64, 128, "f32", "bf16"), S(5, 3, "f32", "f32", law="gauss"),
+             S(256, 512, "bf16", "bf16"), S(512, 256, "bf16", "bf16"), S(1, 9, "f32", "f32")]
+    say(f"step unit-RMS {precision}")
+    _run_step(ctx, torch_mod, specs, precision, seed=27, scale_mode="unit_rms")
+
+
+def test_step_unit_rms_degenerate(ctx, torch_mod):
+    """Unit-RMS mode with the zero-step schedule (X = N / ||N||, so O = N * gamma / RMS(N))
+    and with a zero gradient (X = 0: a zero scale, decay only)."""
+    S = synth.MatrixSpec
+    specs = [S(70, 130), S(130, 70, "f32", "f32")]
+    say("step unit-RMS zero schedule")
+    _run_step(ctx, torch_mod, specs, "bf16", seed=28, coeffs=[], scale_mode="unit_rms")
+    say("step unit-RMS zero gradient")
+    _run_step(ctx, torch_mod, specs, "bf16", seed=29, zero_grad=True, scale_mode="unit_rms")
 
 
 def test_step_single_f32_64x128_workload(ctx, torch_mod):
@@ -260,6 +288,27 @@ def test_apply_update_bitexact(ctx, torch_mod, param_dtype):
     torch_mod.cuda.synchronize()
     ref = oracle.apply_update_f32(w, x, 0.5, 0.5, 0.25, param_dtype == "bf16")
     assert_bitexact(to_np(p), ref, "apply_update")
+
+
+@pytest.mark.parametrize("param_dtype", ["bf16", "f32"])
+def test_apply_update_unit_rms_bitexact(ctx, torch_mod, param_dtype):
+    """The update hook in the unit-RMS mode: s = fl32(lr * gamma * sqrt(n m) / ||x||) with
+    ||x||^2 reduced on the device; finite x with zeros, subnormals and a wide range; x = 0
+    gives s = 0 (decay only)."""
+    ms = _ms()
+    rows, cols = 1100, 77
+    r = np.random.default_rng(33)
+    w = oracle.bf16_round_f32((r.standard_normal((rows, cols)) * 0.02).astype(np.float32))
+    x = r.standard_normal((rows, cols)).astype(np.float32)
+    x.flat[:6] = np.array([0.0, -0.0, 1e-40, -3e-39, 3e4, -1e-20], np.float32)
+    hp = ms.make_hparams(lr=0.5, weight_decay=0.5, gamma=0.25, scale_mode=ms.MUON_SCALE_UNIT_RMS)
+    pt = torch_mod.bfloat16 if param_dtype == "bf16" else torch_mod.float32
+    for xx in (x, np.zeros_like(x)):
+        p = to_dev(w, pt)
+        ctx.muon_apply_update(p, to_dev(xx, torch_mod.float32), hp)
+        torch_mod.cuda.synchronize()
+        ref = oracle.apply_update_f32(w, xx, 0.5, 0.5, 0.25, param_dtype == "bf16", "unit_rms")
+        assert_bitexact(to_np(p), ref, "apply_update unit-RMS")
 
 
 def test_bf16_rounding_ties_bitexact(ctx, torch_mod):
