@@ -347,6 +347,59 @@ __global__ __launch_bounds__(256) void update_from_work_kernel(const MatDesc *__
     }
 }
 
+// Decay + update from the bf16 workspace X when X has W's row layout (not
+// transposed, l a multiple of 8, 16-byte aligned W and ns_out): 8 consecutive
+// elements per lane, 16 + 8 bytes of X and 16 (bf16) or 32 (fp32) bytes of W
+// in one load each.  Same arithmetic as update_from_work_kernel.
+template <typename ParamT>
+__global__ __launch_bounds__(256) void update_from_work_vec_kernel(const MatDesc *__restrict__ descs, Geom g,
+                                                                   Work w, float dscale, float sscale,
+                                                                   int blocks_per_mat) {
+    const int64_t e = blockIdx.x / blocks_per_mat;
+    const int64_t q = static_cast<int64_t>(blockIdx.x % blocks_per_mat) * 256 + threadIdx.x;
+    const int64_t gpr = g.l / 8;
+    if (q >= g.s * gpr) return;
+    const int64_t r = q / gpr, c = (q - r * gpr) * 8;
+    if (w.uscale) sscale = w.uscale[e];
+    const MatDesc d = descs[e];
+    const int64_t xo = e * w.x_stride + r * g.lp + c;
+    const uint4 h = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(w.xb) + xo);
+    const uint2 l = *reinterpret_cast<const uint2 *>(static_cast<const uint8_t *>(w.xl) + xo);
+    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+    const uint32_t lw[2] = {l.x, l.y};
+    float xv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        xv[k] = join_bf16(static_cast<uint16_t>(hw[k >> 1] >> (16 * (k & 1))),
+                          static_cast<uint8_t>(lw[k >> 2] >> (8 * (k & 3))));
+    const int64_t dst = r * g.cols + c;
+    if constexpr (sizeof(ParamT) == 2) {
+        uint4 *pw = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(d.param) + dst);
+        const uint4 wv = *pw;
+        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float r0 = dscale * bf16_bits_to_float(static_cast<uint16_t>(ww[k])) - sscale * xv[2 * k];
+            const float r1 = dscale * bf16_bits_to_float(static_cast<uint16_t>(ww[k] >> 16)) - sscale * xv[2 * k + 1];
+            o[k] = static_cast<uint32_t>(float_to_bf16_bits(r0)) | (static_cast<uint32_t>(float_to_bf16_bits(r1)) << 16);
+        }
+        *pw = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+        float4 *pw = reinterpret_cast<float4 *>(static_cast<float *>(d.param) + dst);
+        const float4 a = pw[0], b = pw[1];
+        pw[0] = make_float4(dscale * a.x - sscale * xv[0], dscale * a.y - sscale * xv[1],
+                            dscale * a.z - sscale * xv[2], dscale * a.w - sscale * xv[3]);
+        pw[1] = make_float4(dscale * b.x - sscale * xv[4], dscale * b.y - sscale * xv[5],
+                            dscale * b.z - sscale * xv[6], dscale * b.w - sscale * xv[7]);
+    }
+    if (d.ns_out) {
+        float4 *po = reinterpret_cast<float4 *>(d.ns_out + dst);
+        po[0] = make_float4(xv[0], xv[1], xv[2], xv[3]);
+        po[1] = make_float4(xv[4], xv[5], xv[6], xv[7]);
+    }
+}
+
 // Unit-RMS mode, first pass: per-block fp64 sums of X^2 over the valid s x l
 // region of each matrix (rows b, b + blocks_per_mat, ...).  The square of an
 // fp32 value is exact in fp64, so only the order of the additions differs
@@ -621,7 +674,18 @@ hipError_t launch_unit_rms_scale(int nmat, const Geom &g, const Work &w, const f
 }
 
 hipError_t launch_update_from_work(const MatDesc *descs, int nmat, const Geom &g, const Work &w,
-                                   int param_bf16, float d, float s, hipStream_t st) {
+                                   int param_bf16, float d, float s, bool aligned16, hipStream_t st) {
+    const int64_t vbpm = (g.s * (g.l / 8) + 255) / 256;
+    if (aligned16 && !w.xf && !g.transposed && g.l % 8 == 0 && g.lp % 8 == 0 && w.x_stride % 8 == 0 &&
+        vbpm * nmat <= 0x7fffffff) {
+        const int bpm = static_cast<int>(vbpm);
+        const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(bpm) * nmat));
+        if (param_bf16)
+            hipLaunchKernelGGL(update_from_work_vec_kernel<uint16_t>, grid, dim3(256), 0, st, descs, g, w, d, s, bpm);
+        else
+            hipLaunchKernelGGL(update_from_work_vec_kernel<float>, grid, dim3(256), 0, st, descs, g, w, d, s, bpm);
+        return hipGetLastError();
+    }
     const int tc = static_cast<int>((g.cols + 63) / 64);
     const int bpm = static_cast<int>(((g.rows + 63) / 64) * tc);
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(bpm) * nmat));

@@ -34,8 +34,11 @@ hipError_t launch_update_plain(void *param, int param_bf16, const float *x, int6
 // pitch g.lp instead).  Uses w.partials[0 .. nmat * blocks_per_mat).
 hipError_t launch_unit_rms_scale(int nmat, const Geom &g, const Work &w, const float *x_override,
                                  int blocks_per_mat, double lr, double gsq, float *out, hipStream_t st);
+// Decay + update from workspace X (per-matrix scale w.uscale when set).
+// aligned16: every param and ns_out of the chunk is 16-byte aligned, which
+// lets the untransposed bf16-workspace case take 8 elements per lane.
 hipError_t launch_update_from_work(const MatDesc *descs, int nmat, const Geom &g, const Work &w,
-                                   int param_bf16, float d, float s, hipStream_t st);
+                                   int param_bf16, float d, float s, bool aligned16, hipStream_t st);
 hipError_t launch_export_x(const Geom &g, const Work &w, float *out, hipStream_t st);
 int64_t adamw_blocks(int64_t numel);
 hipError_t launch_adamw(const void *descs_dev, int count, int64_t total_blocks, const AdamwScalars &k,

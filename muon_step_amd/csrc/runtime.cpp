@@ -549,7 +549,7 @@ void ns_work(int stage, const Geom &g, bool bf16, int n, bool ns_out, int psize,
 // pass applies the decay + update.
 muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom &g, Work &w, bool bf16,
                    const muon_hparams *hp, bool update, int param_bf16, bool any_ns_out, float d, float s,
-                   hipStream_t st, bool params_aligned16 = false, int partial_bpm = 0) {
+                   hipStream_t st, bool params_aligned16 = false, int partial_bpm = 0, bool outs_aligned16 = false) {
     const bool unit_rms = update && hp->scale_mode == MUON_SCALE_UNIT_RMS;
     const double xe = static_cast<double>(g.s) * g.l * nmat;
     // bf16 path with a schedule: X stays N and the first step applies 1/||N||
@@ -598,7 +598,10 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
     if (update && (hp->num_ns_steps == 0 || unit_rms)) {
         const double by = xe * ((bf16 ? 3.0 : 4.0) + 2.0 * psize + (any_ns_out ? 4.0 : 0.0));
         e = timed(ctx, ST_UPDATE, 0.0, by, st,
-                  [&] { return muon::launch_update_from_work(descs, nmat, g, w, param_bf16, d, s, st); });
+                  [&] {
+                      return muon::launch_update_from_work(descs, nmat, g, w, param_bf16, d, s,
+                                                           params_aligned16 && outs_aligned16, st);
+                  });
         if (e != hipSuccess) return hip_fail(ctx, e, "update launch");
     }
     return MUON_OK;
@@ -753,11 +756,12 @@ muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count,
         for (int64_t c0 = 0; c0 < n_all; c0 += gp.chunk) {
             const int n = static_cast<int>(std::min<int64_t>(gp.chunk, n_all - c0));
             const MatDesc *dd = ddev + pos + c0;
-            bool vec_ok = true, params_aligned = true;
+            bool vec_ok = true, params_aligned = true, outs_aligned = true;
             for (int k = 0; k < n; ++k) {
                 const muon_matrix &m = mats[gp.members[c0 + k]];
                 vec_ok = vec_ok && aligned16(m.momentum) && aligned16(m.grad);
                 params_aligned = params_aligned && aligned16(m.param);
+                outs_aligned = outs_aligned && (!m.ns_out || aligned16(m.ns_out));
             }
             bool any_out = false;
             for (int k = 0; k < n; ++k) any_out = any_out || mats[gp.members[c0 + k]].ns_out != nullptr;
@@ -774,7 +778,7 @@ muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count,
                       [&] { return muon::launch_norm_finalize(dd, n, w, gp.bpm, st); });
             if (e != hipSuccess) return hip_fail(ctx, e, "norm launch");
             s = run_ns(ctx, dd, n, gp.g, w, bf16, hp, true, gp.param_dtype == MUON_BF16, any_out, d, sc, st,
-                       params_aligned, gp.bpm);
+                       params_aligned, gp.bpm, outs_aligned);
             if (s != MUON_OK) return s;
         }
         pos += static_cast<size_t>(n_all);
