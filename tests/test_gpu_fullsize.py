@@ -101,6 +101,49 @@ def test_moe_expert_batch_full_size(torch_mod):
     assert bool((moms == grads.float()).all())
 
 
+def test_moe_expert_batch_full_size_unit_rms(torch_mod):
+    """The same batch in the unit-RMS scale mode (X written by the last step, ||X|| reduced
+    per matrix, a separate update pass): expert 97 against the oracle, and every expert's
+    applied update (d W0 - W1) / lr against RMS = gamma, which that mode fixes whatever the
+    singular values are (bf16 rounding of W1 perturbs it by about 1e-4)."""
+    torch = torch_mod
+    ms = _ms()
+    rows, cols, count = 2048, 7168, 256
+    say("moe 256 x 2048x7168 unit-RMS: generating inputs on the device")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    grads = synth.spectral_grad_torch(rows, cols, count, gen, "cuda")
+    params = (torch.randn(count, rows, cols, generator=gen, device="cuda") * synth.gen.PARAM_STD).to(torch.bfloat16)
+    moms = torch.zeros(count, rows, cols, dtype=torch.float32, device="cuda")
+    w0 = params.clone()
+    e = 97
+    out = torch.empty(rows, cols, dtype=torch.float32, device="cuda")
+    mats = [ms.matrix(params[i], grads[i], moms[i], out if i == e else None) for i in range(count)]
+    ctx = ms.Context(0)
+    try:
+        say("moe 256 x 2048x7168 unit-RMS: one Muon step")
+        ctx.muon_step(mats, ms.make_hparams(lr=LR, momentum=MU, weight_decay=WD, gamma=GAMMA,
+                                            scale_mode=ms.MUON_SCALE_UNIT_RMS))
+        torch.cuda.synchronize()
+    finally:
+        ctx.close()
+    say(f"moe expert {e} unit-RMS: oracle")
+    w0_host = to_np(w0[e])
+    ref = oracle.muon_step(w0_host, to_np(grads[e]), np.zeros((rows, cols), np.float32), lr=LR, momentum=MU,
+                           weight_decay=WD, gamma=GAMMA, param_bf16=True, scale_mode="unit_rms")
+    x_gpu = to_np(out)
+    err = rel_fro(x_gpu * oracle.update_scale(x_gpu, GAMMA, "unit_rms"), ref["o"])
+    say(f"  matrix {e} {rows}x{cols}: O rel err {err:.3e}")
+    assert err <= BF16_TOL
+    w_ref = oracle.apply_update_f32(w0_host, x_gpu, LR, WD, GAMMA, True, "unit_rms")
+    assert_bitexact(to_np(params[e]), w_ref, f"param of matrix {e}")
+    d = float(np.float32(1.0 - LR * WD))
+    rms = [float(torch.linalg.vector_norm(((d * w0[i].double() - params[i].double()) / LR))) /
+           math.sqrt(rows * cols) / GAMMA for i in range(count)]
+    say(f"moe unit-RMS: RMS(O)/gamma over 256 experts in [{min(rms):.5f}, {max(rms):.5f}]")
+    assert all(abs(r - 1.0) < 1e-3 for r in rms)
+
+
 def _run_workload_sampled(torch, specs, seed, oracle_names, cap_bytes=0):
     """One call over the workload's matrices (device-generated spectral grads, params
     N(0, 0.02), prefilled momentum where the spec says so); the named matrices
