@@ -153,7 +153,8 @@ def moe16b_step(args):
                            torch.zeros_like(p)))
     tensors = [ms.adamw_tensor(*b) for b in adamw_bufs]
     hp = ms.make_hparams(lr=0.02, momentum=0.95, weight_decay=0.1, gamma=0.2, nesterov=True,
-                         ns_precision=ms.MUON_NS_BF16)
+                         ns_precision=ms.MUON_NS_BF16,
+                         scale_mode=ms.MUON_SCALE_UNIT_RMS if args.scale_mode == "unit_rms" else ms.MUON_SCALE_SQRT_MAX)
     ctx = ms.Context(0, args.workspace_gib << 30)
     stream = torch.cuda.current_stream()
 
@@ -185,7 +186,7 @@ def moe16b_step(args):
         "value": round(1000.0 / ms_per_step, 4), "unit": "steps/s", "ms_per_step": round(ms_per_step, 3),
         "steps": args.steps, "warmup": args.warmup, "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "moe16b_full_step", "muon_matrices": len(specs),
-                   "workspace_cap_gib": args.workspace_gib},
+                   "workspace_cap_gib": args.workspace_gib, "scale_mode": args.scale_mode},
         "ns_tflops": round(ns_flops / ns_ms / 1e9, 2) if ns_ms else None,
         "ns_frac_bf16_peak": round(ns_flops / ns_ms / 1e9 / PEAK_BF16_TFLOPS, 4) if ns_ms else None,
         "stage_ms_per_step": breakdown}), flush=True)
