@@ -258,7 +258,8 @@ muon_status muon_last_norms(muon_context *ctx, double *out, int64_t capacity, in
  * A A, and the bytes it must move to and from HBM) is recorded with it.
  * Stage names: "momentum_nesterov", "norm_finalize", "normalize", "gram",
  * "poly", "apply", "apply_update" (the last product with the fused decay and
- * update), "update", "adamw", "import", "export". */
+ * update), "update", "adamw", "import", "export", "unit_rms" (the per-matrix
+ * ||X||^2 reduction and scale of the unit-RMS mode). */
 typedef struct muon_stage_stats {
     char name[32];
     int64_t launches;
