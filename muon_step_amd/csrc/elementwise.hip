@@ -400,6 +400,80 @@ __global__ __launch_bounds__(256) void update_from_work_vec_kernel(const MatDesc
     }
 }
 
+// The same for a transposed matrix (X = W^T, so W row i is X column i): one
+// 64 x 64 tile per block.  X rows j0 .. j0+63, columns i0 .. i0+63 are read
+// 8 columns per load (16 + 8 bytes) into LDS, always inside the padded
+// workspace (sp and lp are multiples of 256); W rows i0 .. i0+63 are then
+// written 8 columns (W cols = X rows) per lane.  Needs cols % 8 == 0 so that
+// every 8-wide group of a W row is inside the matrix or wholly outside it.
+template <typename ParamT>
+__global__ __launch_bounds__(256) void update_from_work_tvec_kernel(const MatDesc *__restrict__ descs, Geom g,
+                                                                    Work w, float dscale, float sscale,
+                                                                    int tiles_c, int blocks_per_mat) {
+    __shared__ float tile[64][65];
+    const int64_t e = blockIdx.x / blocks_per_mat;
+    const int64_t t = blockIdx.x % blocks_per_mat;
+    const int64_t i0 = (t / tiles_c) * 64;  // W row = X column
+    const int64_t j0 = (t % tiles_c) * 64;  // W column = X row
+    if (w.uscale) sscale = w.uscale[e];
+    const uint16_t *xh = static_cast<const uint16_t *>(w.xb) + e * w.x_stride;
+    const uint8_t *xl = static_cast<const uint8_t *>(w.xl) + e * w.x_stride;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int q = threadIdx.x + 256 * half;
+        const int row = q >> 3, cg = (q & 7) * 8;
+        const int64_t xo = (j0 + row) * g.lp + i0 + cg;
+        const uint4 h = *reinterpret_cast<const uint4 *>(xh + xo);
+        const uint2 l = *reinterpret_cast<const uint2 *>(xl + xo);
+        const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+        const uint32_t lw[2] = {l.x, l.y};
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            tile[row][cg + k] = join_bf16(static_cast<uint16_t>(hw[k >> 1] >> (16 * (k & 1))),
+                                          static_cast<uint8_t>(lw[k >> 2] >> (8 * (k & 3))));
+    }
+    __syncthreads();
+    const MatDesc d = descs[e];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int q = threadIdx.x + 256 * half;
+        const int wr = q >> 3, wc = (q & 7) * 8;
+        const int64_t i = i0 + wr, j = j0 + wc;
+        if (i >= g.rows || j >= g.cols) continue;
+        float xv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) xv[k] = tile[wc + k][wr];
+        const int64_t dst = i * g.cols + j;
+        if constexpr (sizeof(ParamT) == 2) {
+            uint4 *pw = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(d.param) + dst);
+            const uint4 wv = *pw;
+            const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float r0 = dscale * bf16_bits_to_float(static_cast<uint16_t>(ww[k])) - sscale * xv[2 * k];
+                const float r1 =
+                    dscale * bf16_bits_to_float(static_cast<uint16_t>(ww[k] >> 16)) - sscale * xv[2 * k + 1];
+                o[k] = static_cast<uint32_t>(float_to_bf16_bits(r0)) |
+                       (static_cast<uint32_t>(float_to_bf16_bits(r1)) << 16);
+            }
+            *pw = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+            float4 *pw = reinterpret_cast<float4 *>(static_cast<float *>(d.param) + dst);
+            const float4 a = pw[0], b = pw[1];
+            pw[0] = make_float4(dscale * a.x - sscale * xv[0], dscale * a.y - sscale * xv[1],
+                                dscale * a.z - sscale * xv[2], dscale * a.w - sscale * xv[3]);
+            pw[1] = make_float4(dscale * b.x - sscale * xv[4], dscale * b.y - sscale * xv[5],
+                                dscale * b.z - sscale * xv[6], dscale * b.w - sscale * xv[7]);
+        }
+        if (d.ns_out) {
+            float4 *po = reinterpret_cast<float4 *>(d.ns_out + dst);
+            po[0] = make_float4(xv[0], xv[1], xv[2], xv[3]);
+            po[1] = make_float4(xv[4], xv[5], xv[6], xv[7]);
+        }
+    }
+}
+
 // Unit-RMS mode, first pass: per-block fp64 sums of X^2 over the valid s x l
 // region of each matrix (rows b, b + blocks_per_mat, ...).  The square of an
 // fp32 value is exact in fp64, so only the order of the additions differs
@@ -687,6 +761,17 @@ hipError_t launch_update_from_work(const MatDesc *descs, int nmat, const Geom &g
         return hipGetLastError();
     }
     const int tc = static_cast<int>((g.cols + 63) / 64);
+    if (aligned16 && !w.xf && g.transposed && g.cols % 8 == 0) {
+        const int bpm = static_cast<int>(((g.rows + 63) / 64) * tc);
+        const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(bpm) * nmat));
+        if (param_bf16)
+            hipLaunchKernelGGL(update_from_work_tvec_kernel<uint16_t>, grid, dim3(256), 0, st, descs, g, w, d, s, tc,
+                               bpm);
+        else
+            hipLaunchKernelGGL(update_from_work_tvec_kernel<float>, grid, dim3(256), 0, st, descs, g, w, d, s, tc,
+                               bpm);
+        return hipGetLastError();
+    }
     const int bpm = static_cast<int>(((g.rows + 63) / 64) * tc);
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(bpm) * nmat));
     if (param_bf16)

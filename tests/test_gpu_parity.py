@@ -181,7 +181,8 @@ def test_step_unit_rms_degenerate(ctx, torch_mod):
     """Unit-RMS mode with the zero-step schedule (X = N / ||N||, so O = N * gamma / RMS(N))
     and with a zero gradient (X = 0: a zero scale, decay only)."""
     S = synth.MatrixSpec
-    specs = [S(70, 130), S(130, 70, "f32", "f32"), S(40, 136), S(24, 64, "f32", "bf16")]
+    specs = [S(70, 130), S(130, 70, "f32", "f32"), S(40, 136), S(24, 64, "f32", "bf16"), S(200, 72),
+             S(136, 40, "f32", "f32")]
     say("step unit-RMS zero schedule")
     _run_step(ctx, torch_mod, specs, "bf16", seed=28, coeffs=[], scale_mode="unit_rms")
     say("step zero schedule, bf16 workspace")
