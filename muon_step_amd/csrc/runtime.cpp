@@ -551,6 +551,14 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
                    const muon_hparams *hp, bool update, int param_bf16, bool any_ns_out, float d, float s,
                    hipStream_t st, bool params_aligned16 = false, int partial_bpm = 0, bool outs_aligned16 = false) {
     const bool unit_rms = update && hp->scale_mode == MUON_SCALE_UNIT_RMS;
+    // bf16 parameters whose tiles allow staging W through LDS keep the update
+    // fused into the last product.  Other shapes whose W rows allow 8-wide
+    // access run the last step as a plain product plus a separate update
+    // pass, which costs less than the per-element fused epilogue there.
+    const bool w_staged = param_bf16 && params_aligned16 && !g.transposed && g.s % muon::kTile == 0 &&
+                          g.l % muon::kTile == 0;
+    const bool split_update = update && !unit_rms && bf16 && !w_staged && params_aligned16 && outs_aligned16 &&
+                              (g.transposed ? g.cols % 8 == 0 : g.l % 8 == 0);
     const double xe = static_cast<double>(g.s) * g.l * nmat;
     // bf16 path with a schedule: X stays N and the first step applies 1/||N||
     // (only the padding needs zeros); otherwise a normalisation pass.
@@ -569,12 +577,12 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
         p.a = static_cast<float>(hp->schedule[it].a);
         p.b = static_cast<float>(hp->schedule[it].b);
         p.c = static_cast<float>(hp->schedule[it].c);
-        p.final_update = (update && !unit_rms && it == hp->num_ns_steps - 1) ? 1 : 0;
+        p.final_update = (update && !unit_rms && !split_update && it == hp->num_ns_steps - 1) ? 1 : 0;
         p.param_bf16 = param_bf16;
         p.dscale = d;
         p.sscale = s;
         p.unnormalized = (fold && it == 0) ? 1 : 0;
-        p.w_staged = (param_bf16 && params_aligned16 && !g.transposed && g.s % muon::kTile == 0 && g.l % muon::kTile == 0) ? 1 : 0;
+        p.w_staged = w_staged ? 1 : 0;
         for (int kind = 0; kind < 3; ++kind) {
             const int stage = kind == 0 ? ST_GRAM : kind == 1 ? ST_POLY : (p.final_update ? ST_APPLY_UPDATE : ST_APPLY);
             double fl = 0, by = 0;
@@ -595,7 +603,7 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
         if (e != hipSuccess) return hip_fail(ctx, e, "unit-RMS norm launch");
         w.uscale = w.inv_norm;
     }
-    if (update && (hp->num_ns_steps == 0 || unit_rms)) {
+    if (update && (hp->num_ns_steps == 0 || unit_rms || split_update)) {
         const double by = xe * ((bf16 ? 3.0 : 4.0) + 2.0 * psize + (any_ns_out ? 4.0 : 0.0));
         e = timed(ctx, ST_UPDATE, 0.0, by, st,
                   [&] {
