@@ -126,6 +126,8 @@ def _check(lib, mats, hp):
 def test_valid_step_args(lib):
     hp = ms.make_hparams()
     assert _check(lib, [_mat(0), _mat(1, 7168, 2048, ns_out=True)], hp) == (ms.MUON_OK, "")
+    hp_rms = ms.make_hparams(scale_mode=ms.MUON_SCALE_UNIT_RMS)
+    assert _check(lib, [_mat(0), _mat(1, 7168, 2048, ns_out=True)], hp_rms) == (ms.MUON_OK, "")
     assert _check(lib, [], hp)[0] == ms.MUON_OK
 
 
