@@ -218,8 +218,13 @@ const char *muon_last_error(const muon_context *ctx);
 /* One Muon step over `count` matrices (host array mats).  Matrices with the
  * same (rows, cols, param_dtype, grad_dtype) are batched: every stage runs
  * as one grouped launch over all of them.  A matrix whose N_t is all zero
- * gets the decay-only update W_t = (1 - lr wd) W_{t-1}.  Non-finite values
- * propagate (IEEE). */
+ * gets the decay-only update W_t = (1 - lr wd) W_{t-1}.  The result does not
+ * depend on the scale of N_t: any finite nonzero ||N_t|| is applied exactly
+ * (an N_t outside ||N||_F^2 in [2^-40, 2^40] is normalised in double before
+ * the first product).  Non-finite values propagate (IEEE): an Inf or NaN in
+ * N_t makes ||N_t||^2 non-finite (muon_last_norms) and every element of
+ * O'_t and W_t NaN, as the exact Algorithm 1 does (X = N / ||N|| is NaN
+ * where N is infinite, and every product spreads it). */
 muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count,
                       const muon_hparams *hp, void *hip_stream);
 
@@ -259,7 +264,9 @@ muon_status muon_last_norms(muon_context *ctx, double *out, int64_t capacity, in
  * Stage names: "momentum_nesterov", "norm_finalize", "normalize", "gram",
  * "poly", "apply", "apply_update" (the last product with the fused decay and
  * update), "update", "adamw", "import", "export", "unit_rms" (the per-matrix
- * ||X||^2 reduction and scale of the unit-RMS mode). */
+ * ||X||^2 reduction and scale of the unit-RMS mode), "prenormalize" (the bf16
+ * path's normalisation of the matrices whose ||N_t|| lies outside the range
+ * in which the first step folds 1/||N_t|| into its products). */
 typedef struct muon_stage_stats {
     char name[32];
     int64_t launches;

@@ -166,14 +166,47 @@ def _stream_handle(stream):
     return stream.cuda_stream
 
 
+def _on_one_gpu(named):
+    """Raises unless every (name, tensor) is a GPU tensor and all share one device;
+    returns that device's index.  The C ABI takes raw pointers: a host tensor would
+    hand a kernel a host address."""
+    dev = None
+    for name, t in named:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+    return dev.index
+
+
+def _require_f32(named):
+    """Raises unless every (name, tensor) is float32: the C ABI has no dtype field
+    for these buffers, so another dtype would be read and written past its end."""
+    import torch
+    for name, t in named:
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+
+
 def matrix(param, grad, momentum, ns_out=None):
-    """muon_matrix for torch tensors (row-major contiguous, same shape)."""
-    for t in (param, grad, momentum) + ((ns_out,) if ns_out is not None else ()):
+    """muon_matrix for torch tensors (row-major contiguous, same shape, one GPU;
+    momentum and ns_out float32, param and grad float32 or bfloat16)."""
+    named = [("param", param), ("grad", grad), ("momentum", momentum)]
+    if ns_out is not None:
+        named.append(("ns_out", ns_out))
+    for name, t in named:
         if not t.is_contiguous() or t.dim() != 2 or t.shape != param.shape:
             raise ValueError("param, grad, momentum and ns_out must be contiguous 2-D of one shape")
-    return muon_matrix(param.data_ptr(), grad.data_ptr(), momentum.data_ptr(),
-                       ns_out.data_ptr() if ns_out is not None else None,
-                       param.shape[0], param.shape[1], _dtype_code(param), _dtype_code(grad))
+    _require_f32(named[2:])
+    pd, gd = _dtype_code(param), _dtype_code(grad)
+    dev = _on_one_gpu(named)
+    m = muon_matrix(param.data_ptr(), grad.data_ptr(), momentum.data_ptr(),
+                    ns_out.data_ptr() if ns_out is not None else None,
+                    param.shape[0], param.shape[1], pd, gd)
+    m._device = dev
+    return m
 
 
 def _check(lib, ctx, status, what):
@@ -187,6 +220,7 @@ class Context:
 
     def __init__(self, device=0, workspace_cap_bytes=0):
         self.lib = load()
+        self.device = device
         h = ctypes.c_void_p()
         st = self.lib.muon_create(ctypes.byref(h), device, workspace_cap_bytes)
         if st != MUON_OK:
@@ -204,24 +238,49 @@ class Context:
         except Exception:
             pass
 
+    def _check_device(self, items, what):
+        for k, it in enumerate(items):
+            dev = getattr(it, "_device", None)
+            if dev is not None and dev != self.device:
+                raise ValueError(f"{what} {k} lives on cuda:{dev}, the context on cuda:{self.device}")
+
+    def _check_tensors(self, named):
+        if _on_one_gpu(named) != self.device:
+            raise ValueError(f"tensors live on another GPU than the context (cuda:{self.device})")
+
     # The methods below keep the C ABI's names.
     def muon_step(self, mats, hp, stream=None):
+        self._check_device(mats, "matrix")
         arr = (muon_matrix * len(mats))(*mats)
         st = self.lib.muon_step(self.handle, arr, len(mats), ctypes.byref(hp), _stream_handle(stream))
         _check(self.lib, self.handle, st, "muon_step")
 
     def muon_adamw_step(self, tensors, hp, stream=None):
+        self._check_device(tensors, "tensor")
         arr = (muon_adamw_tensor * len(tensors))(*tensors)
         st = self.lib.muon_adamw_step(self.handle, arr, len(tensors), ctypes.byref(hp),
                                       _stream_handle(stream))
         _check(self.lib, self.handle, st, "muon_adamw_step")
 
     def muon_ns_only(self, n_in, x_out, hp, stream=None):
+        named = [("n_in", n_in), ("x_out", x_out)]
+        for name, t in named:
+            if not t.is_contiguous() or t.dim() != 2 or t.shape != n_in.shape:
+                raise ValueError("n_in and x_out must be contiguous 2-D of one shape")
+        _require_f32(named)
+        self._check_tensors(named)
         st = self.lib.muon_ns_only(self.handle, n_in.data_ptr(), x_out.data_ptr(), n_in.shape[0],
                                    n_in.shape[1], ctypes.byref(hp), _stream_handle(stream))
         _check(self.lib, self.handle, st, "muon_ns_only")
 
     def muon_apply_update(self, param, x, hp, stream=None):
+        named = [("param", param), ("x", x)]
+        for name, t in named:
+            if not t.is_contiguous() or t.dim() != 2 or t.shape != param.shape:
+                raise ValueError("param and x must be contiguous 2-D of one shape")
+        _require_f32(named[1:])
+        _dtype_code(param)
+        self._check_tensors(named)
         st = self.lib.muon_apply_update(self.handle, param.data_ptr(), _dtype_code(param), x.data_ptr(),
                                         param.shape[0], param.shape[1], ctypes.byref(hp),
                                         _stream_handle(stream))
@@ -252,12 +311,19 @@ class Context:
 
 
 def adamw_tensor(param, grad, exp_avg, exp_avg_sq):
-    for t in (param, grad, exp_avg, exp_avg_sq):
+    """muon_adamw_tensor for torch tensors (contiguous, equal numel, one GPU;
+    exp_avg and exp_avg_sq float32)."""
+    named = [("param", param), ("grad", grad), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)]
+    for _, t in named:
         if not t.is_contiguous() or t.numel() != param.numel():
             raise ValueError("AdamW tensors must be contiguous with equal numel")
-    return muon_adamw_tensor(param.data_ptr(), grad.data_ptr(), exp_avg.data_ptr(),
-                             exp_avg_sq.data_ptr(), param.numel(), _dtype_code(param),
-                             _dtype_code(grad))
+    _require_f32(named[2:])
+    pd, gd = _dtype_code(param), _dtype_code(grad)
+    dev = _on_one_gpu(named)
+    t = muon_adamw_tensor(param.data_ptr(), grad.data_ptr(), exp_avg.data_ptr(),
+                          exp_avg_sq.data_ptr(), param.numel(), pd, gd)
+    t._device = dev
+    return t
 
 
 def adamw_hparams(lr=0.02, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1):

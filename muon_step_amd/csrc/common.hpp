@@ -66,8 +66,12 @@ struct Work {
     int64_t x_stride;
     int64_t a_stride;
     double *partials;     // per-block sums of N^2
-    double *nrm2;         // per chunk matrix
-    float *inv_norm;      // per chunk matrix: 1/||N||_F (0 when ||N|| == 0)
+    double *nrm2;         // per chunk matrix: ||N||_F^2
+    // per chunk matrix: the factor the bf16 path's first Newton-Schulz step
+    // folds into its epilogues (X_0 = N inv_norm): fl32(1/||N||_F); 1 for a
+    // matrix that the pre-normalisation pass already scaled (prenormalize());
+    // 0 when ||N|| == 0; NaN when ||N||^2 is not finite.
+    float *inv_norm;
     double *call_nrm2;    // per call matrix (indexed by MatDesc::call_index)
     const float *uscale;  // per chunk matrix update scale s (unit-RMS mode), else nullptr
 };
@@ -221,6 +225,20 @@ __device__ __forceinline__ floatx4 join_bf16x4(const u32x2 &h, uint32_t l) {
 // accesses in lgkmcnt).  Every such pointer here points to device memory.
 template <class T> __device__ __forceinline__ __attribute__((address_space(1))) T *as_global(T *p) {
     return (__attribute__((address_space(1))) T *)p;
+}
+
+// Range of ||N||_F^2 inside which the bf16 path keeps X = N through its first
+// Gram and folds 1/||N|| into the epilogues.  Inside it the products of N's
+// entries that make up N N^T stay far inside fp32's normal range for any
+// matrix of up to 2^40 elements (mean square entry >= 2^-80), and the sums
+// far below its maximum.  A matrix outside it (a vanishing momentum, e.g. an
+// expert that received no tokens for hundreds of steps, or a huge one) is
+// normalised first: X = N / ||N||_F computed in double, so the step does not
+// depend on the scale of N (the Frobenius normalisation line of the expanded
+// Algorithm 1, DeepSeek-V4 book ch. 6 section 5).  A non-finite norm is not
+// normalised: it makes the whole output NaN.
+__host__ __device__ inline bool prenormalize(double nrm2) {
+    return (nrm2 > 0.0 && nrm2 < 0x1p-40) || (nrm2 > 0x1p40 && nrm2 <= 1.7976931348623157e308);
 }
 
 // Blocks whose ids the hardware spreads round-robin over the 8 XCDs are

@@ -17,6 +17,8 @@
 //
 // All float arithmetic here is compiled with -ffp-contract=off so every
 // multiply and add rounds once, matching the fp32 bookkeeping reference.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -232,49 +234,67 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc *__res
     if (threadIdx.x == 0) {
         w.nrm2[e] = s;
         w.call_nrm2[descs[e].call_index] = s;
-        // 1/||N||; an all-zero N gives 0, so X = 0 and the update is decay only.
-        w.inv_norm[e] = (s > 0.0) ? static_cast<float>(1.0 / sqrt(s)) : (s == 0.0 ? 0.0f : __builtin_nanf(""));
+        // The first step's fold factor.  An all-zero N gives 0, so X = 0 and
+        // the update is decay only; a non-finite norm gives NaN everywhere
+        // (IEEE propagation of an Inf or NaN in N); a norm outside the fold
+        // range is applied by normalize_kernel instead.
+        float f;
+        if (s == 0.0)
+            f = 0.0f;
+        else if (!(s <= 1.7976931348623157e308))
+            f = __builtin_nanf("");
+        else if (prenormalize(s))
+            f = 1.0f;
+        else
+            f = static_cast<float>(1.0 / sqrt(s));
+        w.inv_norm[e] = f;
     }
 }
 
-// X_0 = N * inv_norm over the padded sp x lp extent (zeros outside s x l), in
-// place: fp32 in xf, or the pair (bf16 hi in xb, 8-bit residual in xl).  The bf16 path runs it only
-// for an empty schedule; otherwise its first step applies inv_norm itself.
-__global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int blocks_per_mat, int rows_per_block) {
+// X_0 = N / ||N||_F over the padded sp x lp extent (zeros outside s x l), in
+// place: fp32 in xf, or the pair (bf16 hi in xb, 8-bit residual in xl).  The
+// factor 1/||N|| is formed in double and each element rounded once, so any
+// finite nonzero norm is applied exactly (in fp32 it could over- or
+// underflow); ||N|| = 0 gives X = 0 and a non-finite norm NaN.  The fp32 path
+// (and the bf16 path with an empty schedule) runs it on every matrix;
+// otherwise the bf16 path folds 1/||N|| into its first step and runs it only
+// on the matrices prenormalize() selects (prenorm_only: the blocks of the
+// others return at once).  Block (e, b) handles padded rows b, b + bpm, ...
+__global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int blocks_per_mat, int prenorm_only) {
     const int64_t e = blockIdx.x / blocks_per_mat;
     const int64_t rb = blockIdx.x % blocks_per_mat;
-    const float inv = w.inv_norm[e];
+    const double s = w.nrm2[e];
+    if (prenorm_only && !prenormalize(s)) return;
+    const double inv = s == 0.0 ? 0.0 : (s <= 1.7976931348623157e308 ? 1.0 / sqrt(s) : __builtin_nan(""));
     const bool split = w.xf == nullptr;
     float *__restrict__ xf = split ? nullptr : w.xf + e * w.x_stride;
     uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb) + e * w.x_stride;
     uint8_t *__restrict__ xl = static_cast<uint8_t *>(w.xl) + e * w.x_stride;
-    const int64_t r0 = rb * rows_per_block;
-    const int64_t r1 = min<int64_t>(g.sp, r0 + rows_per_block);
-    const int64_t cv = g.lp / 4;
-    const int64_t total = (r1 - r0) * cv;
-    for (int64_t t = threadIdx.x; t < total; t += 256) {
-        const int64_t i = r0 + t / cv;
-        const int64_t j = (t % cv) * 4;
-        const int64_t off = i * g.lp + j;
-        floatx4 v = {0.f, 0.f, 0.f, 0.f};
-        if (i < g.s) {
-            floatx4 n;
-            if (split) {
-                // entries past column l of the N pair are never written: mask them
-                n = join_bf16x4(*reinterpret_cast<const u32x2 *>(xh + off), *reinterpret_cast<const uint32_t *>(xl + off));
-            } else {
-                n = *reinterpret_cast<const floatx4 *>(xf + off);
+    for (int64_t i = rb; i < g.sp; i += blocks_per_mat) {
+        for (int64_t j = 4 * static_cast<int64_t>(threadIdx.x); j < g.lp; j += 4 * 256) {
+            const int64_t off = i * g.lp + j;
+            floatx4 v = {0.f, 0.f, 0.f, 0.f};
+            if (i < g.s) {
+                floatx4 n;
+                if (split) {
+                    // entries past column l of the N pair are never written: mask them
+                    n = join_bf16x4(*reinterpret_cast<const u32x2 *>(xh + off),
+                                    *reinterpret_cast<const uint32_t *>(xl + off));
+                } else {
+                    n = *reinterpret_cast<const floatx4 *>(xf + off);
+                }
+                for (int q = 0; q < 4; ++q)
+                    v[q] = (j + q < g.l) ? static_cast<float>(static_cast<double>(n[q]) * inv) : 0.0f;
             }
-            for (int q = 0; q < 4; ++q) v[q] = (j + q < g.l) ? n[q] * inv : 0.0f;
-        }
-        if (split) {
-            u32x2 h;
-            uint32_t l;
-            split_bf16x4(v, &h, &l);
-            *reinterpret_cast<u32x2 *>(xh + off) = h;
-            *reinterpret_cast<uint32_t *>(xl + off) = l;
-        } else {
-            *reinterpret_cast<floatx4 *>(xf + off) = v;
+            if (split) {
+                u32x2 h;
+                uint32_t l;
+                split_bf16x4(v, &h, &l);
+                *reinterpret_cast<u32x2 *>(xh + off) = h;
+                *reinterpret_cast<uint32_t *>(xl + off) = l;
+            } else {
+                *reinterpret_cast<floatx4 *>(xf + off) = v;
+            }
         }
     }
 }
@@ -711,12 +731,11 @@ hipError_t launch_import_n(const float *n_in, const Geom &g, const Work &w, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, hipStream_t st) {
-    int64_t rpb = 65536 / g.lp;
-    if (rpb < 1) rpb = 1;
-    const int bpm = static_cast<int>((g.sp + rpb - 1) / rpb);
+hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, int prenorm_only, hipStream_t st) {
+    // about 16k blocks in all (at least one per matrix, at most one per row)
+    const int bpm = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(g.sp, 16384 / std::max(nmat, 1))));
     hipLaunchKernelGGL(normalize_kernel, dim3(static_cast<unsigned>(static_cast<int64_t>(bpm) * nmat)), dim3(256), 0,
-                       st, g, w, bpm, static_cast<int>(rpb));
+                       st, g, w, bpm, prenorm_only);
     return hipGetLastError();
 }
 

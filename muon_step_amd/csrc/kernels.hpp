@@ -23,7 +23,9 @@ hipError_t launch_norm_finalize(const MatDesc *descs, int nmat, const Work &w, i
                                 hipStream_t st);
 hipError_t launch_import_n(const float *n_in, const Geom &g, const Work &w, hipStream_t st);
 int import_n_blocks(const Geom &g);
-hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, hipStream_t st);
+// X_0 = N / ||N||_F per matrix; prenorm_only: only the matrices whose norm
+// lies outside the bf16 fold range (prenormalize()).
+hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, int prenorm_only, hipStream_t st);
 hipError_t launch_pad_zero(int nmat, const Geom &g, const Work &w, hipStream_t st);
 // s_dev, when non-null, is a device float read in place of s.
 hipError_t launch_update_plain(void *param, int param_bf16, const float *x, int64_t n, float d,
@@ -62,8 +64,11 @@ struct NsStep {
     // scaled by inv_norm^2 and a X + B X by inv_norm (X_0 = N inv_norm).
     int unnormalized;
     // bf16 path, last step: W rows may be staged through LDS (no transpose,
-    // s and l multiples of 256, every parameter 16-byte aligned).
+    // s and l multiples of 256, every parameter and ns_out 16-byte aligned).
     int w_staged;
+    // last step: every parameter and ns_out of the chunk is 16-byte aligned,
+    // so the per-element fused update may move four elements per access.
+    int vec_ok;
 };
 
 // kind: 0 = A = X X^T, 1 = B = bA + cA^2, 2 = X <- aX + BX (or the fused update).

@@ -733,12 +733,14 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::M
 }
 
 // W <- d W - s_scale X' for X' row gi, columns gj .. gj+3 (W row-major with
-// the orientation of X'), and O' = X' when asked.  VEC: the four W elements
-// are 4-aligned and inside the matrix.
+// the orientation of X'), and O' = X' when asked.  The four elements move as
+// one 8- or 16-byte access when they are consecutive in W, inside the matrix
+// and aligned (rows of a multiple of 4 elements, 16-byte aligned parameter and
+// ns_out: NsStep::vec_ok); one by one otherwise.
 template <int PARAM_BF16>
 __device__ __forceinline__ void update_row4(const MatDesc &d, const Geom &g, const NsStep &p, int64_t gi, int64_t gj,
                                             const floatx4 &v) {
-    if (!g.transposed && (g.cols % 4 == 0) && gj + 3 < g.l) {
+    if (p.vec_ok && !g.transposed && (g.cols % 4 == 0) && gj + 3 < g.l) {
         const int64_t widx = gi * g.cols + gj;
         if (PARAM_BF16) {
             auto *pp = as_global(reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(d.param) + widx));

@@ -384,11 +384,11 @@ muon_status hip_fail(muon_context *ctx, hipError_t e, const char *where) {
 
 enum Stage {
     ST_MOMENTUM = 0, ST_FINALIZE, ST_NORMALIZE, ST_GRAM, ST_POLY, ST_APPLY, ST_APPLY_UPDATE, ST_UPDATE,
-    ST_ADAMW, ST_IMPORT, ST_EXPORT, ST_UNIT_RMS, ST_COUNT
+    ST_ADAMW, ST_IMPORT, ST_EXPORT, ST_UNIT_RMS, ST_PRENORM, ST_COUNT
 };
 const char *const kStageNames[ST_COUNT] = {"momentum_nesterov", "norm_finalize", "normalize", "gram", "poly",
                                            "apply", "apply_update", "update", "adamw", "import", "export",
-                                           "unit_rms"};
+                                           "unit_rms", "prenormalize"};
 
 hipError_t take_event(muon_context *ctx, hipEvent_t *ev) {
     if (ctx->ev_used == ctx->ev_pool.size()) {
@@ -555,20 +555,29 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
     // fused into the last product.  Other shapes whose W rows allow 8-wide
     // access run the last step as a plain product plus a separate update
     // pass, which costs less than the per-element fused epilogue there.
-    const bool w_staged = param_bf16 && params_aligned16 && !g.transposed && g.s % muon::kTile == 0 &&
-                          g.l % muon::kTile == 0;
+    const bool w_staged = param_bf16 && params_aligned16 && outs_aligned16 && !g.transposed &&
+                          g.s % muon::kTile == 0 && g.l % muon::kTile == 0;
     const bool split_update = update && !unit_rms && bf16 && !w_staged && params_aligned16 && outs_aligned16 &&
                               (g.transposed ? g.cols % 8 == 0 : g.l % 8 == 0);
     const double xe = static_cast<double>(g.s) * g.l * nmat;
     // bf16 path with a schedule: X stays N and the first step applies 1/||N||
-    // (only the padding needs zeros); otherwise a normalisation pass.
+    // (only the padding needs zeros), except for the matrices whose norm lies
+    // outside the fold range, which a pre-normalisation pass scales first
+    // (its blocks return at once for the others); otherwise a normalisation
+    // pass over every matrix.
     const bool fold = bf16 && hp->num_ns_steps > 0;
     hipError_t e = hipSuccess;
     if (!fold) {
-        e = timed(ctx, ST_NORMALIZE, 0.0, xe * (bf16 ? 6.0 : 8.0), st, [&] { return muon::launch_normalize(nmat, g, w, st); });
-    } else if (g.sp > g.s || g.lp > g.l) {
-        const double pad = (static_cast<double>(g.sp) * g.lp - static_cast<double>(g.s) * g.l) * nmat;
-        e = timed(ctx, ST_NORMALIZE, 0.0, pad * 3.0, st, [&] { return muon::launch_pad_zero(nmat, g, w, st); });
+        e = timed(ctx, ST_NORMALIZE, 0.0, xe * (bf16 ? 6.0 : 8.0), st,
+                  [&] { return muon::launch_normalize(nmat, g, w, 0, st); });
+    } else {
+        if (g.sp > g.s || g.lp > g.l) {
+            const double pad = (static_cast<double>(g.sp) * g.lp - static_cast<double>(g.s) * g.l) * nmat;
+            e = timed(ctx, ST_NORMALIZE, 0.0, pad * 3.0, st, [&] { return muon::launch_pad_zero(nmat, g, w, st); });
+        }
+        // no algorithmic bytes: only matrices with an extreme norm are touched
+        if (e == hipSuccess)
+            e = timed(ctx, ST_PRENORM, 0.0, 0.0, st, [&] { return muon::launch_normalize(nmat, g, w, 1, st); });
     }
     if (e != hipSuccess) return hip_fail(ctx, e, "normalize launch");
     const int psize = param_bf16 ? 2 : 4;
@@ -583,6 +592,7 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
         p.sscale = s;
         p.unnormalized = (fold && it == 0) ? 1 : 0;
         p.w_staged = w_staged ? 1 : 0;
+        p.vec_ok = params_aligned16 && outs_aligned16 ? 1 : 0;
         for (int kind = 0; kind < 3; ++kind) {
             const int stage = kind == 0 ? ST_GRAM : kind == 1 ? ST_POLY : (p.final_update ? ST_APPLY_UPDATE : ST_APPLY);
             double fl = 0, by = 0;

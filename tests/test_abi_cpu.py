@@ -229,3 +229,55 @@ def test_create_without_gpu_reports_device_error(lib):
     assert lib.muon_create(ctypes.byref(h), 0, 0) == ms.MUON_ERR_DEVICE
     assert not h.value
     assert lib.muon_destroy(None) == ms.MUON_OK
+
+
+# ------------------------------------------------------------- binding argument checks
+
+
+def test_binding_rejects_wrong_dtypes_before_any_launch():
+    """The C ABI has no dtype field for momentum, ns_out, exp_avg or exp_avg_sq: a
+    tensor of another dtype must be refused by the binding (a bf16 buffer would be
+    read and written over twice its allocation)."""
+    import torch
+    p = torch.zeros(4, 8, dtype=torch.bfloat16)
+    g = torch.zeros(4, 8, dtype=torch.bfloat16)
+    for bad in (torch.bfloat16, torch.float16, torch.float64):
+        with pytest.raises(TypeError, match="momentum must be float32"):
+            ms.matrix(p, g, torch.zeros(4, 8, dtype=bad))
+        with pytest.raises(TypeError, match="ns_out must be float32"):
+            ms.matrix(p, g, torch.zeros(4, 8), torch.zeros(4, 8, dtype=bad))
+        f = torch.zeros(32)
+        with pytest.raises(TypeError, match="exp_avg must be float32"):
+            ms.adamw_tensor(f, f.clone(), torch.zeros(32, dtype=bad), f.clone())
+        with pytest.raises(TypeError, match="exp_avg_sq must be float32"):
+            ms.adamw_tensor(f, f.clone(), f.clone(), torch.zeros(32, dtype=bad))
+    with pytest.raises(TypeError, match="unsupported dtype"):
+        ms.matrix(torch.zeros(4, 8, dtype=torch.float16), g, torch.zeros(4, 8))
+
+
+def test_binding_rejects_host_tensors_before_any_launch():
+    """A host tensor's data_ptr is a host address: every entry point's tensors must be
+    GPU tensors of the context's device, checked before the library is called."""
+    import torch
+    p = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        ms.matrix(p, p.clone(), torch.zeros(4, 8))
+    f = torch.zeros(32)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        ms.adamw_tensor(f, f.clone(), f.clone(), f.clone())
+    ctx = ms.Context.__new__(ms.Context)   # no device context: the checks come first
+    ctx.lib, ctx.device, ctx.handle = ms.load(), 0, None
+    hp = ms.make_hparams()
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        ctx.muon_ns_only(torch.zeros(4, 8), torch.zeros(4, 8), hp)
+    with pytest.raises(TypeError, match="x_out must be float32"):
+        ctx.muon_ns_only(torch.zeros(4, 8), torch.zeros(4, 8, dtype=torch.bfloat16), hp)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        ctx.muon_apply_update(p, torch.zeros(4, 8), hp)
+    with pytest.raises(ValueError, match="one shape"):
+        ctx.muon_apply_update(p, torch.zeros(8, 4), hp)
+    # a descriptor built on another GPU than the context's
+    m = ms.muon_matrix()
+    m._device = 3
+    with pytest.raises(ValueError, match="cuda:3"):
+        ctx.muon_step([m], hp)
