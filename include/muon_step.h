@@ -41,7 +41,10 @@
 extern "C" {
 #endif
 
-#define MUON_STEP_ABI_VERSION 2
+#define MUON_STEP_ABI_VERSION 3
+
+/* Bytes of the fixed per-GPU device scratch muon_step_noalloc works in. */
+#define MUON_NOALLOC_SCRATCH_BYTES 134217728
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -227,6 +230,24 @@ const char *muon_last_error(const muon_context *ctx);
  * where N is infinite, and every product spreads it). */
 muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count,
                       const muon_hparams *hp, void *hip_stream);
+
+/* For callers that cannot allocate device memory during a step (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * muon_step with the same arguments, results bit-identical to muon_step's,
+ * that allocates nothing.  Its workspace, norm tables and descriptor table
+ * live in a static device array of MUON_NOALLOC_SCRATCH_BYTES (128 MiB)
+ * that every GPU the library runs on holds from muon_create until the
+ * process ends; groups of same-shape matrices are processed in chunks that
+ * fit it.  A call whose matrices cannot fit (one bf16 2048 x 7168 matrix
+ * needs 90 MB; a 4096 x 4096 one does not fit) or that has more than 16384
+ * matrices returns MUON_ERR_OUT_OF_MEMORY before anything is enqueued.
+ * Every call on one GPU shares that GPU's array (across contexts too), and
+ * calls that overlap on one GPU race: order them on one stream or
+ * synchronise.  muon_last_norms reads from the array, so it is valid until
+ * the next muon_step_noalloc on that GPU.  With per-stage timing enabled
+ * (muon_profile_enable) the call may create HIP events. */
+muon_status muon_step_noalloc(muon_context *ctx, const muon_matrix *mats, int64_t count,
+                              const muon_hparams *hp, void *hip_stream);
 
 /* One AdamW step over `count` tensors (host array ts), one launch. */
 muon_status muon_adamw_step(muon_context *ctx, const muon_adamw_tensor *ts, int64_t count,

@@ -33,7 +33,7 @@ EXPORTS = (
     "muon_abi_version", "muon_status_string", "muon_schedule", "muon_check_step_args",
     "muon_check_adamw_args", "muon_workspace_bytes", "muon_create", "muon_destroy",
     "muon_last_error", "muon_step", "muon_adamw_step", "muon_ns_only", "muon_apply_update",
-    "muon_last_norms", "muon_profile_enable", "muon_profile_read",
+    "muon_last_norms", "muon_profile_enable", "muon_profile_read", "muon_step_noalloc",
 )
 
 
@@ -105,6 +105,7 @@ def load(path=LIB_PATH):
         "muon_destroy": (i32, [vp]),
         "muon_last_error": (c.c_char_p, [vp]),
         "muon_step": (i32, [vp, c.POINTER(muon_matrix), i64, c.POINTER(muon_hparams), vp]),
+        "muon_step_noalloc": (i32, [vp, c.POINTER(muon_matrix), i64, c.POINTER(muon_hparams), vp]),
         "muon_adamw_step": (i32, [vp, c.POINTER(muon_adamw_tensor), i64,
                                   c.POINTER(muon_adamw_hparams), vp]),
         "muon_ns_only": (i32, [vp, vp, vp, i64, i64, c.POINTER(muon_hparams), vp]),
@@ -254,6 +255,12 @@ class Context:
         arr = (muon_matrix * len(mats))(*mats)
         st = self.lib.muon_step(self.handle, arr, len(mats), ctypes.byref(hp), _stream_handle(stream))
         _check(self.lib, self.handle, st, "muon_step")
+
+    def muon_step_noalloc(self, mats, hp, stream=None):
+        self._check_device(mats, "matrix")
+        arr = (muon_matrix * len(mats))(*mats)
+        st = self.lib.muon_step_noalloc(self.handle, arr, len(mats), ctypes.byref(hp), _stream_handle(stream))
+        _check(self.lib, self.handle, st, "muon_step_noalloc")
 
     def muon_adamw_step(self, tensors, hp, stream=None):
         self._check_device(tensors, "tensor")

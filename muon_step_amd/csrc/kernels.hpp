@@ -15,6 +15,12 @@ struct AdamwScalars {
 // Newton-Schulz GEMM tile: every padded X dimension is a multiple of this.
 constexpr int kTile = 256;
 
+// ---- fixed scratch of the allocation-free step (noalloc.hip)
+// Size of the static device array; equal to MUON_NOALLOC_SCRATCH_BYTES.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+// Device address of the current device's copy of the array.
+hipError_t scratch_address(void **out);
+
 // ---- elementwise (elementwise.hip)
 int nesterov_blocks_per_mat(const Geom &g, int *rows_per_block, int *tiles_c);
 hipError_t launch_nesterov(const MatDesc *descs, int nmat, const Geom &g, const Work &w, float mu,

@@ -31,6 +31,9 @@ constexpr int64_t kMaxElems = int64_t(1) << 40; // rows * cols
 // products even when bf16 is requested: with so few singular directions the
 // bf16 rounding of X does not average out, and their cost is negligible.
 constexpr int64_t kThinF32Side = 16;
+// Matrices one muon_step_noalloc call may take (its descriptor table is
+// staged through a pinned buffer of this many entries, allocated at creation).
+constexpr int64_t kNoAllocMaxMatrices = 16384;
 
 bool use_bf16(int32_t precision, int64_t s) { return precision == MUON_NS_BF16 && s > kThinF32Side; }
 
@@ -342,6 +345,16 @@ struct muon_context {
     std::vector<unsigned char> mat_cache, adamw_cache;
     hipStream_t last_stream = nullptr;
     int64_t last_count = 0;
+    const double *last_nrm2 = nullptr;  // device: the last step's per-matrix ||N||^2
+    // allocation-free step: this device's copy of the static scratch (from
+    // hipGetSymbolAddress at creation; nullptr if that failed, with the reason
+    // kept in scratch_err) and a pinned staging buffer for its descriptor
+    // table, both set up by muon_create
+    char *scratch = nullptr;
+    std::string scratch_err;
+    void *noalloc_pinned = nullptr;
+    hipEvent_t noalloc_upload_done = nullptr;
+    bool noalloc_upload_recorded = false;
     // per-stage timing
     bool prof_on = false;
     std::vector<hipEvent_t> ev_pool;
@@ -481,11 +494,19 @@ void muon_scalars(const muon_hparams *hp, int64_t rows, int64_t cols, float *d, 
     *s = static_cast<float>(hp->lr * hp->gamma * std::sqrt(static_cast<double>(std::max(rows, cols))));
 }
 
+// Device memory of one muon_step call: the Newton-Schulz workspace, the norm
+// tables (partials | nrm2 | inv_norm) and the per-call norm output.  Either
+// the context's own buffers or the fixed scratch of the allocation-free step.
+struct CallMem {
+    char *ws;
+    char *tabs;
+    double *call_nrm2;
+};
+
 // Work view of a chunk laid out at the workspace base.
-Work chunk_work(muon_context *ctx, const Geom &g, bool bf16, int64_t n, int bpm, size_t call_count) {
-    (void)call_count;
+Work chunk_work(const CallMem &mem, const Geom &g, bool bf16, int64_t n, int bpm) {
     const Layout L = chunk_layout(g, bf16, n);
-    char *base = static_cast<char *>(ctx->ws.p);
+    char *base = mem.ws;
     Work w{};
     w.xf = L.has_xf ? reinterpret_cast<float *>(base + L.xf0) : nullptr;
     w.xf_next = L.has_xf ? reinterpret_cast<float *>(base + L.xf1) : nullptr;
@@ -497,12 +518,12 @@ Work chunk_work(muon_context *ctx, const Geom &g, bool bf16, int64_t n, int bpm,
     w.bb = base + L.bb;
     w.x_stride = g.sp * g.lp;
     w.a_stride = g.sp * g.sp;
-    char *t = static_cast<char *>(ctx->tabs.p);
+    char *t = mem.tabs;
     w.partials = reinterpret_cast<double *>(t);
     const size_t np = align_up(static_cast<size_t>(n) * bpm * sizeof(double));
     w.nrm2 = reinterpret_cast<double *>(t + np);
     w.inv_norm = reinterpret_cast<float *>(t + np + align_up(static_cast<size_t>(n) * sizeof(double)));
-    w.call_nrm2 = static_cast<double *>(ctx->call_nrm2.p);
+    w.call_nrm2 = mem.call_nrm2;
     return w;
 }
 
@@ -627,6 +648,151 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Copies the descriptor table into the fixed scratch through the context's
+// pinned staging buffer (allocated by muon_create), once the previous copy
+// from it has been consumed.  Nothing is allocated.
+muon_status upload_fixed(muon_context *ctx, void *dst, const void *src, size_t n, hipStream_t st) {
+    hipError_t e;
+    if (ctx->noalloc_upload_recorded) {
+        e = hipEventSynchronize(ctx->noalloc_upload_done);
+        if (e != hipSuccess) return hip_fail(ctx, e, "hipEventSynchronize");
+    }
+    std::memcpy(ctx->noalloc_pinned, src, n);
+    e = hipMemcpyAsync(dst, ctx->noalloc_pinned, n, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpyAsync");
+    e = hipEventRecord(ctx->noalloc_upload_done, st);
+    if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
+    ctx->noalloc_upload_recorded = true;
+    return MUON_OK;
+}
+
+// muon_step and muon_step_noalloc.  fixed: every buffer of the call lives in
+// the device's static scratch (descriptor table | per-call norms | norm tables
+// | workspace), the groups are chunked to fit it, and nothing is allocated;
+// otherwise the context's grow-only buffers are used.
+muon_status step_impl(muon_context *ctx, const muon_matrix *mats, int64_t count, const muon_hparams *hp,
+                      void *hip_stream, bool fixed) {
+    if (!ctx) return MUON_ERR_INVALID_ARGUMENT;
+    char msg[512];
+    muon_status s = check_step(mats, count, hp, msg, sizeof msg);
+    if (s != MUON_OK) return fail(ctx, s, "%s", msg);
+    if (count == 0) { ctx->err.clear(); return MUON_OK; }
+    std::vector<GroupPlan> plan;
+    size_t ws = 0, parts = 0;
+    int64_t max_chunk = 0;
+    CallMem mem{};
+    MatDesc *desc_dst = nullptr;
+    if (!fixed) {
+        s = plan_groups(mats, count, hp->ns_precision, ctx->cap, &plan, &ws, &parts, &max_chunk, msg, sizeof msg);
+        if (s != MUON_OK) return fail(ctx, s, "%s", msg);
+    } else {
+        if (!ctx->scratch || !ctx->noalloc_pinned)
+            return fail(ctx, MUON_ERR_DEVICE, "the fixed scratch is not available: %s", ctx->scratch_err.c_str());
+        if (count > kNoAllocMaxMatrices)
+            return fail(ctx, MUON_ERR_OUT_OF_MEMORY, "muon_step_noalloc takes at most %lld matrices per call, got %lld",
+                        (long long)kNoAllocMaxMatrices, (long long)count);
+        const size_t desc_b = align_up(static_cast<size_t>(count) * sizeof(MatDesc));
+        const size_t head = desc_b + align_up(static_cast<size_t>(count) * sizeof(double));
+        const size_t room = muon::kScratchBytes - head;
+        size_t cap = room;
+        for (int tries = 0;; ++tries) {
+            s = plan_groups(mats, count, hp->ns_precision, cap, &plan, &ws, &parts, &max_chunk, msg, sizeof msg);
+            if (s != MUON_OK)
+                return fail(ctx, s, "muon_step_noalloc: %s (the fixed scratch holds %zu bytes)", msg,
+                            static_cast<size_t>(muon::kScratchBytes));
+            const size_t tb = align_up(tabs_bytes(parts, max_chunk));
+            if (ws + tb <= room) {
+                mem.call_nrm2 = reinterpret_cast<double *>(ctx->scratch + desc_b);
+                mem.tabs = ctx->scratch + head;
+                mem.ws = ctx->scratch + head + tb;
+                break;
+            }
+            if (tries == 3 || tb >= room)
+                return fail(ctx, MUON_ERR_OUT_OF_MEMORY,
+                            "muon_step_noalloc: the call needs %zu bytes, the fixed scratch holds %zu", head + ws + tb,
+                            static_cast<size_t>(muon::kScratchBytes));
+            cap = room - tb;
+        }
+        desc_dst = reinterpret_cast<MatDesc *>(ctx->scratch);
+    }
+    DeviceGuard guard(ctx->device);
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (!fixed) {
+        if ((s = ensure(ctx, ctx->ws, ws, "workspace")) != MUON_OK) return s;
+        if ((s = ensure(ctx, ctx->tabs, tabs_bytes(parts, max_chunk), "norm tables")) != MUON_OK) return s;
+        if ((s = ensure(ctx, ctx->call_nrm2, static_cast<size_t>(count) * sizeof(double), "norm output")) != MUON_OK)
+            return s;
+        mem = CallMem{static_cast<char *>(ctx->ws.p), static_cast<char *>(ctx->tabs.p),
+                      static_cast<double *>(ctx->call_nrm2.p)};
+    }
+    // Descriptor table in group order: every chunk is a contiguous slice.
+    std::vector<MatDesc> descs;
+    descs.reserve(static_cast<size_t>(count));
+    for (const GroupPlan &gp : plan)
+        for (int64_t i : gp.members) {
+            MatDesc d{};
+            d.param = mats[i].param;
+            d.grad = mats[i].grad;
+            d.mom = mats[i].momentum;
+            d.ns_out = mats[i].ns_out;
+            d.call_index = i;
+            descs.push_back(d);
+        }
+    const size_t desc_bytes = descs.size() * sizeof(MatDesc);
+    if (fixed) {
+        s = upload_fixed(ctx, desc_dst, descs.data(), desc_bytes, st);
+        if (s != MUON_OK) return s;
+    } else {
+        s = upload(ctx, ctx->mat_desc, ctx->mat_cache, descs.data(), desc_bytes, st, "matrix descriptors");
+        if (s != MUON_OK) return s;
+        desc_dst = static_cast<MatDesc *>(ctx->mat_desc.p);
+    }
+    const MatDesc *ddev = desc_dst;
+    const float mu = static_cast<float>(hp->momentum);
+    size_t pos = 0;
+    for (const GroupPlan &gp : plan) {
+        const bool bf16 = gp.bf16;
+        float d = 0.f, sc = 0.f;
+        muon_scalars(hp, gp.g.rows, gp.g.cols, &d, &sc);
+        const int64_t n_all = static_cast<int64_t>(gp.members.size());
+        for (int64_t c0 = 0; c0 < n_all; c0 += gp.chunk) {
+            const int n = static_cast<int>(std::min<int64_t>(gp.chunk, n_all - c0));
+            const MatDesc *dd = ddev + pos + c0;
+            bool vec_ok = true, params_aligned = true, outs_aligned = true;
+            for (int k = 0; k < n; ++k) {
+                const muon_matrix &m = mats[gp.members[c0 + k]];
+                vec_ok = vec_ok && aligned16(m.momentum) && aligned16(m.grad);
+                params_aligned = params_aligned && aligned16(m.param);
+                outs_aligned = outs_aligned && (!m.ns_out || aligned16(m.ns_out));
+            }
+            bool any_out = false;
+            for (int k = 0; k < n; ++k) any_out = any_out || mats[gp.members[c0 + k]].ns_out != nullptr;
+            Work w = chunk_work(mem, gp.g, bf16, n, gp.bpm);
+            const double elems = static_cast<double>(gp.g.rows) * gp.g.cols * n;
+            const double gsz = gp.grad_dtype == MUON_BF16 ? 2.0 : 4.0;
+            // M read and written (8), N written: fp32 (4) or hi + residual (3)
+            hipError_t e = timed(ctx, ST_MOMENTUM, 0.0, elems * (gsz + (bf16 ? 11.0 : 12.0)), st, [&] {
+                return muon::launch_nesterov(dd, n, gp.g, w, mu, hp->nesterov, gp.grad_dtype == MUON_BF16, vec_ok,
+                                             st);
+            });
+            if (e != hipSuccess) return hip_fail(ctx, e, "momentum launch");
+            e = timed(ctx, ST_FINALIZE, 0.0, static_cast<double>(n) * gp.bpm * 8.0, st,
+                      [&] { return muon::launch_norm_finalize(dd, n, w, gp.bpm, st); });
+            if (e != hipSuccess) return hip_fail(ctx, e, "norm launch");
+            s = run_ns(ctx, dd, n, gp.g, w, bf16, hp, true, gp.param_dtype == MUON_BF16, any_out, d, sc, st,
+                       params_aligned, gp.bpm, outs_aligned);
+            if (s != MUON_OK) return s;
+        }
+        pos += static_cast<size_t>(n_all);
+    }
+    ctx->last_stream = st;
+    ctx->last_count = count;
+    ctx->last_nrm2 = mem.call_nrm2;
+    ctx->err.clear();
+    return MUON_OK;
+}
+
+
 }  // namespace
 
 // ===================================================================== C ABI
@@ -706,9 +872,30 @@ muon_status muon_create(muon_context **out, int32_t hip_device, size_t workspace
     ctx->device = hip_device;
     ctx->cap = workspace_cap_bytes;
     DeviceGuard guard(hip_device);
-    if (hipEventCreateWithFlags(&ctx->upload_done, hipEventDisableTiming) != hipSuccess) {
+    if (hipEventCreateWithFlags(&ctx->upload_done, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ctx->noalloc_upload_done, hipEventDisableTiming) != hipSuccess) {
+        (void)hipGetLastError();
+        if (ctx->upload_done) (void)hipEventDestroy(ctx->upload_done);
         delete ctx;
         return MUON_ERR_DEVICE;
+    }
+    // The allocation-free step's memory: this device's copy of the static
+    // scratch (its address, with this device current) and the pinned staging
+    // of its descriptor table.  A failure here only disables that entry point.
+    void *sp = nullptr;
+    hipError_t e = muon::scratch_address(&sp);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        ctx->scratch_err = std::string("hipGetSymbolAddress: ") + hipGetErrorString(e);
+    } else {
+        ctx->scratch = static_cast<char *>(sp);
+        e = hipHostMalloc(&ctx->noalloc_pinned, static_cast<size_t>(kNoAllocMaxMatrices) * sizeof(MatDesc),
+                          hipHostMallocDefault);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            ctx->noalloc_pinned = nullptr;
+            ctx->scratch_err = std::string("hipHostMalloc: ") + hipGetErrorString(e);
+        }
     }
     *out = ctx;
     return MUON_OK;
@@ -721,7 +908,9 @@ muon_status muon_destroy(muon_context *ctx) {
     for (DevBuf *b : {&ctx->ws, &ctx->tabs, &ctx->call_nrm2, &ctx->mat_desc, &ctx->adamw_desc})
         if (b->p) (void)hipFree(b->p);
     if (ctx->pinned) (void)hipHostFree(ctx->pinned);
+    if (ctx->noalloc_pinned) (void)hipHostFree(ctx->noalloc_pinned);
     if (ctx->upload_done) (void)hipEventDestroy(ctx->upload_done);
+    if (ctx->noalloc_upload_done) (void)hipEventDestroy(ctx->noalloc_upload_done);
     for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
     delete ctx;
     return MUON_OK;
@@ -731,80 +920,12 @@ const char *muon_last_error(const muon_context *ctx) { return ctx ? ctx->err.c_s
 
 muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count, const muon_hparams *hp,
                       void *hip_stream) {
-    if (!ctx) return MUON_ERR_INVALID_ARGUMENT;
-    char msg[512];
-    muon_status s = check_step(mats, count, hp, msg, sizeof msg);
-    if (s != MUON_OK) return fail(ctx, s, "%s", msg);
-    if (count == 0) { ctx->err.clear(); return MUON_OK; }
-    std::vector<GroupPlan> plan;
-    size_t ws = 0, parts = 0;
-    int64_t max_chunk = 0;
-    s = plan_groups(mats, count, hp->ns_precision, ctx->cap, &plan, &ws, &parts, &max_chunk, msg, sizeof msg);
-    if (s != MUON_OK) return fail(ctx, s, "%s", msg);
-    DeviceGuard guard(ctx->device);
-    hipStream_t st = static_cast<hipStream_t>(hip_stream);
-    if ((s = ensure(ctx, ctx->ws, ws, "workspace")) != MUON_OK) return s;
-    if ((s = ensure(ctx, ctx->tabs, tabs_bytes(parts, max_chunk), "norm tables")) != MUON_OK) return s;
-    if ((s = ensure(ctx, ctx->call_nrm2, static_cast<size_t>(count) * sizeof(double), "norm output")) != MUON_OK)
-        return s;
-    // Descriptor table in group order: every chunk is a contiguous slice.
-    std::vector<MatDesc> descs;
-    descs.reserve(static_cast<size_t>(count));
-    for (const GroupPlan &gp : plan)
-        for (int64_t i : gp.members) {
-            MatDesc d{};
-            d.param = mats[i].param;
-            d.grad = mats[i].grad;
-            d.mom = mats[i].momentum;
-            d.ns_out = mats[i].ns_out;
-            d.call_index = i;
-            descs.push_back(d);
-        }
-    s = upload(ctx, ctx->mat_desc, ctx->mat_cache, descs.data(), descs.size() * sizeof(MatDesc), st,
-               "matrix descriptors");
-    if (s != MUON_OK) return s;
-    const MatDesc *ddev = static_cast<const MatDesc *>(ctx->mat_desc.p);
-    const float mu = static_cast<float>(hp->momentum);
-    size_t pos = 0;
-    for (const GroupPlan &gp : plan) {
-        const bool bf16 = gp.bf16;
-        float d = 0.f, sc = 0.f;
-        muon_scalars(hp, gp.g.rows, gp.g.cols, &d, &sc);
-        const int64_t n_all = static_cast<int64_t>(gp.members.size());
-        for (int64_t c0 = 0; c0 < n_all; c0 += gp.chunk) {
-            const int n = static_cast<int>(std::min<int64_t>(gp.chunk, n_all - c0));
-            const MatDesc *dd = ddev + pos + c0;
-            bool vec_ok = true, params_aligned = true, outs_aligned = true;
-            for (int k = 0; k < n; ++k) {
-                const muon_matrix &m = mats[gp.members[c0 + k]];
-                vec_ok = vec_ok && aligned16(m.momentum) && aligned16(m.grad);
-                params_aligned = params_aligned && aligned16(m.param);
-                outs_aligned = outs_aligned && (!m.ns_out || aligned16(m.ns_out));
-            }
-            bool any_out = false;
-            for (int k = 0; k < n; ++k) any_out = any_out || mats[gp.members[c0 + k]].ns_out != nullptr;
-            Work w = chunk_work(ctx, gp.g, bf16, n, gp.bpm, count);
-            const double elems = static_cast<double>(gp.g.rows) * gp.g.cols * n;
-            const double gsz = gp.grad_dtype == MUON_BF16 ? 2.0 : 4.0;
-            // M read and written (8), N written: fp32 (4) or hi + residual (3)
-            hipError_t e = timed(ctx, ST_MOMENTUM, 0.0, elems * (gsz + (bf16 ? 11.0 : 12.0)), st, [&] {
-                return muon::launch_nesterov(dd, n, gp.g, w, mu, hp->nesterov, gp.grad_dtype == MUON_BF16, vec_ok,
-                                             st);
-            });
-            if (e != hipSuccess) return hip_fail(ctx, e, "momentum launch");
-            e = timed(ctx, ST_FINALIZE, 0.0, static_cast<double>(n) * gp.bpm * 8.0, st,
-                      [&] { return muon::launch_norm_finalize(dd, n, w, gp.bpm, st); });
-            if (e != hipSuccess) return hip_fail(ctx, e, "norm launch");
-            s = run_ns(ctx, dd, n, gp.g, w, bf16, hp, true, gp.param_dtype == MUON_BF16, any_out, d, sc, st,
-                       params_aligned, gp.bpm, outs_aligned);
-            if (s != MUON_OK) return s;
-        }
-        pos += static_cast<size_t>(n_all);
-    }
-    ctx->last_stream = st;
-    ctx->last_count = count;
-    ctx->err.clear();
-    return MUON_OK;
+    return step_impl(ctx, mats, count, hp, hip_stream, false);
+}
+
+muon_status muon_step_noalloc(muon_context *ctx, const muon_matrix *mats, int64_t count, const muon_hparams *hp,
+                              void *hip_stream) {
+    return step_impl(ctx, mats, count, hp, hip_stream, true);
 }
 
 muon_status muon_ns_only(muon_context *ctx, const float *n_in, float *x_out, int64_t rows, int64_t cols,
@@ -835,7 +956,9 @@ muon_status muon_ns_only(muon_context *ctx, const float *n_in, float *x_out, int
     s = upload(ctx, ctx->mat_desc, ctx->mat_cache, &d, sizeof d, st, "matrix descriptors");
     if (s != MUON_OK) return s;
     const MatDesc *ddev = static_cast<const MatDesc *>(ctx->mat_desc.p);
-    Work w = chunk_work(ctx, g, bf16, 1, nb_blocks, 1);
+    Work w = chunk_work(CallMem{static_cast<char *>(ctx->ws.p), static_cast<char *>(ctx->tabs.p),
+                                static_cast<double *>(ctx->call_nrm2.p)},
+                        g, bf16, 1, nb_blocks);
     const double elems = static_cast<double>(rows) * cols;
     hipError_t e = timed(ctx, ST_IMPORT, 0.0, elems * 8.0, st, [&] { return muon::launch_import_n(n_in, g, w, st); });
     if (e != hipSuccess) return hip_fail(ctx, e, "import launch");
@@ -848,6 +971,7 @@ muon_status muon_ns_only(muon_context *ctx, const float *n_in, float *x_out, int
     if (e != hipSuccess) return hip_fail(ctx, e, "export launch");
     ctx->last_stream = st;
     ctx->last_count = 1;
+    ctx->last_nrm2 = w.call_nrm2;
     ctx->err.clear();
     return MUON_OK;
 }
@@ -952,7 +1076,7 @@ muon_status muon_last_norms(muon_context *ctx, double *out, int64_t capacity, in
     DeviceGuard guard(ctx->device);
     hipError_t e = hipStreamSynchronize(ctx->last_stream);
     if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamSynchronize");
-    e = hipMemcpy(out, ctx->call_nrm2.p, static_cast<size_t>(n) * sizeof(double), hipMemcpyDeviceToHost);
+    e = hipMemcpy(out, ctx->last_nrm2, static_cast<size_t>(n) * sizeof(double), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy");
     return MUON_OK;
 }
