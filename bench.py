@@ -192,6 +192,89 @@ def moe16b_step(args):
         "stage_ms_per_step": breakdown}), flush=True)
 
 
+def workload_step(args):
+    """Times one Muon step over a listed workload (the dense block: 4 x 4096^2,
+    2 x 4096x14336, 14336x4096; or the aspect-ratio set: 1024x16384, 16384x1024,
+    7168^2, 512x32768 with pre-filled momentum), all matrices in one call, and
+    prints one JSON line of its own: ms/step, NS TFLOP/s on the algorithmic
+    count and its fraction of the bf16 peak, per-stage times and the
+    elementwise kernels' GB/s."""
+    import torch
+
+    import muon_step_amd as ms
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    specs = list(wl.matrices)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.base_seed)
+    log(f"generating {wl.name}: {len(specs)} matrices")
+    by_shape = {}
+    for i, sp in enumerate(specs):
+        by_shape.setdefault((sp.rows, sp.cols), []).append(i)
+    grads, moms = [None] * len(specs), [None] * len(specs)
+    for (rows, cols), ids in by_shape.items():
+        g = synth.spectral_grad_torch(rows, cols, len(ids), gen, "cuda")
+        pf = [i for i in ids if specs[i].prefill_momentum]
+        gp = synth.spectral_grad_torch(rows, cols, len(pf), gen, "cuda") if pf else None
+        for k, i in enumerate(ids):
+            grads[i] = g[k]
+        for k, i in enumerate(pf):
+            moms[i] = gp[k].float()
+    params = [(torch.randn(sp.rows, sp.cols, generator=gen, device="cuda") * synth.gen.PARAM_STD).to(torch.bfloat16)
+              for sp in specs]
+    moms = [m if m is not None else torch.zeros(sp.rows, sp.cols, device="cuda") for sp, m in zip(specs, moms)]
+    mats = [ms.matrix(params[i], grads[i], moms[i]) for i in range(len(specs))]
+    hp = ms.make_hparams(lr=0.02, momentum=0.95, weight_decay=0.1, gamma=0.2, nesterov=True,
+                         ns_precision=ms.MUON_NS_BF16,
+                         scale_mode=ms.MUON_SCALE_UNIT_RMS if args.scale_mode == "unit_rms" else ms.MUON_SCALE_SQRT_MAX)
+    ctx = ms.Context(0)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        ctx.muon_step(mats, hp, stream)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    ctx.muon_profile_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        ctx.muon_step(mats, hp, stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    stages = ctx.muon_profile_read()
+    ctx.close()
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+    for name, st in stages.items():
+        rate = (f"{st['flops'] / st['total_ms'] / 1e9:8.1f} TFLOP/s" if st["flops"] else
+                f"{st['bytes'] / st['total_ms'] / 1e6:8.1f} GB/s" if st["total_ms"] else "")
+        log(f"  {name:18s} launches {st['launches']:5d}  total/step {st['total_ms'] / args.steps:9.3f} ms  {rate}")
+    ns_ms = sum(stages[k]["total_ms"] for k in NS_STAGES if k in stages)
+    ns_flops = sum(stages[k]["flops"] for k in NS_STAGES if k in stages)
+    ns_tflops = ns_flops / ns_ms / 1e9 if ns_ms else 0.0
+    dense = sum(10 * 2 * (2 * max(sp.rows, sp.cols) * min(sp.rows, sp.cols) ** 2 + min(sp.rows, sp.cols) ** 3)
+                for sp in specs)
+    elementwise = {}
+    for k in ("momentum_nesterov", "normalize", "unit_rms", "update"):
+        if k in stages and stages[k]["total_ms"] and stages[k]["bytes"]:
+            gbs = stages[k]["bytes"] / stages[k]["total_ms"] / 1e6
+            elementwise[k] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                              "ms_per_step": round(stages[k]["total_ms"] / args.steps, 4)}
+    print(json.dumps({
+        "metric": f"Muon optimizer steps/sec + NS TFLOP/s (% bf16 MFMA peak), {wl.name}",
+        "value": round(1000.0 / ms_per_step, 4), "unit": "steps/s", "ms_per_step": round(ms_per_step, 3),
+        "steps": args.steps, "warmup": args.warmup, "n_gpus": 1, "dtype": "bf16",
+        "data": "synthetic (seeded low-rank-plus-noise bf16 gradients, N(0,0.02) bf16 params)",
+        "config": {"workload": wl.name, "matrices": [[sp.rows, sp.cols] for sp in specs], "ns_steps": 10,
+                   "scale_mode": args.scale_mode},
+        "ns_tflops": round(ns_tflops, 2), "ns_frac_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4),
+        "ns_dense_equivalent_tflops": round(dense * args.steps / ns_ms / 1e9, 2) if ns_ms else None,
+        "ns_ms_per_step": round(ns_ms / args.steps, 3),
+        "elementwise": elementwise,
+        "stage_ms_per_step": {k: round(v["total_ms"] / args.steps, 4) for k, v in stages.items()}}), flush=True)
+
+
 def cpu_baseline(rows, cols, count, scale_mode="sqrt_max"):
     """The oracle as it stands on one matrix of the batch; scaled to one step."""
     import numpy as np
@@ -223,8 +306,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB copy (reference for the HBM byte counters)")
     ap.add_argument("--workload", default="moe_256x2048x7168_bf16",
-                    choices=["moe_256x2048x7168_bf16", "moe16b"],
-                    help="moe16b: time the full 16B-MoE optimizer step instead (own JSON line)")
+                    choices=["moe_256x2048x7168_bf16", "moe16b", "dense_block_bf16", "aspect_stress_bf16"],
+                    help="moe16b: time the full 16B-MoE optimizer step instead; dense_block_bf16, "
+                         "aspect_stress_bf16: one step over that matrix set (each its own JSON line)")
     ap.add_argument("--workspace-gib", type=int, default=64, help="NS workspace cap for --workload moe16b")
     ap.add_argument("--scale-mode", default="sqrt_max", choices=["sqrt_max", "unit_rms"],
                     help="update scale: sqrt(max(n,m))*gamma (DeepSeek-V4) or the unit-RMS mode")
@@ -244,6 +328,9 @@ def main():
         sys.exit(2)
     if args.workload == "moe16b":
         moe16b_step(args)
+        return
+    if args.workload in ("dense_block_bf16", "aspect_stress_bf16"):
+        workload_step(args)
         return
 
     import torch
@@ -316,7 +403,7 @@ def main():
                 "bytes_per_launch": dom["bytes"] / dom["launches"], "avg_launch_ms": round(avg_ms, 4)}
     elementwise = {}
     for k in ("momentum_nesterov", "normalize", "unit_rms", "update"):
-        if k in stages and stages[k]["total_ms"]:
+        if k in stages and stages[k]["total_ms"] and stages[k]["bytes"]:
             gbs = stages[k]["bytes"] / stages[k]["total_ms"] / 1e6
             elementwise[k] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                               "ms_per_step": round(stages[k]["total_ms"] / args.steps, 4)}

@@ -74,6 +74,10 @@ struct Work {
     float *inv_norm;
     double *call_nrm2;    // per call matrix (indexed by MatDesc::call_index)
     const float *uscale;  // per chunk matrix update scale s (unit-RMS mode), else nullptr
+    // split-K Gram / A^2 (bf16 path): the fp32 partial product of every
+    // (matrix, tile, K range), 256 x 256 values each, in the lane-major order
+    // the product kernel stores them; nullptr when the chunk splits no product
+    float *kpart;
 };
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {

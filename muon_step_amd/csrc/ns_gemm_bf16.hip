@@ -37,6 +37,8 @@
 // a bf16 W brings W's rows by DMA too).  K loops stop at the true length
 // rounded to 128 (the padding is zero).  Block ids are renumbered so one
 // matrix's tiles share an XCD (and its L2).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -509,17 +511,53 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
     }
 }
 
+// The 128 x 64 output block (block row wm, block column wn of the tile) that
+// wave `wave` owns: row-major over the wave grid, or on a diagonal tile the
+// permuted order of CfgDiag.
+template <class C> __device__ __forceinline__ void wave_block(bool diag, int wave, int *wm, int *wn) {
+    *wm = diag ? static_cast<int>((CfgDiag::WM_OF >> wave) & 1) : wave / C::WAVES_N;
+    *wn = diag ? static_cast<int>((CfgDiag::WN_OF >> (2 * wave)) & 3) : wave % C::WAVES_N;
+}
+
+// Split-K partial of one (matrix, tile, K range): 256 x 256 fp32, stored as
+// the accumulators lie, wave by wave, then accumulator group j = (mi NI + ni)
+// 4 + c4 (four values), then lane: every store moves 1 KB of consecutive
+// bytes.  sym_reduce_kernel reads the same order back.
+constexpr int KPART_VALUES = 256 * 256;
+template <class C>
+__device__ __forceinline__ void store_kpart(const floatx16 (&acc)[C::MI][C::NI], float *dst, int wave, int lane) {
+    floatx4 *base = reinterpret_cast<floatx4 *>(dst) + wave * (C::MI * C::NI * 4 * 64) + lane;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                floatx4 v;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = acc[mi][ni][4 * c4 + q];
+                *as_global(base + ((mi * C::NI + ni) * 4 + c4) * 64) = v;
+            }
+}
+
 template <class C, int KIND>
 __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep p,
                                                                           int64_t tiles_per_mat, int64_t nblocks) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t L = xcd_swizzle(blockIdx.x, nblocks);
-    const int64_t e = L / tiles_per_mat;
+    // split-K: workgroups of one matrix and one K range are consecutive (they
+    // read the same K slab of the operand)
+    const int splits = KIND == GRAM ? p.gram_splits : p.poly_splits;
+    const int units = KIND == GRAM ? p.gram_units : p.poly_units;
+    const int64_t e = L / (tiles_per_mat * splits);
+    const int64_t rem = L % (tiles_per_mat * splits);
+    const int ks = static_cast<int>(rem / tiles_per_mat);
+    const int64_t t = rem % tiles_per_mat;
     int ti, tj;
-    tri_decode(L % tiles_per_mat, &ti, &tj);
+    tri_decode(t, &ti, &tj);
     const bool diag = ti == tj;
-    const int wm = diag ? static_cast<int>((CfgDiag::WM_OF >> wave) & 1) : wave / C::WAVES_N;
-    const int wn = diag ? static_cast<int>((CfgDiag::WN_OF >> (2 * wave)) & 3) : wave % C::WAVES_N;
+    int wm, wn;
+    wave_block<C>(diag, wave, &wm, &wn);
 
     // P supplies output rows (tile ti), Q output columns (tile tj); both are
     // rows of X (GRAM) or of the symmetric A (POLY), K-contiguous.
@@ -546,6 +584,12 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
         src.p = a + static_cast<int64_t>(ti) * C::BM * src.ld_p;
         src.q = a + static_cast<int64_t>(tj) * C::BN * src.ld_q;
     }
+    // this workgroup's K range (the whole extent when the product is not split;
+    // ranges are multiples of 128, as the loop runs stages in pairs)
+    const int64_t k0 = static_cast<int64_t>(ks) * units * 2 * C::BK;
+    const int64_t k1 = splits > 1 ? min(kdim, k0 + static_cast<int64_t>(units) * 2 * C::BK) : kdim;
+    src.p += k0 * 2;
+    src.q += k0 * 2;
 
     floatx16 acc[C::MI][C::NI];
 #pragma unroll
@@ -554,14 +598,17 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
         for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+    // POLY's epilogue rows of A are requested under the last K stage; a split
+    // product has no epilogue of its own (sym_reduce_kernel forms B)
     auto pre_last = [&] {
         if constexpr (KIND == POLY)
-            dma_bf16_rows<C>(epi_area<0>(wave),
-                             poly_a_rows(g, w, e, static_cast<int64_t>(ti) * C::BM + wm * C::WM,
-                                         static_cast<int64_t>(tj) * C::BN + wn * C::WN),
-                             g.sp * 2, lane);
+            if (splits == 1)
+                dma_bf16_rows<C>(epi_area<0>(wave),
+                                 poly_a_rows(g, w, e, static_cast<int64_t>(ti) * C::BM + wm * C::WM,
+                                             static_cast<int64_t>(tj) * C::BN + wn * C::WN),
+                                 g.sp * 2, lane);
     };
-    const int nk = static_cast<int>(kdim / C::BK);
+    const int nk = static_cast<int>((k1 - k0) / C::BK);
     if (diag)
         main_loop<CfgDiag, KIND>(acc, src, nk, wave, wm, wn, lane, pre_last);
     else if (__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(ti) * C::BM + wm * C::WM >= g.s)))
@@ -569,12 +616,80 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
     else
         main_loop<C, KIND>(acc, src, nk, wave, wm, wn, lane, pre_last);
 
+    if (splits > 1) {
+        store_kpart<C>(acc, w.kpart + ((e * tiles_per_mat + t) * splits + ks) * KPART_VALUES, wave, lane);
+        return;
+    }
+
     // acc[mi][ni][4*c4 + q] holds output row wm*WM + mi*32 + lane%32, column
     // wn*WN + ni*32 + 8*c4 + 4*(lane/32) + q of the tile.
     wait_lgkm0();
     stage_barrier();  // every wave is done with the operand ring
     char *const area[2] = {epi_area<0>(wave), epi_area<1>(wave)};
     sym_epilogue<C, KIND>(acc, g, w, p, e, ti, tj, wm, wn, area, lane);
+}
+
+// Split-K Gram / A^2: sums the K ranges' partials of one (matrix, tile) in
+// range order (fixed, so the result is deterministic) and finishes them as
+// sym_epilogue does: GRAM writes A = sum (times inv_norm^2 on the bf16 path's
+// first step), POLY writes B = b A + c sum (b and c times inv_norm on that
+// step) with A read back in bf16; both in bf16, with the mirrored element
+// for off-diagonal blocks.  Blocks of a diagonal tile above its diagonal were
+// not computed and are skipped.  Thread (item) = one partial float4: wave,
+// accumulator group and lane, as store_kpart laid them out; 64 blocks of 256
+// threads per tile.
+template <int KIND>
+__global__ __launch_bounds__(256) void sym_reduce_kernel(Geom g, Work w, NsStep p, int64_t tiles_per_mat) {
+    using C = Cfg;
+    const int64_t tile = blockIdx.x / 64;  // matrix * tiles_per_mat + tile of the matrix
+    const int item = static_cast<int>(blockIdx.x % 64) * 256 + threadIdx.x;
+    const int64_t e = tile / tiles_per_mat;
+    int ti, tj;
+    tri_decode(tile % tiles_per_mat, &ti, &tj);
+    const int splits = KIND == GRAM ? p.gram_splits : p.poly_splits;
+    const floatx4 *src = reinterpret_cast<const floatx4 *>(w.kpart) + tile * splits * (KPART_VALUES / 4) + item;
+    floatx4 sum = src[0];
+    for (int k = 1; k < splits; ++k) {
+        const floatx4 v = src[static_cast<int64_t>(k) * (KPART_VALUES / 4)];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum[q] += v[q];
+    }
+    const int wave = item >> 11, j = (item >> 6) & 31, lane = item & 63;
+    const int mi = j / (C::NI * 4), ni = (j / 4) % C::NI, c4 = j % 4;
+    const bool diag = ti == tj;
+    int wm, wn;
+    wave_block<C>(diag, wave, &wm, &wn);
+    const int brow = wm * C::MI + mi, bcol = wn * C::NI + ni;  // 32 x 32 blocks of the tile
+    if (diag && brow < bcol) return;
+    const int64_t row = static_cast<int64_t>(ti) * C::BM + wm * C::WM + mi * 32 + (lane & 31);
+    const int64_t col = static_cast<int64_t>(tj) * C::BN + wn * C::WN + ni * 32 + 8 * c4 + 4 * (lane >> 5);
+    const int64_t ld = g.sp;
+    const float inv = p.unnormalized ? w.inv_norm[e] : 1.0f;
+    float v[4];
+    if constexpr (KIND == GRAM) {
+        const float gscale = inv * inv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = sum[q] * gscale;
+    } else {
+        const float pb = p.b * inv, pc = p.c * inv;
+        const u32x2 a2 = *as_global(reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(w.ab) +
+                                                                   e * w.a_stride + row * ld + col));
+        const float a4[4] = {__uint_as_float(a2[0] << 16), __uint_as_float(a2[0] & 0xffff0000u),
+                             __uint_as_float(a2[1] << 16), __uint_as_float(a2[1] & 0xffff0000u)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(pb, a4[q], pc * sum[q]);
+    }
+    uint16_t *dst = static_cast<uint16_t *>(KIND == GRAM ? w.ab : w.bb) + e * w.a_stride;
+    u32x2 pk;
+    pk[0] = pack_bf16x2(v[0], v[1]);
+    pk[1] = pack_bf16x2(v[2], v[3]);
+    *as_global(reinterpret_cast<u32x2 *>(dst + row * ld + col)) = pk;
+    // the mirror: every block of an off-diagonal tile and the blocks strictly
+    // below the diagonal of a diagonal tile (a diagonal block holds both halves)
+    if (!diag || brow > bcol) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) as_global(dst)[(col + q) * ld + row] = float_to_bf16_bits(v[q]);
+    }
 }
 
 // --------------------------------------------------------------------- a X + B X
@@ -969,6 +1084,18 @@ __global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__r
 
 }  // namespace bf16path
 
+int ns_sym_splits(int64_t tiles_w, int64_t units, int64_t max_splits, int *units_per_split) {
+    int64_t splits = 1;
+    if (tiles_w > 0 && tiles_w < 128) splits = std::min<int64_t>(std::min<int64_t>(256 / tiles_w, units / 4), max_splits);
+    if (splits < 2) {
+        *units_per_split = static_cast<int>(units);
+        return 1;
+    }
+    const int64_t ups = (units + splits - 1) / splits;
+    *units_per_split = static_cast<int>(ups);
+    return static_cast<int>((units + ups - 1) / ups);
+}
+
 hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const Geom &g, const Work &w,
                                 const NsStep &p, hipStream_t st) {
     using namespace bf16path;
@@ -976,12 +1103,20 @@ hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const 
         using C = Cfg;
         const int64_t nt = g.sp / C::BM;
         const int64_t tiles = nt * (nt + 1) / 2;
-        const int64_t nblocks = tiles * nmat;
+        const int splits = kind == GRAM ? p.gram_splits : p.poly_splits;
+        const int64_t nblocks = tiles * nmat * splits;
         const dim3 grid(static_cast<unsigned>(nblocks)), block(C::NT);
         if (kind == GRAM)
             ns_sym_kernel<C, GRAM><<<grid, block, 0, st>>>(g, w, p, tiles, nblocks);
         else
             ns_sym_kernel<C, POLY><<<grid, block, 0, st>>>(g, w, p, tiles, nblocks);
+        if (splits > 1) {
+            const dim3 rgrid(static_cast<unsigned>(tiles * nmat * 64));
+            if (kind == GRAM)
+                sym_reduce_kernel<GRAM><<<rgrid, dim3(256), 0, st>>>(g, w, p, tiles);
+            else
+                sym_reduce_kernel<POLY><<<rgrid, dim3(256), 0, st>>>(g, w, p, tiles);
+        }
         return hipGetLastError();
     }
     const int64_t tiles = (g.sp / Cfg::BM) * (g.lp / Cfg::BN);

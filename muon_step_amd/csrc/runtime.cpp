@@ -221,29 +221,69 @@ Geom make_geom(int64_t rows, int64_t cols) {
     return g;
 }
 
+// Split-K of the bf16 Gram and A^2 products of a group of `group_n` matrices
+// of geometry g (all 1 on the fp32 path).
+struct Splits {
+    int gram = 1, gram_units = 0, poly = 1, poly_units = 0;
+    int max() const { return std::max(gram, poly); }
+};
+
+int64_t sym_tiles(const Geom &g) {
+    const int64_t nt = g.sp / muon::kTile;
+    return nt * (nt + 1) / 2;
+}
+
+Splits plan_splits(const Geom &g, bool bf16, int64_t group_n) {
+    Splits sp;
+    if (!bf16) return sp;
+    const int64_t w = sym_tiles(g) * group_n;
+    // K extents of the loops (the true length rounded up to 128), in units of 128
+    const int64_t gram_k = std::min(g.lp, round_up(g.l, 128)) / 128;
+    const int64_t poly_k = std::min(g.sp, round_up(g.s, 128)) / 128;
+    // the partial tiles take at most half of a matrix's own workspace
+    const size_t x = static_cast<size_t>(g.sp * g.lp), a = static_cast<size_t>(g.sp * g.sp);
+    const size_t per_split = static_cast<size_t>(sym_tiles(g)) * 256 * 256 * 4;
+    const int64_t max_splits = static_cast<int64_t>((x * 5 + a * 4) / 2 / per_split);
+    sp.gram = muon::ns_sym_splits(w, gram_k, max_splits, &sp.gram_units);
+    sp.poly = muon::ns_sym_splits(w, poly_k, max_splits, &sp.poly_units);
+    return sp;
+}
+
+// One group: every matrix with the same (min, max) of its shape and the same
+// dtypes.  The Newton-Schulz stages see only X (s x l), so both orientations
+// of a shape share their launches; the momentum pass and the update, which
+// touch W's layout, run once per orientation ("run").  members lists the
+// matrices with rows <= cols first (n_flat of them), then those with
+// rows > cols (X = W^T), each in call order.
 struct GroupPlan {
-    Geom g;
+    Geom g;                       // X geometry: rows = s, cols = l, untransposed
     bool bf16;                    // bf16 Newton-Schulz products for this group
     int32_t param_dtype, grad_dtype;
     std::vector<int64_t> members; // indices into the caller's list
+    int64_t n_flat = 0;           // members with rows <= cols (a prefix)
     int64_t chunk = 0;            // matrices per chunk
-    int bpm = 0;                  // stage-1 blocks per matrix
+    int bpm = 0;                  // stage-1 blocks per matrix (the larger of the two orientations)
+    Splits splits;
 };
 
+// Geometry of W for a member of the group: rows <= cols (flat) or rows > cols.
+Geom run_geom(const Geom &g, bool tall) { return tall ? make_geom(g.l, g.s) : make_geom(g.s, g.l); }
+
 // Bytes of NS workspace one matrix of geometry g needs.
-size_t per_matrix_bytes(const Geom &g, bool bf16) {
+size_t per_matrix_bytes(const Geom &g, bool bf16, int splits) {
     const size_t x = static_cast<size_t>(g.sp * g.lp), a = static_cast<size_t>(g.sp * g.sp);
-    return bf16 ? (x * (2 + 2 + 1) + a * (2 + 2)) : (x * (4 + 4) + a * (4 + 4 + 4));
+    return (bf16 ? (x * (2 + 2 + 1) + a * (2 + 2)) : (x * (4 + 4) + a * (4 + 4 + 4))) +
+           muon::ns_kpart_bytes(sym_tiles(g), 1, splits);
 }
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-    size_t xf0, xf1, xb0, xb1, xl, af, ab, bb, total;
-    bool has_xf;
+    size_t xf0, xf1, xb0, xb1, xl, af, ab, bb, kp, total;
+    bool has_xf, has_kp;
 };
 
-Layout chunk_layout(const Geom &g, bool bf16, int64_t n) {
+Layout chunk_layout(const Geom &g, bool bf16, int64_t n, int splits) {
     const size_t x = static_cast<size_t>(g.sp * g.lp) * n, a = static_cast<size_t>(g.sp * g.sp) * n;
     Layout L{};
     size_t off = 0;
@@ -266,6 +306,9 @@ Layout chunk_layout(const Geom &g, bool bf16, int64_t n) {
         L.ab = off; off = align_up(off + a * 4);
         L.bb = off; off = align_up(off + a * 4);
     }
+    const size_t kp = muon::ns_kpart_bytes(sym_tiles(g), n, splits);
+    L.has_kp = kp > 0;
+    L.kp = off; off = align_up(off + kp);
     L.total = off;
     return L;
 }
@@ -274,46 +317,64 @@ muon_status plan_groups(const muon_matrix *mats, int64_t count, int32_t precisio
                         size_t *ws_bytes, size_t *partial_count, int64_t *max_chunk, char *msg, size_t msg_cap) {
     std::map<std::tuple<int64_t, int64_t, int32_t, int32_t>, size_t> index;
     out->clear();
+    std::vector<std::vector<int64_t>> tall;  // per group: members with rows > cols
     for (int64_t i = 0; i < count; ++i) {
-        const auto key = std::make_tuple(mats[i].rows, mats[i].cols, mats[i].param_dtype, mats[i].grad_dtype);
+        const int64_t s = std::min(mats[i].rows, mats[i].cols), l = std::max(mats[i].rows, mats[i].cols);
+        const auto key = std::make_tuple(s, l, mats[i].param_dtype, mats[i].grad_dtype);
         auto it = index.find(key);
+        size_t gi;
         if (it == index.end()) {
             GroupPlan gp;
-            gp.g = make_geom(mats[i].rows, mats[i].cols);
-            gp.bf16 = use_bf16(precision, gp.g.s);
+            gp.g = make_geom(s, l);
+            gp.bf16 = use_bf16(precision, s);
             gp.param_dtype = mats[i].param_dtype;
             gp.grad_dtype = mats[i].grad_dtype;
-            index.emplace(key, out->size());
+            gi = out->size();
+            index.emplace(key, gi);
             out->push_back(gp);
-            out->back().members.push_back(i);
+            tall.emplace_back();
         } else {
-            (*out)[it->second].members.push_back(i);
+            gi = it->second;
         }
+        if (mats[i].rows > mats[i].cols)
+            tall[gi].push_back(i);
+        else
+            (*out)[gi].members.push_back(i);
+    }
+    for (size_t gi = 0; gi < out->size(); ++gi) {
+        GroupPlan &gp = (*out)[gi];
+        gp.n_flat = static_cast<int64_t>(gp.members.size());
+        gp.members.insert(gp.members.end(), tall[gi].begin(), tall[gi].end());
     }
     *ws_bytes = 0;
     *partial_count = 0;
     *max_chunk = 0;
     for (GroupPlan &gp : *out) {
         const bool bf16 = gp.bf16;
-        const size_t per = per_matrix_bytes(gp.g, bf16);
-        int64_t n = static_cast<int64_t>(gp.members.size());
+        const int64_t n_all = static_cast<int64_t>(gp.members.size());
+        gp.splits = plan_splits(gp.g, bf16, n_all);
+        const int sm = gp.splits.max();
+        const size_t per = per_matrix_bytes(gp.g, bf16, sm);
+        int64_t n = n_all;
         if (cap) {
-            if (chunk_layout(gp.g, bf16, 1).total > cap) {
+            const size_t one = chunk_layout(gp.g, bf16, 1, sm).total;
+            if (one > cap) {
                 set_msg(msg, msg_cap, "a %lld x %lld matrix needs %zu bytes of workspace, above the cap %zu",
-                        (long long)gp.g.rows, (long long)gp.g.cols, chunk_layout(gp.g, bf16, 1).total, cap);
+                        (long long)gp.g.s, (long long)gp.g.l, one, cap);
                 return MUON_ERR_OUT_OF_MEMORY;
             }
             n = std::min<int64_t>(n, std::max<int64_t>(1, static_cast<int64_t>(cap / per)));
-            while (n > 1 && chunk_layout(gp.g, bf16, n).total > cap) --n;
+            while (n > 1 && chunk_layout(gp.g, bf16, n, sm).total > cap) --n;
         }
         // Keep every grouped launch inside a 32-bit grid.
         const int64_t apply_tiles = (gp.g.sp / muon::kTile) * (gp.g.lp / muon::kTile);
         n = std::min<int64_t>(n, std::max<int64_t>(1, ((int64_t(1) << 31) - 1) / apply_tiles));
         int rpb = 0, tc = 0;
-        gp.bpm = muon::nesterov_blocks_per_mat(gp.g, &rpb, &tc);
+        gp.bpm = std::max(muon::nesterov_blocks_per_mat(run_geom(gp.g, false), &rpb, &tc),
+                          muon::nesterov_blocks_per_mat(run_geom(gp.g, true), &rpb, &tc));
         n = std::min<int64_t>(n, std::max<int64_t>(1, ((int64_t(1) << 31) - 1) / gp.bpm));
         gp.chunk = n;
-        *ws_bytes = std::max(*ws_bytes, chunk_layout(gp.g, bf16, n).total);
+        *ws_bytes = std::max(*ws_bytes, chunk_layout(gp.g, bf16, n, sm).total);
         *partial_count = std::max(*partial_count, static_cast<size_t>(n) * gp.bpm);
         *max_chunk = std::max(*max_chunk, n);
     }
@@ -504,8 +565,8 @@ struct CallMem {
 };
 
 // Work view of a chunk laid out at the workspace base.
-Work chunk_work(const CallMem &mem, const Geom &g, bool bf16, int64_t n, int bpm) {
-    const Layout L = chunk_layout(g, bf16, n);
+Work chunk_work(const CallMem &mem, const Geom &g, bool bf16, int64_t n, int bpm, int splits) {
+    const Layout L = chunk_layout(g, bf16, n, splits);
     char *base = mem.ws;
     Work w{};
     w.xf = L.has_xf ? reinterpret_cast<float *>(base + L.xf0) : nullptr;
@@ -524,8 +585,38 @@ Work chunk_work(const CallMem &mem, const Geom &g, bool bf16, int64_t n, int bpm
     w.nrm2 = reinterpret_cast<double *>(t + np);
     w.inv_norm = reinterpret_cast<float *>(t + np + align_up(static_cast<size_t>(n) * sizeof(double)));
     w.call_nrm2 = mem.call_nrm2;
+    w.kpart = L.has_kp ? reinterpret_cast<float *>(base + L.kp) : nullptr;
     return w;
 }
+
+// The view of matrices k, k+1, ... of a chunk (a run of one orientation):
+// per-matrix workspace and tables shifted by k, stage-1 partial sums by
+// partial_off.
+Work offset_work(const Work &w, int64_t k, bool bf16, int64_t partial_off) {
+    Work o = w;
+    const int64_t xo = k * w.x_stride, ao = k * w.a_stride;
+    if (o.xf) o.xf += xo;
+    if (o.xf_next) o.xf_next += xo;
+    if (o.xb) o.xb = static_cast<uint16_t *>(o.xb) + xo;
+    if (o.xb_next) o.xb_next = static_cast<uint16_t *>(o.xb_next) + xo;
+    if (o.xl) o.xl = static_cast<uint8_t *>(o.xl) + xo;
+    if (o.af) o.af += ao;
+    o.ab = static_cast<char *>(o.ab) + ao * (bf16 ? 2 : 4);
+    o.bb = static_cast<char *>(o.bb) + ao * (bf16 ? 2 : 4);
+    o.partials += partial_off;
+    o.nrm2 += k;
+    o.inv_norm += k;
+    if (o.uscale) o.uscale += k;
+    o.kpart = nullptr;
+    return o;
+}
+
+// Matrices [k0, k0 + n) of a chunk that share W's orientation, g their W
+// geometry (transposed when rows > cols).
+struct Run {
+    int64_t k0, n;
+    Geom g;
+};
 
 size_t tabs_bytes(size_t partials, int64_t max_chunk) {
     return align_up(partials * sizeof(double)) + align_up(static_cast<size_t>(max_chunk) * sizeof(double)) +
@@ -561,25 +652,37 @@ void ns_work(int stage, const Geom &g, bool bf16, int n, bool ns_out, int psize,
     *bytes *= n;
 }
 
-// Runs normalisation + the NS schedule (+ the fused update when `update`) on
-// one chunk whose first stage already wrote X = N and the norms.  Returns the
-// workspace view holding the final X in xf (fp32 path) or xb + xl (bf16 path),
-// meaningful when !update.  In the unit-RMS scale mode the last step writes X
-// like the others; ||X||^2 per matrix is then reduced (partial_bpm partial
-// sums per matrix fit in w.partials) into a per-matrix scale, and a separate
-// pass applies the decay + update.
-muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom &g, Work &w, bool bf16,
+// Runs normalisation + the NS schedule (+ the decay and update when
+// `update`) on one chunk whose first stage already wrote X = N and the norms.
+// gx is X's geometry (s x l); runs[] split the chunk into its matrices with
+// rows <= cols and those with rows > cols (W = X^T), runs[k].g being W's
+// geometry.  The products see only X, so one launch per stage covers both
+// runs; a chunk of one run may fuse the update into the last product, a
+// chunk of two runs updates each run in a pass of its own.  Returns the
+// workspace view holding the final X in xf (fp32 path) or xb + xl (bf16
+// path), meaningful when !update.  In the unit-RMS scale mode the last step
+// writes X like the others; ||X||^2 per matrix is then reduced (partial_bpm
+// partial sums per matrix fit in w.partials) into a per-matrix scale, and a
+// separate pass applies the decay + update.
+muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom &gx, Work &w, bool bf16,
                    const muon_hparams *hp, bool update, int param_bf16, bool any_ns_out, float d, float s,
-                   hipStream_t st, bool params_aligned16 = false, int partial_bpm = 0, bool outs_aligned16 = false) {
+                   hipStream_t st, const Splits &sp, const Run *runs, int nruns, bool params_aligned16 = false,
+                   int partial_bpm = 0, bool outs_aligned16 = false) {
     const bool unit_rms = update && hp->scale_mode == MUON_SCALE_UNIT_RMS;
+    // the geometry the product launches see: W's own for a chunk of one run (the
+    // fused update needs its orientation), X's otherwise
+    const Geom &g = nruns == 1 ? runs[0].g : gx;
     // bf16 parameters whose tiles allow staging W through LDS keep the update
     // fused into the last product.  Other shapes whose W rows allow 8-wide
     // access run the last step as a plain product plus a separate update
-    // pass, which costs less than the per-element fused epilogue there.
-    const bool w_staged = param_bf16 && params_aligned16 && outs_aligned16 && !g.transposed &&
+    // pass, which costs less than the per-element fused epilogue there, and
+    // so does a chunk of both orientations.
+    const bool w_staged = nruns == 1 && param_bf16 && params_aligned16 && outs_aligned16 && !g.transposed &&
                           g.s % muon::kTile == 0 && g.l % muon::kTile == 0;
-    const bool split_update = update && !unit_rms && bf16 && !w_staged && params_aligned16 && outs_aligned16 &&
-                              (g.transposed ? g.cols % 8 == 0 : g.l % 8 == 0);
+    const bool split_update =
+        update && !unit_rms &&
+        (nruns > 1 || (bf16 && !w_staged && params_aligned16 && outs_aligned16 &&
+                       (g.transposed ? g.cols % 8 == 0 : g.l % 8 == 0)));
     const double xe = static_cast<double>(g.s) * g.l * nmat;
     // bf16 path with a schedule: X stays N and the first step applies 1/||N||
     // (only the padding needs zeros), except for the matrices whose norm lies
@@ -614,6 +717,10 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
         p.unnormalized = (fold && it == 0) ? 1 : 0;
         p.w_staged = w_staged ? 1 : 0;
         p.vec_ok = params_aligned16 && outs_aligned16 ? 1 : 0;
+        p.gram_splits = sp.gram;
+        p.gram_units = sp.gram_units;
+        p.poly_splits = sp.poly;
+        p.poly_units = sp.poly_units;
         for (int kind = 0; kind < 3; ++kind) {
             const int stage = kind == 0 ? ST_GRAM : kind == 1 ? ST_POLY : (p.final_update ? ST_APPLY_UPDATE : ST_APPLY);
             double fl = 0, by = 0;
@@ -635,13 +742,17 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
         w.uscale = w.inv_norm;
     }
     if (update && (hp->num_ns_steps == 0 || unit_rms || split_update)) {
-        const double by = xe * ((bf16 ? 3.0 : 4.0) + 2.0 * psize + (any_ns_out ? 4.0 : 0.0));
-        e = timed(ctx, ST_UPDATE, 0.0, by, st,
-                  [&] {
-                      return muon::launch_update_from_work(descs, nmat, g, w, param_bf16, d, s,
-                                                           params_aligned16 && outs_aligned16, st);
-                  });
-        if (e != hipSuccess) return hip_fail(ctx, e, "update launch");
+        for (int r = 0; r < nruns; ++r) {
+            const Run &run = runs[r];
+            const Work wr = offset_work(w, run.k0, bf16, 0);
+            const double by = static_cast<double>(g.s) * g.l * run.n *
+                              ((bf16 ? 3.0 : 4.0) + 2.0 * psize + (any_ns_out ? 4.0 : 0.0));
+            e = timed(ctx, ST_UPDATE, 0.0, by, st, [&] {
+                return muon::launch_update_from_work(descs + run.k0, static_cast<int>(run.n), run.g, wr, param_bf16,
+                                                     d, s, params_aligned16 && outs_aligned16, st);
+            });
+            if (e != hipSuccess) return hip_fail(ctx, e, "update launch");
+        }
     }
     return MUON_OK;
 }
@@ -758,29 +869,47 @@ muon_status step_impl(muon_context *ctx, const muon_matrix *mats, int64_t count,
         for (int64_t c0 = 0; c0 < n_all; c0 += gp.chunk) {
             const int n = static_cast<int>(std::min<int64_t>(gp.chunk, n_all - c0));
             const MatDesc *dd = ddev + pos + c0;
-            bool vec_ok = true, params_aligned = true, outs_aligned = true;
+            bool params_aligned = true, outs_aligned = true, any_out = false;
             for (int k = 0; k < n; ++k) {
                 const muon_matrix &m = mats[gp.members[c0 + k]];
-                vec_ok = vec_ok && aligned16(m.momentum) && aligned16(m.grad);
                 params_aligned = params_aligned && aligned16(m.param);
                 outs_aligned = outs_aligned && (!m.ns_out || aligned16(m.ns_out));
+                any_out = any_out || m.ns_out != nullptr;
             }
-            bool any_out = false;
-            for (int k = 0; k < n; ++k) any_out = any_out || mats[gp.members[c0 + k]].ns_out != nullptr;
-            Work w = chunk_work(mem, gp.g, bf16, n, gp.bpm);
-            const double elems = static_cast<double>(gp.g.rows) * gp.g.cols * n;
+            // the chunk's runs: members with rows <= cols, then those with rows > cols
+            Run runs[2];
+            int nruns = 0;
+            if (c0 < gp.n_flat) runs[nruns++] = Run{0, std::min<int64_t>(c0 + n, gp.n_flat) - c0, run_geom(gp.g, false)};
+            if (c0 + n > gp.n_flat) {
+                const int64_t k0 = std::max<int64_t>(c0, gp.n_flat) - c0;
+                runs[nruns++] = Run{k0, n - k0, run_geom(gp.g, true)};
+            }
+            Work w = chunk_work(mem, gp.g, bf16, n, gp.bpm, gp.splits.max());
             const double gsz = gp.grad_dtype == MUON_BF16 ? 2.0 : 4.0;
-            // M read and written (8), N written: fp32 (4) or hi + residual (3)
-            hipError_t e = timed(ctx, ST_MOMENTUM, 0.0, elems * (gsz + (bf16 ? 11.0 : 12.0)), st, [&] {
-                return muon::launch_nesterov(dd, n, gp.g, w, mu, hp->nesterov, gp.grad_dtype == MUON_BF16, vec_ok,
-                                             st);
-            });
-            if (e != hipSuccess) return hip_fail(ctx, e, "momentum launch");
-            e = timed(ctx, ST_FINALIZE, 0.0, static_cast<double>(n) * gp.bpm * 8.0, st,
-                      [&] { return muon::launch_norm_finalize(dd, n, w, gp.bpm, st); });
-            if (e != hipSuccess) return hip_fail(ctx, e, "norm launch");
+            for (int r = 0; r < nruns; ++r) {
+                const Run &run = runs[r];
+                const MatDesc *dr = dd + run.k0;
+                const Work wr = offset_work(w, run.k0, bf16, run.k0 * gp.bpm);
+                bool vec_ok = true;
+                for (int64_t k = run.k0; k < run.k0 + run.n; ++k) {
+                    const muon_matrix &m = mats[gp.members[c0 + k]];
+                    vec_ok = vec_ok && aligned16(m.momentum) && aligned16(m.grad);
+                }
+                int rpb = 0, tc = 0;
+                const int bpm = muon::nesterov_blocks_per_mat(run.g, &rpb, &tc);
+                const double elems = static_cast<double>(gp.g.s) * gp.g.l * run.n;
+                // M read and written (8), N written: fp32 (4) or hi + residual (3)
+                hipError_t e = timed(ctx, ST_MOMENTUM, 0.0, elems * (gsz + (bf16 ? 11.0 : 12.0)), st, [&] {
+                    return muon::launch_nesterov(dr, static_cast<int>(run.n), run.g, wr, mu, hp->nesterov,
+                                                 gp.grad_dtype == MUON_BF16, vec_ok, st);
+                });
+                if (e != hipSuccess) return hip_fail(ctx, e, "momentum launch");
+                e = timed(ctx, ST_FINALIZE, 0.0, static_cast<double>(run.n) * bpm * 8.0, st,
+                          [&] { return muon::launch_norm_finalize(dr, static_cast<int>(run.n), wr, bpm, st); });
+                if (e != hipSuccess) return hip_fail(ctx, e, "norm launch");
+            }
             s = run_ns(ctx, dd, n, gp.g, w, bf16, hp, true, gp.param_dtype == MUON_BF16, any_out, d, sc, st,
-                       params_aligned, gp.bpm, outs_aligned);
+                       gp.splits, runs, nruns, params_aligned, gp.bpm, outs_aligned);
             if (s != MUON_OK) return s;
         }
         pos += static_cast<size_t>(n_all);
@@ -941,7 +1070,8 @@ muon_status muon_ns_only(muon_context *ctx, const float *n_in, float *x_out, int
     if (a0 < b0 + nb && b0 < a0 + nb) return fail(ctx, MUON_ERR_INVALID_ARGUMENT, "n_in and x_out overlap");
     const Geom g = make_geom(rows, cols);
     const bool bf16 = use_bf16(hp->ns_precision, g.s);
-    const size_t need = chunk_layout(g, bf16, 1).total;
+    const Splits sp = plan_splits(g, bf16, 1);
+    const size_t need = chunk_layout(g, bf16, 1, sp.max()).total;
     if (ctx->cap && need > ctx->cap)
         return fail(ctx, MUON_ERR_OUT_OF_MEMORY, "matrix needs %zu bytes of workspace, above the cap", need);
     DeviceGuard guard(ctx->device);
@@ -958,14 +1088,15 @@ muon_status muon_ns_only(muon_context *ctx, const float *n_in, float *x_out, int
     const MatDesc *ddev = static_cast<const MatDesc *>(ctx->mat_desc.p);
     Work w = chunk_work(CallMem{static_cast<char *>(ctx->ws.p), static_cast<char *>(ctx->tabs.p),
                                 static_cast<double *>(ctx->call_nrm2.p)},
-                        g, bf16, 1, nb_blocks);
+                        g, bf16, 1, nb_blocks, sp.max());
     const double elems = static_cast<double>(rows) * cols;
     hipError_t e = timed(ctx, ST_IMPORT, 0.0, elems * 8.0, st, [&] { return muon::launch_import_n(n_in, g, w, st); });
     if (e != hipSuccess) return hip_fail(ctx, e, "import launch");
     e = timed(ctx, ST_FINALIZE, 0.0, nb_blocks * 8.0, st,
               [&] { return muon::launch_norm_finalize(ddev, 1, w, nb_blocks, st); });
     if (e != hipSuccess) return hip_fail(ctx, e, "norm launch");
-    s = run_ns(ctx, ddev, 1, g, w, bf16, hp, false, 0, false, 0.f, 0.f, st);
+    const Run run{0, 1, g};
+    s = run_ns(ctx, ddev, 1, g, w, bf16, hp, false, 0, false, 0.f, 0.f, st, sp, &run, 1);
     if (s != MUON_OK) return s;
     e = timed(ctx, ST_EXPORT, 0.0, elems * 8.0, st, [&] { return muon::launch_export_x(g, w, x_out, st); });
     if (e != hipSuccess) return hip_fail(ctx, e, "export launch");

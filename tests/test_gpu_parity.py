@@ -152,13 +152,16 @@ def _run_step(ctx, torch_mod, specs, precision, seed, lr=0.02, wd=0.1, gamma=0.2
 @pytest.mark.parametrize("precision", ["bf16", "f32"])
 def test_step_mixed_group(ctx, torch_mod, precision):
     """Several shapes and dtype combinations in one call: grouped launches, ragged tiles,
-    transposed matrices, bf16/fp32 params and grads (256 x 512 bf16: the fused update
-    that stages W through LDS)."""
+    transposed matrices, bf16/fp32 params and grads; a shape and its transpose share one
+    group (96 x 300 with 300 x 96, 256 x 512 with 512 x 256: one launch per product stage,
+    momentum and update per orientation); the 512 x 768 bf16 pair, all of one
+    orientation, stages W through LDS in the fused update."""
     S = synth.MatrixSpec
     specs = [S(96, 300, "bf16", "bf16"), S(96, 300, "bf16", "bf16"), S(300, 96, "bf16", "bf16"),
              S(260, 260, "f32", "f32", law="gauss"), S(64, 128, "f32", "bf16"), S(128, 64, "bf16", "f32"),
              S(96, 300, "bf16", "bf16", prefill_momentum=True), S(5, 3, "f32", "f32", law="gauss"),
-             S(256, 512, "bf16", "bf16"), S(256, 512, "bf16", "bf16"), S(512, 256, "bf16", "bf16")]
+             S(256, 512, "bf16", "bf16"), S(256, 512, "bf16", "bf16"), S(512, 256, "bf16", "bf16"),
+             S(512, 768, "bf16", "bf16"), S(512, 768, "bf16", "bf16")]
     say(f"step mixed group {precision}")
     _run_step(ctx, torch_mod, specs, precision, seed=21)
 
@@ -215,10 +218,26 @@ def test_step_zero_gradient_is_decay_only(ctx, torch_mod):
     _run_step(ctx, torch_mod, [S(70, 130), S(130, 70, "f32", "f32")], "bf16", seed=25, zero_grad=True)
 
 
+def test_step_split_k_products(ctx, torch_mod):
+    """Groups with few Gram / A^2 tiles and a long K split the products' K loop over
+    several workgroups and sum the partial tiles in a fixed order: a (1024, 1536) group
+    of both orientations (Gram and A^2 in 2 ranges), a 128 x 4096 matrix (Gram in 8),
+    a ragged 300 x 3000 one (Gram in 5), against the oracle; the whole call twice,
+    bit for bit."""
+    S = synth.MatrixSpec
+    specs = [S(1024, 1536), S(1536, 1024), S(128, 4096), S(300, 3000)]
+    say("step split-K products")
+    _, dev1 = _run_step(ctx, torch_mod, specs, "bf16", seed=35)
+    _, dev2 = _run_step(ctx, torch_mod, specs, "bf16", seed=35)
+    for (p1, _, m1, o1), (p2, _, m2, o2) in zip(dev1, dev2):
+        for a, b in ((p1, p2), (o1, o2)):
+            assert np.array_equal(to_np(a).view(np.uint32), to_np(b).view(np.uint32))
+
+
 def test_step_is_deterministic(ctx, torch_mod):
     ms = _ms()
     S = synth.MatrixSpec
-    specs = [S(300, 700), S(700, 300)]
+    specs = [S(300, 700), S(700, 300), S(256, 2048), S(2048, 256)]
     wl = synth.Workload("t", 26, tuple(specs))
     outs = []
     for rep in range(2):
