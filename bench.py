@@ -119,6 +119,37 @@ def adamw_rate(ctx, torch, ms, stream, steps=5):
             "workload": "embedding + head, 2 x 102400x2048 fp32, 28 B/elem"}
 
 
+PROBE_MIX = {"momentum_nesterov": (6, 7), "adamw": (4, 3), "update": (5, 2), "copy": (1, 1)}
+
+
+def hbm_probe(ctx, torch, stream, stream_bytes=1 << 30, steps=5):
+    """The library's streaming probe at each elementwise kernel's read : write mix
+    (streams of 1 GiB, every 16-byte vector read or written once, 1 GiB + 197,632
+    bytes apart so that the streams do not start at power-of-two distances, as
+    separate allocations do not), timed with its per-launch events: the HBM
+    ceiling those kernels are compared with."""
+    out = {}
+    pitch = stream_bytes + 12352 * 16
+    for name, (r, w) in PROBE_MIX.items():
+        src = torch.empty((r - 1) * pitch + stream_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty((w - 1) * pitch + stream_bytes, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        ctx.muon_stream_probe(src, dst, stream_bytes, r, w, pitch, stream)
+        torch.cuda.synchronize()
+        ctx.muon_profile_enable(True)
+        for _ in range(steps):
+            ctx.muon_stream_probe(src, dst, stream_bytes, r, w, pitch, stream)
+        torch.cuda.synchronize()
+        st = ctx.muon_profile_read()["stream_probe"]
+        ctx.muon_profile_enable(False)
+        gbs = st["bytes"] / st["total_ms"] / 1e6
+        log(f"  probe {r}:{w} ({name:17s}) avg {st['total_ms'] / st['launches']:8.4f} ms  {gbs:8.1f} GB/s")
+        out[name] = {"reads_writes": [r, w], "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        del src, dst
+        torch.cuda.empty_cache()
+    return out
+
+
 def moe16b_step(args):
     """Times the full synthetic 16B-MoE optimizer step (27 layers: 4 x 2048^2
     attention matrices and 64 experts x (2048x1408 up, gate; 1408x2048 down),
@@ -314,12 +345,22 @@ def main():
                     help="update scale: sqrt(max(n,m))*gamma (DeepSeek-V4) or the unit-RMS mode")
     ap.add_argument("--library-baseline", action="store_true",
                     help="only time torch bf16 batched products of the same shapes (64 matrices)")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="only time the library's streaming probe at the elementwise kernels' read:write mixes")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
         return
     if args.library_baseline:
         library_baseline(2048, 7168, 64)
+        return
+    if args.hbm_probe:
+        import torch
+
+        import muon_step_amd as ms
+        ctx = ms.Context(0)
+        print(json.dumps({"hbm_probe": hbm_probe(ctx, torch, torch.cuda.current_stream())}), flush=True)
+        ctx.close()
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the per-GPU work of a sharded "
@@ -437,6 +478,11 @@ def main():
     del grads, params, moms, mats
     torch.cuda.empty_cache()
     out["elementwise"]["adamw"] = adamw_rate(ctx, torch, ms, stream)
+    probe = hbm_probe(ctx, torch, stream)
+    for k, v in out["elementwise"].items():
+        if k in probe:
+            v["frac_of_probe"] = round(v["GB/s"] / probe[k]["GB/s"], 4)
+    out["hbm_probe"] = probe
     ctx.close()
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -271,11 +271,49 @@ muon_status muon_apply_update(muon_context *ctx, void *param, int32_t param_dtyp
                               int64_t rows, int64_t cols, const muon_hparams *hp,
                               void *hip_stream);
 
+/* Test hook: one Newton-Schulz product of the bf16 path on one matrix, with
+ * its operands rounded as that path rounds them (DeepSeek-V4 book ch. 6,
+ * section 3: one step is X <- a X + b A X + c A^2 X with A = X X^T, here
+ * split into its three products).  X is s x l with 1 <= s <= l (X's own
+ * orientation; muon_step transposes W with rows > cols into it).  All
+ * pointers are device fp32, row-major; out must not overlap the inputs.
+ *   MUON_STAGE_GRAM:  x (s x l) -> out (s x s):  A = X_hi X_hi^T, X_hi =
+ *                     bf16(x); fp32 accumulation, A rounded to bf16.
+ *   MUON_STAGE_POLY:  m (s x s, symmetric; rounded to bf16 as A) -> out
+ *                     (s x s):  B = b A + c A A, fp32 accumulation, B
+ *                     rounded to bf16.
+ *   MUON_STAGE_APPLY: m (s x s, symmetric; rounded to bf16 as B), x (s x l,
+ *                     kept as X_hi = bf16(x) plus its 8-bit residual) ->
+ *                     out (s x l):  X' = a X + B X_hi (aX from hi + residual,
+ *                     fp32 accumulation), as the value of the pair X' is
+ *                     stored in.
+ * The products run exactly as inside muon_step for a single matrix of this
+ * shape (same tiles, same split of long K loops). */
+#define MUON_STAGE_GRAM 0
+#define MUON_STAGE_POLY 1
+#define MUON_STAGE_APPLY 2
+muon_status muon_ns_stage(muon_context *ctx, int32_t stage, const float *x, const float *m, float *out, int64_t s,
+                          int64_t l, double a, double b, double c, void *hip_stream);
+
 /* Blocks until the context's device memory holds the per-matrix squared
  * Frobenius norms of the last muon_step's N_t (matrix order of that call)
  * and copies min(count, capacity) of them to out (host doubles).  Returns
  * the count through *count_out.  Synchronises the last call's stream. */
 muon_status muon_last_norms(muon_context *ctx, double *out, int64_t capacity, int64_t *count_out);
+
+/* Measurement aid, no step of the method: streams `reads` source streams of
+ * stream_bytes each (src, device; stream k starts k * pitch_bytes into it)
+ * and `writes` destination streams (dst, device, the same pitch), every
+ * 16-byte vector read and written once, coalesced, each written vector
+ * depending on its thread's reads.  Its rate is the HBM ceiling for a kernel
+ * with that read : write mix, the reference for the elementwise kernels'
+ * GB/s: (reads, writes) = (6, 7) the momentum pass (bf16 G 2 + M 4 bytes
+ * read, M 4 + X 3 written per element), (4, 3) AdamW, (5, 2) the separate
+ * update pass, (1, 1) a copy; others UNSUPPORTED.  stream_bytes and
+ * pitch_bytes (>= stream_bytes) must be multiples of 16, src and dst 16-byte
+ * aligned and disjoint.  Timed as stage "stream_probe". */
+muon_status muon_stream_probe(muon_context *ctx, const void *src, void *dst, int64_t stream_bytes,
+                              int64_t pitch_bytes, int32_t reads, int32_t writes, void *hip_stream);
 
 /* Per-stage timing of a context's launches.  While enabled, every kernel
  * launch the context makes is bracketed by two HIP events recorded on the
@@ -285,7 +323,8 @@ muon_status muon_last_norms(muon_context *ctx, double *out, int64_t capacity, in
  * Stage names: "momentum_nesterov", "norm_finalize", "normalize", "gram",
  * "poly", "apply", "apply_update" (the last product with the fused decay and
  * update), "update", "adamw", "import", "export", "unit_rms" (the per-matrix
- * ||X||^2 reduction and scale of the unit-RMS mode), "prenormalize" (the bf16
+ * ||X||^2 reduction and scale of the unit-RMS mode), "stream_probe"
+ * (muon_stream_probe), "prenormalize" (the bf16
  * path's normalisation of the matrices whose ||N_t|| lies outside the range
  * in which the first step folds 1/||N_t|| into its products). */
 typedef struct muon_stage_stats {

@@ -34,7 +34,12 @@ EXPORTS = (
     "muon_check_adamw_args", "muon_workspace_bytes", "muon_create", "muon_destroy",
     "muon_last_error", "muon_step", "muon_adamw_step", "muon_ns_only", "muon_apply_update",
     "muon_last_norms", "muon_profile_enable", "muon_profile_read", "muon_step_noalloc",
+    "muon_stream_probe", "muon_ns_stage",
 )
+
+MUON_STAGE_GRAM = 0
+MUON_STAGE_POLY = 1
+MUON_STAGE_APPLY = 2
 
 
 class MuonError(RuntimeError):
@@ -111,6 +116,8 @@ def load(path=LIB_PATH):
         "muon_ns_only": (i32, [vp, vp, vp, i64, i64, c.POINTER(muon_hparams), vp]),
         "muon_apply_update": (i32, [vp, vp, i32, vp, i64, i64, c.POINTER(muon_hparams), vp]),
         "muon_last_norms": (i32, [vp, c.POINTER(c.c_double), i64, c.POINTER(i64)]),
+        "muon_stream_probe": (i32, [vp, vp, vp, i64, i64, i32, i32, vp]),
+        "muon_ns_stage": (i32, [vp, i32, vp, vp, vp, i64, i64, c.c_double, c.c_double, c.c_double, vp]),
         "muon_profile_enable": (i32, [vp, i32]),
         "muon_profile_read": (i32, [vp, c.POINTER(muon_stage_stats), i32, c.POINTER(i32)]),
     }
@@ -300,6 +307,33 @@ class Context:
         _check(self.lib, self.handle, st, "muon_last_norms")
         return list(out[:min(capacity, n.value)])
 
+
+    def muon_ns_stage(self, stage, out, x=None, m=None, a=0.0, b=0.0, c=0.0, stream=None):
+        """One bf16 product stage; x (s x l), m (s x s), out: fp32 GPU tensors."""
+        named = [("out", out)] + [(n, t) for n, t in (("x", x), ("m", m)) if t is not None]
+        for name, t in named:
+            if not t.is_contiguous() or t.dim() != 2:
+                raise ValueError(f"{name} must be a contiguous 2-D tensor")
+        _require_f32(named)
+        self._check_tensors(named)
+        s, l = (x.shape if x is not None else (m.shape[0], m.shape[0]))
+        st = self.lib.muon_ns_stage(self.handle, stage, x.data_ptr() if x is not None else None,
+                                    m.data_ptr() if m is not None else None, out.data_ptr(), s, l, a, b, c,
+                                    _stream_handle(stream))
+        _check(self.lib, self.handle, st, "muon_ns_stage")
+
+    def muon_stream_probe(self, src, dst, stream_bytes, reads, writes, pitch_bytes=None, stream=None):
+        """src, dst: GPU tensors holding `reads` / `writes` streams of stream_bytes each,
+        pitch_bytes (default stream_bytes) apart."""
+        pitch = stream_bytes if pitch_bytes is None else pitch_bytes
+        for name, t, k in (("src", src, reads), ("dst", dst, writes)):
+            if not t.is_contiguous() or t.numel() * t.element_size() < (k - 1) * pitch + stream_bytes:
+                raise ValueError(f"{name} must be contiguous and hold {k} streams of {stream_bytes} bytes "
+                                 f"{pitch} bytes apart")
+        self._check_tensors([("src", src), ("dst", dst)])
+        st = self.lib.muon_stream_probe(self.handle, src.data_ptr(), dst.data_ptr(), stream_bytes, pitch, reads,
+                                        writes, _stream_handle(stream))
+        _check(self.lib, self.handle, st, "muon_stream_probe")
 
     def muon_profile_enable(self, enable=True):
         _check(self.lib, self.handle, self.lib.muon_profile_enable(self.handle, 1 if enable else 0),

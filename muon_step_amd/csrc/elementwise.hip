@@ -610,6 +610,33 @@ __global__ __launch_bounds__(256) void import_n_kernel(Geom g, const float *__re
     if (threadIdx.x == 0) w.partials[blockIdx.x] = s;
 }
 
+// Operands of a single product stage (muon_ns_stage): a plain fp32 s x l X
+// into the workspace pair (hi, residual) over the padded sp x lp extent
+// (zeros outside s x l), and a plain fp32 s x s matrix into a bf16 sp x sp
+// operand (zeros outside), and a bf16 sp x sp operand back out as fp32.
+__global__ __launch_bounds__(256) void import_pair_kernel(Geom g, const float *__restrict__ x, Work w) {
+    const int64_t i = blockIdx.x;  // padded row
+    uint16_t *xh = static_cast<uint16_t *>(w.xb) + i * g.lp;
+    uint8_t *xl = static_cast<uint8_t *>(w.xl) + i * g.lp;
+    for (int64_t j = threadIdx.x; j < g.lp; j += 256) {
+        const float v = (i < g.s && j < g.l) ? x[i * g.l + j] : 0.0f;
+        split_bf16(v, xh + j, xl + j);
+    }
+}
+
+__global__ __launch_bounds__(256) void import_bf16_square_kernel(int64_t s, int64_t sp, const float *__restrict__ m,
+                                                                 uint16_t *__restrict__ dst) {
+    const int64_t i = blockIdx.x;
+    for (int64_t j = threadIdx.x; j < sp; j += 256)
+        dst[i * sp + j] = float_to_bf16_bits((i < s && j < s) ? m[i * s + j] : 0.0f);
+}
+
+__global__ __launch_bounds__(256) void export_bf16_square_kernel(int64_t s, int64_t sp, const uint16_t *__restrict__ src,
+                                                                 float *__restrict__ out) {
+    const int64_t i = blockIdx.x;
+    for (int64_t j = threadIdx.x; j < s; j += 256) out[i * s + j] = bf16_bits_to_float(src[i * sp + j]);
+}
+
 // ---------------------------------------------------------------------------
 // AdamW over a table of tensors.  Block b processes elements
 // [(b - first_block[k]) * 1024, ...) of tensor k, k found by binary search.
@@ -670,6 +697,55 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamwDesc *__restrict_
             d.v[ii] = v1;
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming probe (a measurement aid, no step of the method): `reads` source
+// streams and `writes` destination streams of nvec 16-byte vectors each,
+// stream k starting k * pitch vectors into its buffer, every vector read and
+// written once, coalesced; each written vector depends on all the vectors
+// read by its thread, so no read can be dropped.  Its rate is the HBM
+// ceiling for a kernel with the same read : write mix.
+template <int R, int W>
+__global__ __launch_bounds__(256) void stream_probe_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                           int64_t nvec, int64_t pitch) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < nvec;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        uint4 v[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) v[r] = src[i + r * pitch];
+        uint4 x = v[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) {
+            x.x ^= v[r].x;
+            x.y ^= v[r].y;
+            x.z ^= v[r].z;
+            x.w ^= v[r].w;
+        }
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            dst[i + k * pitch] = x;
+            x.x += 1u;
+        }
+    }
+}
+
+template <int R, int W>
+static hipError_t launch_probe_rw(const void *src, void *dst, int64_t nvec, int64_t pitch, hipStream_t st) {
+    const int64_t blocks = std::min<int64_t>((nvec + 255) / 256, 65536);
+    hipLaunchKernelGGL((stream_probe_kernel<R, W>), dim3(static_cast<unsigned>(std::max<int64_t>(blocks, 1))),
+                       dim3(256), 0, st, static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), nvec, pitch);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_probe(const void *src, void *dst, int64_t nvec, int64_t pitch, int reads, int writes,
+                               hipStream_t st) {
+    // the mixes of the elementwise kernels: momentum 6 : 7, AdamW 4 : 3, update 5 : 2, copy 1 : 1
+    if (reads == 6 && writes == 7) return launch_probe_rw<6, 7>(src, dst, nvec, pitch, st);
+    if (reads == 4 && writes == 3) return launch_probe_rw<4, 3>(src, dst, nvec, pitch, st);
+    if (reads == 5 && writes == 2) return launch_probe_rw<5, 2>(src, dst, nvec, pitch, st);
+    if (reads == 1 && writes == 1) return launch_probe_rw<1, 1>(src, dst, nvec, pitch, st);
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------
@@ -797,6 +873,23 @@ hipError_t launch_update_from_work(const MatDesc *descs, int nmat, const Geom &g
         hipLaunchKernelGGL(update_from_work_kernel<uint16_t>, grid, dim3(256), 0, st, descs, g, w, d, s, tc, bpm);
     else
         hipLaunchKernelGGL(update_from_work_kernel<float>, grid, dim3(256), 0, st, descs, g, w, d, s, tc, bpm);
+    return hipGetLastError();
+}
+
+hipError_t launch_import_pair(const Geom &g, const float *x, const Work &w, hipStream_t st) {
+    hipLaunchKernelGGL(import_pair_kernel, dim3(static_cast<unsigned>(g.sp)), dim3(256), 0, st, g, x, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_import_bf16_square(int64_t s, int64_t sp, const float *m, void *dst, hipStream_t st) {
+    hipLaunchKernelGGL(import_bf16_square_kernel, dim3(static_cast<unsigned>(sp)), dim3(256), 0, st, s, sp, m,
+                       static_cast<uint16_t *>(dst));
+    return hipGetLastError();
+}
+
+hipError_t launch_export_bf16_square(int64_t s, int64_t sp, const void *src, float *out, hipStream_t st) {
+    hipLaunchKernelGGL(export_bf16_square_kernel, dim3(static_cast<unsigned>(s)), dim3(256), 0, st, s, sp,
+                       static_cast<const uint16_t *>(src), out);
     return hipGetLastError();
 }
 

@@ -48,10 +48,20 @@ hipError_t launch_unit_rms_scale(int nmat, const Geom &g, const Work &w, const f
 hipError_t launch_update_from_work(const MatDesc *descs, int nmat, const Geom &g, const Work &w,
                                    int param_bf16, float d, float s, bool aligned16, hipStream_t st);
 hipError_t launch_export_x(const Geom &g, const Work &w, float *out, hipStream_t st);
+// Operands of a single product stage: fp32 s x l X into the pair (w.xb, w.xl),
+// fp32 s x s into a bf16 sp x sp operand, and such an operand back to fp32.
+hipError_t launch_import_pair(const Geom &g, const float *x, const Work &w, hipStream_t st);
+hipError_t launch_import_bf16_square(int64_t s, int64_t sp, const float *m, void *dst, hipStream_t st);
+hipError_t launch_export_bf16_square(int64_t s, int64_t sp, const void *src, float *out, hipStream_t st);
 int64_t adamw_blocks(int64_t numel);
 hipError_t launch_adamw(const void *descs_dev, int count, int64_t total_blocks, const AdamwScalars &k,
                         hipStream_t st);
 size_t adamw_desc_size();
+// Streaming probe: `reads` source and `writes` destination streams of nvec
+// 16-byte vectors each, `pitch` vectors apart ((reads, writes) in {(6,7),
+// (4,3), (5,2), (1,1)}).
+hipError_t launch_stream_probe(const void *src, void *dst, int64_t nvec, int64_t pitch, int reads, int writes,
+                               hipStream_t st);
 void adamw_fill_desc(void *dst, float *param, const float *grad, float *m, float *v, int64_t numel,
                      int64_t first_block);
 

@@ -458,11 +458,11 @@ muon_status hip_fail(muon_context *ctx, hipError_t e, const char *where) {
 
 enum Stage {
     ST_MOMENTUM = 0, ST_FINALIZE, ST_NORMALIZE, ST_GRAM, ST_POLY, ST_APPLY, ST_APPLY_UPDATE, ST_UPDATE,
-    ST_ADAMW, ST_IMPORT, ST_EXPORT, ST_UNIT_RMS, ST_PRENORM, ST_COUNT
+    ST_ADAMW, ST_IMPORT, ST_EXPORT, ST_UNIT_RMS, ST_PRENORM, ST_PROBE, ST_COUNT
 };
 const char *const kStageNames[ST_COUNT] = {"momentum_nesterov", "norm_finalize", "normalize", "gram", "poly",
                                            "apply", "apply_update", "update", "adamw", "import", "export",
-                                           "unit_rms", "prenormalize"};
+                                           "unit_rms", "prenormalize", "stream_probe"};
 
 hipError_t take_event(muon_context *ctx, hipEvent_t *ev) {
     if (ctx->ev_used == ctx->ev_pool.size()) {
@@ -931,7 +931,13 @@ extern "C" {
 int32_t muon_abi_version(void) { return MUON_STEP_ABI_VERSION; }
 
 const char *muon_status_string(muon_status status) {
-    switch (status) {
+    // Callers in C (or through a foreign-function layer) may pass any 32-bit
+    // value; reading it as the enum would be undefined for values outside the
+    // enumerators' range, so the bytes are read as an integer.
+    int32_t v = 0;
+    static_assert(sizeof(status) == sizeof(v), "muon_status is 32 bits");
+    std::memcpy(&v, &status, sizeof v);
+    switch (v) {
         case MUON_OK: return "ok";
         case MUON_ERR_INVALID_ARGUMENT: return "invalid argument";
         case MUON_ERR_UNSUPPORTED: return "unsupported";
@@ -1195,6 +1201,94 @@ muon_status muon_adamw_step(muon_context *ctx, const muon_adamw_tensor *ts, int6
     hipError_t e = timed(ctx, ST_ADAMW, 0.0, elems * 28.0, st,
                          [&] { return muon::launch_adamw(ctx->adamw_desc.p, n, blocks, k, st); });
     if (e != hipSuccess) return hip_fail(ctx, e, "AdamW launch");
+    ctx->err.clear();
+    return MUON_OK;
+}
+
+muon_status muon_ns_stage(muon_context *ctx, int32_t stage, const float *x, const float *m, float *out, int64_t s,
+                          int64_t l, double a, double b, double c, void *hip_stream) {
+    if (!ctx) return MUON_ERR_INVALID_ARGUMENT;
+    if (stage != MUON_STAGE_GRAM && stage != MUON_STAGE_POLY && stage != MUON_STAGE_APPLY)
+        return fail(ctx, MUON_ERR_INVALID_ARGUMENT, "unknown stage %d", stage);
+    if (!out || (stage != MUON_STAGE_POLY && !x) || (stage != MUON_STAGE_GRAM && !m))
+        return fail(ctx, MUON_ERR_INVALID_ARGUMENT, "missing operand or output");
+    if (s < 1 || l < s || l > kMaxDim || s * l > kMaxElems)
+        return fail(ctx, MUON_ERR_INVALID_ARGUMENT, "unsupported shape %lld x %lld (need 1 <= s <= l)", (long long)s,
+                    (long long)l);
+    if (!std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c))
+        return fail(ctx, MUON_ERR_INVALID_ARGUMENT, "non-finite coefficient");
+    const uintptr_t o0 = reinterpret_cast<uintptr_t>(out);
+    const uintptr_t on = static_cast<uintptr_t>(stage == MUON_STAGE_APPLY ? s * l : s * s) * 4;
+    for (const float *in : {x, m}) {
+        if (!in) continue;
+        const uintptr_t i0 = reinterpret_cast<uintptr_t>(in);
+        const uintptr_t in_n = static_cast<uintptr_t>(in == x ? s * l : s * s) * 4;
+        if (i0 < o0 + on && o0 < i0 + in_n) return fail(ctx, MUON_ERR_INVALID_ARGUMENT, "an operand overlaps out");
+    }
+    const Geom g = make_geom(s, l);
+    const Splits sp = plan_splits(g, true, 1);
+    const size_t need = chunk_layout(g, true, 1, sp.max()).total;
+    if (ctx->cap && need > ctx->cap)
+        return fail(ctx, MUON_ERR_OUT_OF_MEMORY, "matrix needs %zu bytes of workspace, above the cap", need);
+    DeviceGuard guard(ctx->device);
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    muon_status rs;
+    if ((rs = ensure(ctx, ctx->ws, need, "workspace")) != MUON_OK) return rs;
+    if ((rs = ensure(ctx, ctx->tabs, tabs_bytes(1, 1), "norm tables")) != MUON_OK) return rs;
+    if ((rs = ensure(ctx, ctx->call_nrm2, sizeof(double), "norm output")) != MUON_OK) return rs;
+    Work w = chunk_work(CallMem{static_cast<char *>(ctx->ws.p), static_cast<char *>(ctx->tabs.p),
+                                static_cast<double *>(ctx->call_nrm2.p)},
+                        g, true, 1, 1, sp.max());
+    muon::NsStep p{};
+    p.a = static_cast<float>(a);
+    p.b = static_cast<float>(b);
+    p.c = static_cast<float>(c);
+    p.gram_splits = sp.gram;
+    p.gram_units = sp.gram_units;
+    p.poly_splits = sp.poly;
+    p.poly_units = sp.poly_units;
+    hipError_t e = hipSuccess;
+    if (stage != MUON_STAGE_POLY) e = muon::launch_import_pair(g, x, w, st);
+    if (e == hipSuccess && stage != MUON_STAGE_GRAM)
+        e = muon::launch_import_bf16_square(s, g.sp, m, stage == MUON_STAGE_POLY ? w.ab : w.bb, st);
+    if (e != hipSuccess) return hip_fail(ctx, e, "operand import");
+    const int kind = stage == MUON_STAGE_GRAM ? 0 : stage == MUON_STAGE_POLY ? 1 : 2;
+    double fl = 0, by = 0;
+    ns_work(kind == 0 ? ST_GRAM : kind == 1 ? ST_POLY : ST_APPLY, g, true, 1, false, 2, &fl, &by);
+    e = timed(ctx, kind == 0 ? ST_GRAM : kind == 1 ? ST_POLY : ST_APPLY, fl, by, st,
+              [&] { return muon::launch_ns_stage_bf16(kind, nullptr, 1, g, w, p, st); });
+    if (e != hipSuccess) return hip_fail(ctx, e, "Newton-Schulz launch");
+    if (stage == MUON_STAGE_APPLY) {
+        std::swap(w.xb, w.xb_next);
+        e = muon::launch_export_x(g, w, out, st);
+    } else {
+        e = muon::launch_export_bf16_square(s, g.sp, stage == MUON_STAGE_GRAM ? w.ab : w.bb, out, st);
+    }
+    if (e != hipSuccess) return hip_fail(ctx, e, "export launch");
+    ctx->err.clear();
+    return MUON_OK;
+}
+
+muon_status muon_stream_probe(muon_context *ctx, const void *src, void *dst, int64_t stream_bytes,
+                              int64_t pitch_bytes, int32_t reads, int32_t writes, void *hip_stream) {
+    if (!ctx) return MUON_ERR_INVALID_ARGUMENT;
+    if (!src || !dst || stream_bytes <= 0 || stream_bytes % 16 != 0 || pitch_bytes < stream_bytes ||
+        pitch_bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0)
+        return fail(ctx, MUON_ERR_INVALID_ARGUMENT, "src and dst must be 16-byte aligned, stream_bytes a positive "
+                                                    "multiple of 16, pitch_bytes a multiple of 16 >= stream_bytes");
+    if (!((reads == 6 && writes == 7) || (reads == 4 && writes == 3) || (reads == 5 && writes == 2) ||
+          (reads == 1 && writes == 1)))
+        return fail(ctx, MUON_ERR_UNSUPPORTED, "no probe for %d reads : %d writes", reads, writes);
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(src), b0 = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t na = static_cast<uintptr_t>(pitch_bytes) * (reads - 1) + static_cast<uintptr_t>(stream_bytes);
+    const uintptr_t nb = static_cast<uintptr_t>(pitch_bytes) * (writes - 1) + static_cast<uintptr_t>(stream_bytes);
+    if (a0 < b0 + nb && b0 < a0 + na) return fail(ctx, MUON_ERR_INVALID_ARGUMENT, "src and dst overlap");
+    DeviceGuard guard(ctx->device);
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = timed(ctx, ST_PROBE, 0.0, static_cast<double>(stream_bytes) * (reads + writes), st, [&] {
+        return muon::launch_stream_probe(src, dst, stream_bytes / 16, pitch_bytes / 16, reads, writes, st);
+    });
+    if (e != hipSuccess) return hip_fail(ctx, e, "probe launch");
     ctx->err.clear();
     return MUON_OK;
 }

@@ -395,3 +395,23 @@ def test_momentum_special_values_bitexact(ctx, torch_mod):
     torch_mod.cuda.synchronize()
     m_ref, _ = oracle.nesterov_momentum_f32(m0, g, 0.95)
     assert_bitexact(to_np(tm), m_ref, "momentum specials")
+
+
+def test_stream_probe_moves_every_vector(ctx, torch_mod):
+    """The HBM probe behind the elementwise ceilings reads every source vector and
+    writes every destination vector: destination stream k holds the xor of the
+    thread's source vectors plus k in its first word."""
+    torch = torch_mod
+    nvec, pitch = 3000, 3011
+    for r, w in ((6, 7), (4, 3), (5, 2), (1, 1)):
+        src = torch.randint(0, 2 ** 31 - 1, (r * pitch * 4,), dtype=torch.int32, device="cuda")
+        dst = torch.zeros(w * pitch * 4, dtype=torch.int32, device="cuda")
+        ctx.muon_stream_probe(src, dst, nvec * 16, r, w, pitch * 16)
+        torch.cuda.synchronize()
+        a = src.cpu().numpy().view(np.uint32).reshape(r, pitch, 4)[:, :nvec]
+        x = np.bitwise_xor.reduce(a, axis=0)
+        d = dst.cpu().numpy().view(np.uint32).reshape(w, pitch, 4)[:, :nvec]
+        for k in range(w):
+            want = x.copy()
+            want[:, 0] = want[:, 0] + np.uint32(k)
+            assert np.array_equal(d[k], want), (r, w, k)
