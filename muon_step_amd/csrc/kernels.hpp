@@ -85,28 +85,15 @@ struct NsStep {
     // last step: every parameter and ns_out of the chunk is 16-byte aligned,
     // so the per-element fused update may move four elements per access.
     int vec_ok;
-    // bf16 Gram and A^2 products: K split into `splits` ranges of
-    // k_units_per_split x 128 (the last may be shorter); splits == 1 runs the
-    // whole K loop in one workgroup per tile.
+    // bf16 Gram and A^2 products: the chunk's lower-triangle tiles from
+    // split_from on (in the order (matrix, tile of the matrix); 0: all of them)
+    // run with K split into `splits` ranges of `units` x 128 (the last may be
+    // shorter) whose fp32 partial tiles a reduce finishes; splits == 1: no
+    // tile is split.
     int gram_splits, gram_units;
     int poly_splits, poly_units;
+    int64_t split_from;
 };
-
-// Split-K of the bf16 Gram / A^2 products of a group: the number of K ranges
-// for W lower-triangle tiles (over all matrices of the group) and a K extent
-// of `units` x 128.  A group with fewer than half a wave of tiles (W < 128 on
-// 256 CUs) takes floor(256 / W) ranges, at least 512 of K each and at most
-// max_splits, so that one wave of workgroups covers it; others 1.
-// *units_per_split receives the K extent of one range (x 128).  Depends only
-// on the shape and the group size, so every chunk of a group, and every call
-// with the same matrices, splits alike (a different split changes the order
-// of the fp32 sums).
-int ns_sym_splits(int64_t tiles_w, int64_t units, int64_t max_splits, int *units_per_split);
-// Bytes of split-K partial tiles a chunk of n matrices with `tiles`
-// lower-triangle tiles each needs at `splits` ranges.
-inline size_t ns_kpart_bytes(int64_t tiles, int64_t n, int splits) {
-    return splits > 1 ? static_cast<size_t>(tiles) * n * splits * 256 * 256 * 4 : 0;
-}
 
 // kind: 0 = A = X X^T, 1 = B = bA + cA^2, 2 = X <- aX + BX (or the fused update).
 hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const Geom &g, const Work &w,

@@ -540,19 +540,23 @@ __device__ __forceinline__ void store_kpart(const floatx16 (&acc)[C::MI][C::NI],
             }
 }
 
+// One launch covers the chunk's lower-triangle tiles [tile_base, tile_base +
+// tile_count) in the order (matrix, tile of the matrix); with splits > 1 each
+// of them runs as `splits` workgroups over K ranges of `units` x 128 that store
+// fp32 partial tiles (slot (tile - tile_base) * splits + range of w.kpart),
+// finished by sym_reduce_kernel.  Workgroups of one K range are consecutive:
+// tiles of one matrix then read the same K slab of the operand.
 template <class C, int KIND>
-__global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep p,
-                                                                          int64_t tiles_per_mat, int64_t nblocks) {
+__global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep p, int64_t tiles_per_mat,
+                                                           int64_t nblocks, int64_t tile_base, int64_t tile_count,
+                                                           int splits, int units) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t L = xcd_swizzle(blockIdx.x, nblocks);
-    // split-K: workgroups of one matrix and one K range are consecutive (they
-    // read the same K slab of the operand)
-    const int splits = KIND == GRAM ? p.gram_splits : p.poly_splits;
-    const int units = KIND == GRAM ? p.gram_units : p.poly_units;
-    const int64_t e = L / (tiles_per_mat * splits);
-    const int64_t rem = L % (tiles_per_mat * splits);
-    const int ks = static_cast<int>(rem / tiles_per_mat);
-    const int64_t t = rem % tiles_per_mat;
+    const int ks = static_cast<int>(L / tile_count);
+    const int64_t tl = L % tile_count;  // tile of the launch
+    const int64_t f = tile_base + tl;   // tile of the chunk
+    const int64_t e = f / tiles_per_mat;
+    const int64_t t = f % tiles_per_mat;
     int ti, tj;
     tri_decode(t, &ti, &tj);
     const bool diag = ti == tj;
@@ -617,7 +621,7 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
         main_loop<C, KIND>(acc, src, nk, wave, wm, wn, lane, pre_last);
 
     if (splits > 1) {
-        store_kpart<C>(acc, w.kpart + ((e * tiles_per_mat + t) * splits + ks) * KPART_VALUES, wave, lane);
+        store_kpart<C>(acc, w.kpart + (tl * splits + ks) * KPART_VALUES, wave, lane);
         return;
     }
 
@@ -639,15 +643,16 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
 // accumulator group and lane, as store_kpart laid them out; 64 blocks of 256
 // threads per tile.
 template <int KIND>
-__global__ __launch_bounds__(256) void sym_reduce_kernel(Geom g, Work w, NsStep p, int64_t tiles_per_mat) {
+__global__ __launch_bounds__(256) void sym_reduce_kernel(Geom g, Work w, NsStep p, int64_t tiles_per_mat,
+                                                         int64_t tile_base, int splits) {
     using C = Cfg;
-    const int64_t tile = blockIdx.x / 64;  // matrix * tiles_per_mat + tile of the matrix
+    const int64_t tl = blockIdx.x / 64;  // tile of the split launch
+    const int64_t tile = tile_base + tl; // matrix * tiles_per_mat + tile of the matrix
     const int item = static_cast<int>(blockIdx.x % 64) * 256 + threadIdx.x;
     const int64_t e = tile / tiles_per_mat;
     int ti, tj;
     tri_decode(tile % tiles_per_mat, &ti, &tj);
-    const int splits = KIND == GRAM ? p.gram_splits : p.poly_splits;
-    const floatx4 *src = reinterpret_cast<const floatx4 *>(w.kpart) + tile * splits * (KPART_VALUES / 4) + item;
+    const floatx4 *src = reinterpret_cast<const floatx4 *>(w.kpart) + tl * splits * (KPART_VALUES / 4) + item;
     floatx4 sum = src[0];
     for (int k = 1; k < splits; ++k) {
         const floatx4 v = src[static_cast<int64_t>(k) * (KPART_VALUES / 4)];
@@ -1084,18 +1089,6 @@ __global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__r
 
 }  // namespace bf16path
 
-int ns_sym_splits(int64_t tiles_w, int64_t units, int64_t max_splits, int *units_per_split) {
-    int64_t splits = 1;
-    if (tiles_w > 0 && tiles_w < 128) splits = std::min<int64_t>(std::min<int64_t>(256 / tiles_w, units / 4), max_splits);
-    if (splits < 2) {
-        *units_per_split = static_cast<int>(units);
-        return 1;
-    }
-    const int64_t ups = (units + splits - 1) / splits;
-    *units_per_split = static_cast<int>(ups);
-    return static_cast<int>((units + ups - 1) / ups);
-}
-
 hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const Geom &g, const Work &w,
                                 const NsStep &p, hipStream_t st) {
     using namespace bf16path;
@@ -1103,19 +1096,27 @@ hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const 
         using C = Cfg;
         const int64_t nt = g.sp / C::BM;
         const int64_t tiles = nt * (nt + 1) / 2;
+        const int64_t all = tiles * nmat;
         const int splits = kind == GRAM ? p.gram_splits : p.poly_splits;
-        const int64_t nblocks = tiles * nmat * splits;
-        const dim3 grid(static_cast<unsigned>(nblocks)), block(C::NT);
-        if (kind == GRAM)
-            ns_sym_kernel<C, GRAM><<<grid, block, 0, st>>>(g, w, p, tiles, nblocks);
-        else
-            ns_sym_kernel<C, POLY><<<grid, block, 0, st>>>(g, w, p, tiles, nblocks);
-        if (splits > 1) {
-            const dim3 rgrid(static_cast<unsigned>(tiles * nmat * 64));
+        const int units = kind == GRAM ? p.gram_units : p.poly_units;
+        // tiles [0, from) whole, [from, all) split over K (none when splits == 1)
+        const int64_t from = splits > 1 ? std::min<int64_t>(std::max<int64_t>(p.split_from, 0), all) : all;
+        auto launch = [&](int64_t base, int64_t count, int sp) {
+            const int64_t nblocks = count * sp;
+            const dim3 grid(static_cast<unsigned>(nblocks)), block(C::NT);
             if (kind == GRAM)
-                sym_reduce_kernel<GRAM><<<rgrid, dim3(256), 0, st>>>(g, w, p, tiles);
+                ns_sym_kernel<C, GRAM><<<grid, block, 0, st>>>(g, w, p, tiles, nblocks, base, count, sp, units);
             else
-                sym_reduce_kernel<POLY><<<rgrid, dim3(256), 0, st>>>(g, w, p, tiles);
+                ns_sym_kernel<C, POLY><<<grid, block, 0, st>>>(g, w, p, tiles, nblocks, base, count, sp, units);
+        };
+        if (from > 0) launch(0, from, 1);
+        if (from < all) {
+            launch(from, all - from, splits);
+            const dim3 rgrid(static_cast<unsigned>((all - from) * 64));
+            if (kind == GRAM)
+                sym_reduce_kernel<GRAM><<<rgrid, dim3(256), 0, st>>>(g, w, p, tiles, from, splits);
+            else
+                sym_reduce_kernel<POLY><<<rgrid, dim3(256), 0, st>>>(g, w, p, tiles, from, splits);
         }
         return hipGetLastError();
     }

@@ -221,11 +221,19 @@ Geom make_geom(int64_t rows, int64_t cols) {
     return g;
 }
 
-// Split-K of the bf16 Gram and A^2 products of a group of `group_n` matrices
-// of geometry g (all 1 on the fp32 path).
+// Split-K of the bf16 Gram and A^2 products of a group (all 1 on the fp32
+// path).  The group's lower-triangle tiles, counted in the order (matrix,
+// tile of the matrix) over all its matrices, from `from` on run with K split
+// into ranges (gram / poly of them, of gram_units / poly_units x 128), their
+// fp32 partial tiles (kpart(n) bytes in a chunk of n matrices) summed in range order
+// by a reduce.  Depends only on the shape and the group size, so every
+// chunking of a group (and muon_step_noalloc) splits the same tiles alike.
 struct Splits {
     int gram = 1, gram_units = 0, poly = 1, poly_units = 0;
-    int max() const { return std::max(gram, poly); }
+    int64_t from = 0;
+    size_t per_matrix = 0;  // partial bytes per matrix of a chunk (every tile split)
+    size_t fixed = 0;       // partial bytes of a chunk holding the split tail tiles
+    size_t kpart(int64_t n) const { return per_matrix * static_cast<size_t>(n) + fixed; }
 };
 
 int64_t sym_tiles(const Geom &g) {
@@ -233,19 +241,65 @@ int64_t sym_tiles(const Geom &g) {
     return nt * (nt + 1) / 2;
 }
 
+constexpr size_t kPartTileBytes = size_t(256) * 256 * 4;  // one fp32 partial tile
+constexpr int64_t kCUs = 256;                              // workgroups in one wave (one per CU)
+
+// Ranges for `count` tiles of K extent `units` x 128 that otherwise run as
+// the last, partial wave of a launch (whole: as the whole launch).  Model in
+// microseconds, from the kernels' measured rates: a 256 x 256 tile takes 3.5
+// per 128 of K; a split piece adds 3 to start and 13 to store its fp32
+// partial tile (a wave of 256 pieces moves 64 MB); the reduce costs 5 plus
+// 0.055 per piece; splitting only the tail waits for the whole tiles' launch
+// to drain (0.1 tile).  The S (at most max_splits, each range at least 512 of
+// K) with the least time is taken if it saves a tenth of a tile (of the one
+// wave when whole), else 1.  *ups receives the range length (x 128).
+int tail_splits(int64_t count, int64_t units, int64_t max_splits, bool whole, int *ups) {
+    const double tile = 3.5 * static_cast<double>(units);
+    int best = 1;
+    double best_t = 0.9 * tile;
+    for (int64_t sp = 2; sp <= std::min<int64_t>(max_splits, units / 4); ++sp) {
+        const int64_t u = (units + sp - 1) / sp;
+        const int64_t real = (units + u - 1) / u;  // ranges actually used
+        const double waves = static_cast<double>((count * real + kCUs - 1) / kCUs);
+        const double t = waves * (tile / static_cast<double>(real) + 16.0) + 5.0 +
+                         0.055 * static_cast<double>(count * real) + (whole ? 0.0 : 0.1 * tile);
+        if (t < best_t) {
+            best_t = t;
+            best = static_cast<int>(real);
+        }
+    }
+    *ups = static_cast<int>(best > 1 ? (units + best - 1) / best : units);
+    return best;
+}
+
 Splits plan_splits(const Geom &g, bool bf16, int64_t group_n) {
     Splits sp;
     if (!bf16) return sp;
-    const int64_t w = sym_tiles(g) * group_n;
+    const int64_t tiles = sym_tiles(g);
+    const int64_t w = tiles * group_n;
     // K extents of the loops (the true length rounded up to 128), in units of 128
     const int64_t gram_k = std::min(g.lp, round_up(g.l, 128)) / 128;
     const int64_t poly_k = std::min(g.sp, round_up(g.s, 128)) / 128;
-    // the partial tiles take at most half of a matrix's own workspace
+    // partial tiles take at most half of a matrix's own workspace: per matrix
+    // when every tile of the group is split, in all when only the tail is
     const size_t x = static_cast<size_t>(g.sp * g.lp), a = static_cast<size_t>(g.sp * g.sp);
-    const size_t per_split = static_cast<size_t>(sym_tiles(g)) * 256 * 256 * 4;
-    const int64_t max_splits = static_cast<int64_t>((x * 5 + a * 4) / 2 / per_split);
-    sp.gram = muon::ns_sym_splits(w, gram_k, max_splits, &sp.gram_units);
-    sp.poly = muon::ns_sym_splits(w, poly_k, max_splits, &sp.poly_units);
+    const int64_t max_pieces = static_cast<int64_t>((x * 5 + a * 4) / 2 / kPartTileBytes);
+    // a group under half a wave splits every tile; a larger one only the tiles
+    // of its last, partial wave
+    const bool whole = w < kCUs / 2;
+    const int64_t count = whole ? w : w % kCUs;
+    const int64_t max_splits = whole ? max_pieces / tiles : (count > 0 ? max_pieces / count : 0);
+    sp.from = w;
+    if (count == 0 || max_splits < 2) return sp;
+    sp.gram = tail_splits(count, gram_k, max_splits, whole, &sp.gram_units);
+    sp.poly = tail_splits(count, poly_k, max_splits, whole, &sp.poly_units);
+    if (sp.gram == 1 && sp.poly == 1) return sp;
+    const size_t piece = static_cast<size_t>(std::max(sp.gram, sp.poly)) * kPartTileBytes;
+    sp.from = w - count;
+    if (whole)
+        sp.per_matrix = static_cast<size_t>(tiles) * piece;
+    else
+        sp.fixed = static_cast<size_t>(count) * piece;
     return sp;
 }
 
@@ -269,11 +323,10 @@ struct GroupPlan {
 // Geometry of W for a member of the group: rows <= cols (flat) or rows > cols.
 Geom run_geom(const Geom &g, bool tall) { return tall ? make_geom(g.l, g.s) : make_geom(g.s, g.l); }
 
-// Bytes of NS workspace one matrix of geometry g needs.
-size_t per_matrix_bytes(const Geom &g, bool bf16, int splits) {
+// Bytes of NS workspace one matrix of geometry g needs (without split-K partials).
+size_t per_matrix_bytes(const Geom &g, bool bf16) {
     const size_t x = static_cast<size_t>(g.sp * g.lp), a = static_cast<size_t>(g.sp * g.sp);
-    return (bf16 ? (x * (2 + 2 + 1) + a * (2 + 2)) : (x * (4 + 4) + a * (4 + 4 + 4))) +
-           muon::ns_kpart_bytes(sym_tiles(g), 1, splits);
+    return bf16 ? (x * (2 + 2 + 1) + a * (2 + 2)) : (x * (4 + 4) + a * (4 + 4 + 4));
 }
 
 size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
@@ -283,7 +336,7 @@ struct Layout {
     bool has_xf, has_kp;
 };
 
-Layout chunk_layout(const Geom &g, bool bf16, int64_t n, int splits) {
+Layout chunk_layout(const Geom &g, bool bf16, int64_t n, size_t kpart_bytes) {
     const size_t x = static_cast<size_t>(g.sp * g.lp) * n, a = static_cast<size_t>(g.sp * g.sp) * n;
     Layout L{};
     size_t off = 0;
@@ -306,9 +359,8 @@ Layout chunk_layout(const Geom &g, bool bf16, int64_t n, int splits) {
         L.ab = off; off = align_up(off + a * 4);
         L.bb = off; off = align_up(off + a * 4);
     }
-    const size_t kp = muon::ns_kpart_bytes(sym_tiles(g), n, splits);
-    L.has_kp = kp > 0;
-    L.kp = off; off = align_up(off + kp);
+    L.has_kp = kpart_bytes > 0;
+    L.kp = off; off = align_up(off + kpart_bytes);
     L.total = off;
     return L;
 }
@@ -353,18 +405,18 @@ muon_status plan_groups(const muon_matrix *mats, int64_t count, int32_t precisio
         const bool bf16 = gp.bf16;
         const int64_t n_all = static_cast<int64_t>(gp.members.size());
         gp.splits = plan_splits(gp.g, bf16, n_all);
-        const int sm = gp.splits.max();
-        const size_t per = per_matrix_bytes(gp.g, bf16, sm);
+        const Splits &sm = gp.splits;
+        const size_t per = per_matrix_bytes(gp.g, bf16) + sm.per_matrix;
         int64_t n = n_all;
         if (cap) {
-            const size_t one = chunk_layout(gp.g, bf16, 1, sm).total;
+            const size_t one = chunk_layout(gp.g, bf16, 1, sm.kpart(1)).total;
             if (one > cap) {
                 set_msg(msg, msg_cap, "a %lld x %lld matrix needs %zu bytes of workspace, above the cap %zu",
                         (long long)gp.g.s, (long long)gp.g.l, one, cap);
                 return MUON_ERR_OUT_OF_MEMORY;
             }
-            n = std::min<int64_t>(n, std::max<int64_t>(1, static_cast<int64_t>(cap / per)));
-            while (n > 1 && chunk_layout(gp.g, bf16, n, sm).total > cap) --n;
+            n = std::min<int64_t>(n, std::max<int64_t>(1, static_cast<int64_t>((cap > sm.fixed ? cap - sm.fixed : 0) / per)));
+            while (n > 1 && chunk_layout(gp.g, bf16, n, sm.kpart(n)).total > cap) --n;
         }
         // Keep every grouped launch inside a 32-bit grid.
         const int64_t apply_tiles = (gp.g.sp / muon::kTile) * (gp.g.lp / muon::kTile);
@@ -374,7 +426,7 @@ muon_status plan_groups(const muon_matrix *mats, int64_t count, int32_t precisio
                           muon::nesterov_blocks_per_mat(run_geom(gp.g, true), &rpb, &tc));
         n = std::min<int64_t>(n, std::max<int64_t>(1, ((int64_t(1) << 31) - 1) / gp.bpm));
         gp.chunk = n;
-        *ws_bytes = std::max(*ws_bytes, chunk_layout(gp.g, bf16, n, sm).total);
+        *ws_bytes = std::max(*ws_bytes, chunk_layout(gp.g, bf16, n, sm.kpart(n)).total);
         *partial_count = std::max(*partial_count, static_cast<size_t>(n) * gp.bpm);
         *max_chunk = std::max(*max_chunk, n);
     }
@@ -565,8 +617,8 @@ struct CallMem {
 };
 
 // Work view of a chunk laid out at the workspace base.
-Work chunk_work(const CallMem &mem, const Geom &g, bool bf16, int64_t n, int bpm, int splits) {
-    const Layout L = chunk_layout(g, bf16, n, splits);
+Work chunk_work(const CallMem &mem, const Geom &g, bool bf16, int64_t n, int bpm, size_t kpart_bytes) {
+    const Layout L = chunk_layout(g, bf16, n, kpart_bytes);
     char *base = mem.ws;
     Work w{};
     w.xf = L.has_xf ? reinterpret_cast<float *>(base + L.xf0) : nullptr;
@@ -666,8 +718,8 @@ void ns_work(int stage, const Geom &g, bool bf16, int n, bool ns_out, int psize,
 // separate pass applies the decay + update.
 muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom &gx, Work &w, bool bf16,
                    const muon_hparams *hp, bool update, int param_bf16, bool any_ns_out, float d, float s,
-                   hipStream_t st, const Splits &sp, const Run *runs, int nruns, bool params_aligned16 = false,
-                   int partial_bpm = 0, bool outs_aligned16 = false) {
+                   hipStream_t st, const Splits &sp, const Run *runs, int nruns, int64_t chunk_tile0 = 0,
+                   bool params_aligned16 = false, int partial_bpm = 0, bool outs_aligned16 = false) {
     const bool unit_rms = update && hp->scale_mode == MUON_SCALE_UNIT_RMS;
     // the geometry the product launches see: W's own for a chunk of one run (the
     // fused update needs its orientation), X's otherwise
@@ -721,6 +773,7 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
         p.gram_units = sp.gram_units;
         p.poly_splits = sp.poly;
         p.poly_units = sp.poly_units;
+        p.split_from = sp.from - chunk_tile0;  // the launch clamps it to the chunk
         for (int kind = 0; kind < 3; ++kind) {
             const int stage = kind == 0 ? ST_GRAM : kind == 1 ? ST_POLY : (p.final_update ? ST_APPLY_UPDATE : ST_APPLY);
             double fl = 0, by = 0;
@@ -884,7 +937,7 @@ muon_status step_impl(muon_context *ctx, const muon_matrix *mats, int64_t count,
                 const int64_t k0 = std::max<int64_t>(c0, gp.n_flat) - c0;
                 runs[nruns++] = Run{k0, n - k0, run_geom(gp.g, true)};
             }
-            Work w = chunk_work(mem, gp.g, bf16, n, gp.bpm, gp.splits.max());
+            Work w = chunk_work(mem, gp.g, bf16, n, gp.bpm, gp.splits.kpart(n));
             const double gsz = gp.grad_dtype == MUON_BF16 ? 2.0 : 4.0;
             for (int r = 0; r < nruns; ++r) {
                 const Run &run = runs[r];
@@ -909,7 +962,7 @@ muon_status step_impl(muon_context *ctx, const muon_matrix *mats, int64_t count,
                 if (e != hipSuccess) return hip_fail(ctx, e, "norm launch");
             }
             s = run_ns(ctx, dd, n, gp.g, w, bf16, hp, true, gp.param_dtype == MUON_BF16, any_out, d, sc, st,
-                       gp.splits, runs, nruns, params_aligned, gp.bpm, outs_aligned);
+                       gp.splits, runs, nruns, c0 * sym_tiles(gp.g), params_aligned, gp.bpm, outs_aligned);
             if (s != MUON_OK) return s;
         }
         pos += static_cast<size_t>(n_all);
@@ -1077,7 +1130,7 @@ muon_status muon_ns_only(muon_context *ctx, const float *n_in, float *x_out, int
     const Geom g = make_geom(rows, cols);
     const bool bf16 = use_bf16(hp->ns_precision, g.s);
     const Splits sp = plan_splits(g, bf16, 1);
-    const size_t need = chunk_layout(g, bf16, 1, sp.max()).total;
+    const size_t need = chunk_layout(g, bf16, 1, sp.kpart(1)).total;
     if (ctx->cap && need > ctx->cap)
         return fail(ctx, MUON_ERR_OUT_OF_MEMORY, "matrix needs %zu bytes of workspace, above the cap", need);
     DeviceGuard guard(ctx->device);
@@ -1094,7 +1147,7 @@ muon_status muon_ns_only(muon_context *ctx, const float *n_in, float *x_out, int
     const MatDesc *ddev = static_cast<const MatDesc *>(ctx->mat_desc.p);
     Work w = chunk_work(CallMem{static_cast<char *>(ctx->ws.p), static_cast<char *>(ctx->tabs.p),
                                 static_cast<double *>(ctx->call_nrm2.p)},
-                        g, bf16, 1, nb_blocks, sp.max());
+                        g, bf16, 1, nb_blocks, sp.kpart(1));
     const double elems = static_cast<double>(rows) * cols;
     hipError_t e = timed(ctx, ST_IMPORT, 0.0, elems * 8.0, st, [&] { return muon::launch_import_n(n_in, g, w, st); });
     if (e != hipSuccess) return hip_fail(ctx, e, "import launch");
@@ -1227,7 +1280,7 @@ muon_status muon_ns_stage(muon_context *ctx, int32_t stage, const float *x, cons
     }
     const Geom g = make_geom(s, l);
     const Splits sp = plan_splits(g, true, 1);
-    const size_t need = chunk_layout(g, true, 1, sp.max()).total;
+    const size_t need = chunk_layout(g, true, 1, sp.kpart(1)).total;
     if (ctx->cap && need > ctx->cap)
         return fail(ctx, MUON_ERR_OUT_OF_MEMORY, "matrix needs %zu bytes of workspace, above the cap", need);
     DeviceGuard guard(ctx->device);
@@ -1238,7 +1291,7 @@ muon_status muon_ns_stage(muon_context *ctx, int32_t stage, const float *x, cons
     if ((rs = ensure(ctx, ctx->call_nrm2, sizeof(double), "norm output")) != MUON_OK) return rs;
     Work w = chunk_work(CallMem{static_cast<char *>(ctx->ws.p), static_cast<char *>(ctx->tabs.p),
                                 static_cast<double *>(ctx->call_nrm2.p)},
-                        g, true, 1, 1, sp.max());
+                        g, true, 1, 1, sp.kpart(1));
     muon::NsStep p{};
     p.a = static_cast<float>(a);
     p.b = static_cast<float>(b);
@@ -1247,6 +1300,7 @@ muon_status muon_ns_stage(muon_context *ctx, int32_t stage, const float *x, cons
     p.gram_units = sp.gram_units;
     p.poly_splits = sp.poly;
     p.poly_units = sp.poly_units;
+    p.split_from = sp.from;
     hipError_t e = hipSuccess;
     if (stage != MUON_STAGE_POLY) e = muon::launch_import_pair(g, x, w, st);
     if (e == hipSuccess && stage != MUON_STAGE_GRAM)

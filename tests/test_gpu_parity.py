@@ -220,18 +220,58 @@ def test_step_zero_gradient_is_decay_only(ctx, torch_mod):
 
 def test_step_split_k_products(ctx, torch_mod):
     """Groups with few Gram / A^2 tiles and a long K split the products' K loop over
-    several workgroups and sum the partial tiles in a fixed order: a (1024, 1536) group
-    of both orientations (Gram and A^2 in 2 ranges), a 128 x 4096 matrix (Gram in 8),
+    several workgroups and sum the partial tiles in a fixed order: a (2048, 4096) group
+    of both orientations (Gram in 3 ranges), a 128 x 4096 matrix (Gram in 8),
     a ragged 300 x 3000 one (Gram in 5), against the oracle; the whole call twice,
     bit for bit."""
     S = synth.MatrixSpec
-    specs = [S(1024, 1536), S(1536, 1024), S(128, 4096), S(300, 3000)]
+    specs = [S(2048, 4096), S(4096, 2048), S(128, 4096), S(300, 3000)]
     say("step split-K products")
     _, dev1 = _run_step(ctx, torch_mod, specs, "bf16", seed=35)
     _, dev2 = _run_step(ctx, torch_mod, specs, "bf16", seed=35)
     for (p1, _, m1, o1), (p2, _, m2, o2) in zip(dev1, dev2):
         for a, b in ((p1, p2), (o1, o2)):
             assert np.array_equal(to_np(a).view(np.uint32), to_np(b).view(np.uint32))
+
+
+def test_step_split_k_tail(ctx, torch_mod):
+    """A group whose Gram tiles fill one wave of 256 workgroups and two tiles of a
+    second (43 x 768x8192: 258 tiles) splits only those last two tiles over K (16
+    ranges each, their partials reduced in order).  The first matrix (whole tiles only)
+    and the last one (holding the split tiles) against the oracle; the call repeated
+    bit for bit."""
+    ms = _ms()
+    rows, cols, count = 768, 8192, 43
+    wl = synth.Workload("t", 36, tuple(synth.MatrixSpec(rows, cols) for _ in range(count)))
+    hp = ms.make_hparams()
+    results = []
+    for rep in range(2):
+        host, dev, mats = {}, [], []
+        for i in range(count):
+            inp = synth.matrix_inputs(wl, i)
+            if i in (0, count - 1):
+                host[i] = inp
+            p = to_dev(inp["w"], torch_mod.bfloat16)
+            g = to_dev(inp["g"], torch_mod.bfloat16)
+            m = to_dev(inp["m"], torch_mod.float32)
+            o = torch_mod.empty((rows, cols), dtype=torch_mod.float32, device="cuda")
+            dev.append((p, g, m, o))
+            mats.append(ms.matrix(p, g, m, o))
+        ctx.muon_step(mats, hp)
+        torch_mod.cuda.synchronize()
+        results.append([(to_np(p), to_np(o)) for p, g, m, o in dev])
+        if rep == 0:
+            for i, inp in host.items():
+                ref = oracle.muon_step(inp["w"], inp["g"], inp["m"], param_bf16=True)
+                x = results[0][i][1]
+                err = rel_fro(x * math.sqrt(cols) * 0.2, ref["o"])
+                say(f"split-K tail: matrix {i} {rows}x{cols}: O rel err {err:.3e}")
+                assert err <= BF16_TOL
+                assert_bitexact(results[0][i][0], oracle.apply_update_f32(inp["w"], x, 0.02, 0.1, 0.2, True),
+                                f"param of matrix {i}")
+    for (p1, o1), (p2, o2) in zip(*results):
+        assert np.array_equal(p1.view(np.uint32), p2.view(np.uint32))
+        assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
 def test_step_is_deterministic(ctx, torch_mod):
