@@ -432,16 +432,21 @@ def main():
             tr = json.load(f)
         if tr.get("kernel_stage") == dom_name and tr.get("source_sha256") == gemm_source_sha():
             traffic = tr.get("hbm_bytes_per_launch")
+    # the bytes the dominant kernel must move at least once per launch (its
+    # operands once, X_lo, and X_hi + X_lo out for the apply product)
+    compulsory = dom["bytes"] / dom["launches"]
     if dom["flops"]:
         achieved = dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "flops_per_launch": dom["flops"] / dom["launches"], "avg_launch_ms": round(avg_ms, 4)}
+                "traffic_compulsory": compulsory, "flops_per_launch": dom["flops"] / dom["launches"],
+                "avg_launch_ms": round(avg_ms, 4)}
     else:
         achieved = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "bytes_per_launch": dom["bytes"] / dom["launches"], "avg_launch_ms": round(avg_ms, 4)}
+                "traffic_compulsory": compulsory, "bytes_per_launch": dom["bytes"] / dom["launches"],
+                "avg_launch_ms": round(avg_ms, 4)}
     elementwise = {}
     for k in ("momentum_nesterov", "normalize", "unit_rms", "update"):
         if k in stages and stages[k]["total_ms"] and stages[k]["bytes"]:
