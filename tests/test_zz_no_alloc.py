@@ -1,9 +1,10 @@
 """The allocation-free step muon_step_noalloc (for callers that cannot allocate
-device memory) against muon_step on the same inputs, through the C ABI: two
-calls in a row, the second with a smaller input, every output bit for bit
-(both entry points run the same kernels on every matrix; only the chunking of
-a group differs, and no result depends on it); then a call that cannot fit
-the fixed scratch, which must be refused before anything is enqueued."""
+device memory) against muon_step on the same inputs, through the C ABI: calls
+in a row, the second with a smaller input, every output bit for bit (both
+entry points run the same kernels on every matrix; only the chunking of a
+group differs, and no result depends on it, split-K tiles included); then a
+call that cannot fit the fixed scratch, which must be refused before anything
+is enqueued."""
 
 import numpy as np
 import pytest
@@ -55,10 +56,13 @@ def test_noalloc_matches_muon_step(torch_mod):
     first = [S(1024, 2048), S(1024, 2048), S(1024, 2048), S(2048, 1024), S(2048, 1024), S(300, 520, "f32", "bf16"),
              S(520, 300, prefill_momentum=True), S(2048, 7168), S(5, 3, "f32", "f32", law="gauss")]
     second = [S(300, 520), S(64, 128, "f32", "f32", law="gauss")]
+    # 43 x 768x8192: the group's last two Gram tiles run split over K; in the fixed
+    # scratch the group runs in chunks of three matrices, whose last chunk holds them
+    tail = [S(768, 8192)] * 43
     ctx = ms.Context(0)
     try:
         for k, (specs, seed, prec) in enumerate(((first, 201, ms.MUON_NS_BF16), (second, 202, ms.MUON_NS_BF16),
-                                                 (second, 203, ms.MUON_NS_F32))):
+                                                 (second, 203, ms.MUON_NS_F32), (tail, 205, ms.MUON_NS_BF16))):
             hosts = _hosts(specs, seed)
             hp = ms.make_hparams(ns_precision=prec)
             say(f"call {k + 1}: {len(specs)} matrices, muon_step_noalloc then muon_step")
