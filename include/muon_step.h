@@ -61,9 +61,10 @@ typedef enum muon_dtype {
 
 /* Arithmetic of the Newton-Schulz products.
  * MUON_NS_BF16: bf16 MFMA operands, fp32 accumulation; between iterations X
- *               is kept as hi = bf16(x) plus an 8-bit residual of x - hi
- *               (~16 significant bits), hi being the MFMA operand (relative
- *               Frobenius error vs fp64 ~1e-2).
+ *               is kept as a bf16 hi (x rounded to nearest, low halves
+ *               from 0x7f80 rounding up) plus an 8-bit residual, the pair
+ *               carrying x to 2^-16 of its magnitude; hi is the MFMA operand
+ *               (relative Frobenius error vs fp64 ~1e-2).
  *               Matrices whose smaller side is at most 16 use the fp32
  *               products instead (too few singular directions for the bf16
  *               rounding of X to average out; their cost is negligible).
@@ -277,13 +278,14 @@ muon_status muon_apply_update(muon_context *ctx, void *param, int32_t param_dtyp
  * split into its three products).  X is s x l with 1 <= s <= l (X's own
  * orientation; muon_step transposes W with rows > cols into it).  All
  * pointers are device fp32, row-major; out must not overlap the inputs.
- *   MUON_STAGE_GRAM:  x (s x l) -> out (s x s):  A = X_hi X_hi^T, X_hi =
- *                     bf16(x); fp32 accumulation, A rounded to bf16.
+ *   MUON_STAGE_GRAM:  x (s x l) -> out (s x s):  A = X_hi X_hi^T, X_hi the
+ *                     bf16 hi of x as stored in the pair (MUON_NS_BF16);
+ *                     fp32 accumulation, A rounded to bf16.
  *   MUON_STAGE_POLY:  m (s x s, symmetric; rounded to bf16 as A) -> out
  *                     (s x s):  B = b A + c A A, fp32 accumulation, B
  *                     rounded to bf16.
  *   MUON_STAGE_APPLY: m (s x s, symmetric; rounded to bf16 as B), x (s x l,
- *                     kept as X_hi = bf16(x) plus its 8-bit residual) ->
+ *                     kept as the pair X_hi plus its 8-bit residual) ->
  *                     out (s x l):  X' = a X + B X_hi (aX from hi + residual,
  *                     fp32 accumulation), as the value of the pair X' is
  *                     stored in.

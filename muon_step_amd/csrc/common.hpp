@@ -39,7 +39,8 @@ struct Geom {
 // Workspace of one chunk: matrix e of the chunk owns
 //   xf      + e*x_stride  fp32 X (sp x lp), read by the current step (fp32 path)
 //   xf_next + e*x_stride  where the current step writes X (fp32 path)
-//   xb      + e*x_stride  X_hi = bf16(X), the MFMA operand (bf16 path)
+//   xb      + e*x_stride  X_hi, X rounded to bf16 by the pair codec below: the
+//                         MFMA operand (bf16 path)
 //   xb_next + e*x_stride  where the current step writes X_hi: the product B X
 //                         reads whole column panels of X, so X_hi is
 //                         double-buffered
@@ -98,129 +99,62 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
-// A float kept as hi = bf16(x) and a signed 8-bit residual q:
-//   x ~= hi + q * 2^(e - 15),  e the exponent of hi,  q = rne((x - hi) 2^(15 - e))
-// clamped to [-128, 127].  x - hi is exact in fp32 and at most half a bf16
-// ulp (2^(e - 8)), so |q| <= 128 and the residual's rounding error is at most
-// 2^(e - 16), or 2^(e - 15) where q clamps: x is carried to 2^-15 relative
-// (2^-16 but for that clamp).  hi + q 2^(e - 15) spans at most 17 bits and is
-// exact in fp32.
-//
-// The unit 2^(e - 15) is never formed.  The codec works against a reference
-// float m whose exponent is e + 8 and whose mantissa is 0.5 (plus, in the
-// paired form, a few low bits that change nothing): m sits mid-binade with
-// ulp 2^(e - 15), so the single rounding of m + (x - hi) rounds x - hi to a
-// multiple of the unit (to nearest, ties to even q) and leaves q as the
-// difference of the two bit patterns; decoding adds q to m's bits and
-// subtracts m, both exact.  e is capped at 119 (|hi| < 2^120; above that only
-// hi's precision is kept, and infinite or NaN hi absorbs any residual); below
-// 2^-126 the unit is still consistent, with hi's precision the limit.
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-typedef int16_t s16x2 __attribute__((ext_vector_type(2)));
-constexpr uint32_t LO8_REF_ADD = 0x04400000u;  // exponent + 8, mantissa 0.5
-constexpr uint32_t LO8_EXP_CAP = 246u << 23;    // exponent field 246 (e = 119)
-
-// Reference bits for one hi given as fp32 bits.
-__device__ __forceinline__ uint32_t lo8_ref(uint32_t hf_bits) {
-    return min(hf_bits & 0x7f800000u, LO8_EXP_CAP) + LO8_REF_ADD;
-}
-// Reference bits for the two bf16 of one packed pair (element 0 in the low
-// half).  m1 keeps element 0's capped exponent in its bits 14..7: mantissa
-// bits far below m's top bit that leave its binade, its ulp and its last bit
-// (hence ties) unchanged.
-__device__ __forceinline__ void lo8_ref2(uint32_t h2, uint32_t *m0, uint32_t *m1) {
-    const u16x2 cap = {static_cast<uint16_t>(LO8_EXP_CAP >> 16), static_cast<uint16_t>(LO8_EXP_CAP >> 16)};
-    const uint32_t eb = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, h2 & 0x7f807f80u), cap));
-    *m0 = (eb << 16) + LO8_REF_ADD;
-    *m1 = eb + LO8_REF_ADD;
-}
-// q of x against hi (as a float) and its reference bits.
-__device__ __forceinline__ int lo8_q(float x, float hf, uint32_t mb) {
-    const float t = (x - hf) + __uint_as_float(mb);  // x - hf exact; one rounding to the unit
-    return min(max(static_cast<int>(__float_as_uint(t) - mb), -128), 127);
-}
-// The residual q * 2^(e - 15) from q and the reference bits.
-__device__ __forceinline__ float lo8_value(int q, uint32_t mb) {
-    return __uint_as_float(mb + static_cast<uint32_t>(q)) - __uint_as_float(mb);
+// A float kept as a bf16 hi and an 8-bit residual lo, by integer arithmetic
+// on its bit pattern b (monotonic in |x|, sign bit apart):
+//   hi = bits 16..31 of b + 0x8080,   lo = bits 8..15 of b + 0x80,
+//   decoded b' = (hi << 16) + (int8(lo) << 8),   |b' - b| <= 0x80.
+// lo is the next byte of b rounded to 24 bits (to nearest on the pattern,
+// halves up), read as a signed offset from hi, so x is carried to 2^-16 of
+// its magnitude at every finite value, subnormals included: 0x80 units of the
+// last place of an fp32 significand.  hi is x rounded to the nearest bf16,
+// except that low halves in [0x7f80, 0x8000] round up: at most 0.502 ulp from
+// x.  All-zero bytes decode to +0, and a residual of 0 to hi itself.  Before
+// the addition b is capped at 0x7fff7f7f as a signed integer and the sum
+// saturates as an unsigned one, so the carry never reaches the sign bit and
+// every quiet NaN stays a NaN; finite values within 0x80 units of the largest
+// float get an infinite hi and still decode to themselves.  Signalling NaNs
+// with a payload below 0x7f80 (never the result of arithmetic) would decode
+// as infinities; data read from memory passes __builtin_canonicalizef first.
+__device__ __forceinline__ uint32_t pair_sum(float x) {
+    const int32_t b = __builtin_elementwise_min(__float_as_int(x), 0x7fff7f7f);
+    return __builtin_elementwise_add_sat(static_cast<uint32_t>(b), 0x8080u);
 }
 __device__ __forceinline__ void split_bf16(float x, uint16_t *hi, uint8_t *lo) {
-    const uint16_t h = float_to_bf16_bits(x);
-    const uint32_t hb = static_cast<uint32_t>(h) << 16;
-    *hi = h;
-    *lo = static_cast<uint8_t>(lo8_q(x, __uint_as_float(hb), lo8_ref(hb)) & 0xff);
+    const uint32_t y = pair_sum(x);
+    *hi = static_cast<uint16_t>(y >> 16);
+    *lo = static_cast<uint8_t>(((y >> 8) & 0xffu) ^ 0x80u);
+}
+// b' from the bytes P = hi << 16 | lo << 8: (P ^ 0x8000) - 0x8000 in one
+// v_xad_u32 (a VOP3 operation reads at most one scalar or constant operand, so
+// the compiler would otherwise split it; -0x8000 is given in a VGPR).
+__device__ __forceinline__ float join_bits(uint32_t p) {
+    uint32_t r;
+    asm("v_xad_u32 %0, %1, %2, %3" : "=v"(r) : "v"(p), "s"(0x8000u), "v"(0xffff8000u));
+    return __uint_as_float(r);
 }
 __device__ __forceinline__ float join_bf16(uint16_t hi, uint8_t lo) {
-    const uint32_t hb = static_cast<uint32_t>(hi) << 16;
-    return __uint_as_float(hb) + lo8_value(static_cast<int8_t>(lo), lo8_ref(hb));
+    return join_bits((static_cast<uint32_t>(hi) << 16) | (static_cast<uint32_t>(lo) << 8));
 }
-// Four consecutive values: hi as packed bf16 pairs, the residuals as four
-// bytes of one word (value k in byte k).  BOUNDED: the caller guarantees
-// |x| < 2^120 or a non-finite hi (a Newton-Schulz iterate of a normalised
-// matrix), so the exponent cap is not needed: for infinite or NaN hi the
-// reference overflows, q is meaningless and the decode (which caps) adds a
-// finite residual to a non-finite hi.
-template <bool BOUNDED = false>
+// Four consecutive values: hi as packed bf16 pairs (value 2k in the low half
+// of word k), the residuals as the four bytes of one word (value k in byte k).
 __device__ __forceinline__ void split_bf16x4(const floatx4 &v, u32x2 *hi, uint32_t *lo) {
-    u32x2 h;
-    h[0] = pack_bf16x2(v[0], v[1]);
-    h[1] = pack_bf16x2(v[2], v[3]);
-    // opaque to the optimiser, which would otherwise convert each value to
-    // bf16 a second time to get its float hi
-    asm volatile("" : "+v"(h[0]), "+v"(h[1]));
-    *hi = h;
-    if (BOUNDED) {
-        // References with clear low halves: the low 16 bits of the rounded
-        // sum are then q itself (|q| <= 128 never borrows across bit 16), two
-        // of them gather into one register and one packed min clamps both
-        // (q >= -128 always holds).
-        u32x2 qq;
+    uint32_t y[4];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const uint32_t m0 = ((h[k] & 0x7f80u) << 16) + LO8_REF_ADD;
-            const uint32_t m1 = (h[k] & 0x7f800000u) + LO8_REF_ADD;
-            const float t0 = (v[2 * k] - __uint_as_float(h[k] << 16)) + __uint_as_float(m0);
-            const float t1 = (v[2 * k + 1] - __uint_as_float(h[k] & 0xffff0000u)) + __uint_as_float(m1);
-            // v_perm_b32 picks bytes of {src0, src1} (src1 = bytes 0..3)
-            const uint32_t g = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x05040100u);
-            const s16x2 c = {127, 127};
-            qq[k] = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(s16x2, g), c));
-        }
-        *lo = __builtin_amdgcn_perm(qq[1], qq[0], 0x06040200u);
-        return;
-    }
-    int q[4];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        uint32_t m0, m1;
-        lo8_ref2(h[k], &m0, &m1);
-        q[2 * k] = lo8_q(v[2 * k], __uint_as_float(h[k] << 16), m0);
-        q[2 * k + 1] = lo8_q(v[2 * k + 1], __uint_as_float(h[k] & 0xffff0000u), m1);
-    }
-    // v_perm_b32 picks bytes of {src0, src1} (src1 = bytes 0..3; 0x0c = zero)
-    const uint32_t p01 = __builtin_amdgcn_perm(static_cast<uint32_t>(q[1]), static_cast<uint32_t>(q[0]), 0x0c0c0400u);
-    const uint32_t p23 = __builtin_amdgcn_perm(static_cast<uint32_t>(q[3]), static_cast<uint32_t>(q[2]), 0x0c0c0400u);
-    *lo = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+    for (int k = 0; k < 4; ++k) y[k] = pair_sum(v[k]);
+    // v_perm_b32 picks bytes of {src0, src1} (src1 = bytes 0..3, src0 = 4..7)
+    (*hi)[0] = __builtin_amdgcn_perm(y[1], y[0], 0x07060302u);
+    (*hi)[1] = __builtin_amdgcn_perm(y[3], y[2], 0x07060302u);
+    const uint32_t l01 = __builtin_amdgcn_perm(y[1], y[0], 0x07060501u);  // bytes 1 of y0, y1
+    const uint32_t l23 = __builtin_amdgcn_perm(y[3], y[2], 0x07060501u);
+    *lo = __builtin_amdgcn_perm(l23, l01, 0x05040100u) ^ 0x80808080u;
 }
-// BOUNDED: the values were written by split_bf16x4<true> (|x| < 2^120 or a
-// non-finite hi), so the exponent cap is not needed either.
-template <bool BOUNDED = false>
 __device__ __forceinline__ floatx4 join_bf16x4(const u32x2 &h, uint32_t l) {
     floatx4 v;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        uint32_t m0, m1;
-        if (BOUNDED) {
-            const uint32_t eb = h[k] & 0x7f807f80u;
-            m0 = (eb << 16) + LO8_REF_ADD;
-            m1 = eb + LO8_REF_ADD;
-        } else {
-            lo8_ref2(h[k], &m0, &m1);
-        }
-        const int q0 = static_cast<int8_t>((l >> (16 * k)) & 0xffu);
-        const int q1 = static_cast<int8_t>((l >> (16 * k + 8)) & 0xffu);
-        v[2 * k] = __uint_as_float(h[k] << 16) + lo8_value(q0, m0);
-        v[2 * k + 1] = __uint_as_float(h[k] & 0xffff0000u) + lo8_value(q1, m1);
-    }
+    // bytes [0, l.k, h.lo16 of value k] with 0x0c selecting a zero byte
+    v[0] = join_bits(__builtin_amdgcn_perm(h[0], l, 0x0504000cu));
+    v[1] = join_bits(__builtin_amdgcn_perm(h[0], l, 0x0706010cu));
+    v[2] = join_bits(__builtin_amdgcn_perm(h[1], l, 0x0504020cu));
+    v[3] = join_bits(__builtin_amdgcn_perm(h[1], l, 0x0706030cu));
     return v;
 }
 

@@ -620,7 +620,7 @@ __global__ __launch_bounds__(256) void import_pair_kernel(Geom g, const float *_
     uint8_t *xl = static_cast<uint8_t *>(w.xl) + i * g.lp;
     for (int64_t j = threadIdx.x; j < g.lp; j += 256) {
         const float v = (i < g.s && j < g.l) ? x[i * g.l + j] : 0.0f;
-        split_bf16(v, xh + j, xl + j);
+        split_bf16(__builtin_canonicalizef(v), xh + j, xl + j);
     }
 }
 

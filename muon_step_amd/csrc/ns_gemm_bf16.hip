@@ -747,12 +747,11 @@ __device__ __forceinline__ void dma_x_round(char *dst, const XRows &x, int h, in
 // staged in `reg` (X_hi rows, 128 bytes each, in the first PAIR_HALF bytes;
 // X_lo rows, 64 bytes each, after).  While X still holds N, `a` is a inv_norm
 // (and B was scaled by inv_norm when it was formed).
-template <bool BOUNDED = false>
 __device__ __forceinline__ floatx4 apply_value(const floatx16 &acc, const char *reg, int lrow, int lcol, int c4,
                                                float a) {
     const u32x2 h = *reinterpret_cast<const u32x2 *>(reg + pair_offset(lrow, lcol));
     const uint32_t l = *reinterpret_cast<const uint32_t *>(reg + PAIR_HALF + lo8_offset(lrow, lcol));
-    const floatx4 x = join_bf16x4<BOUNDED>(h, l);
+    const floatx4 x = join_bf16x4(h, l);
     floatx4 v;
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(a, x[q], acc[4 * c4 + q]);
@@ -764,7 +763,7 @@ __device__ __forceinline__ floatx4 apply_value(const floatx16 &acc, const char *
 // for the row-contiguous pass.  All of the lane's reads precede its writes, and
 // one wave's LDS accesses execute in order, so no value is overwritten before
 // it is read.
-template <class C, bool BOUNDED = false>
+template <class C>
 __device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char *reg, float a, int lane) {
     const int lrow = lane & 31;
     floatx4 v[C::NI][4];
@@ -772,7 +771,7 @@ __device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char
     for (int ni = 0; ni < C::NI; ++ni)
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
-            v[ni][c4] = apply_value<BOUNDED>(accm[ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, a);
+            v[ni][c4] = apply_value(accm[ni], reg, lrow, ni * 32 + 8 * c4 + 4 * (lane >> 5), c4, a);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int ni = 0; ni < C::NI; ++ni)
@@ -786,31 +785,77 @@ __device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char
 }
 
 
+// DMA of round h's X_hi rows to hi and X_lo rows to lo (two staging places).
+__device__ __forceinline__ void dma_x_round_to(char *hi, char *lo, const XRows &x, int h, int lane) {
+    dma_bf16_rows<Cfg>(hi, x.hi + Cfg::EPI_ROWS * h * x.ld_hi, x.ld_hi, lane);
+    dma_lo8_rows<Cfg>(lo, x.lo + Cfg::EPI_ROWS * h * x.ld_lo, x.ld_lo, lane);
+}
+
+// The wave's 32 x 64 block of X' = a X + acc, X read from the pair staged at
+// (hi rows, lo rows) in the accumulator layout, encoded there and written
+// back over the very bytes each lane read (so no lane's write can meet
+// another lane's read); the lane's eight reads precede its writes.
+template <class C>
+__device__ __forceinline__ void stage_pair(const floatx16 (&accm)[C::NI], char *hi, char *lo, float a, int lane) {
+    const int lrow = lane & 31;
+    u32x2 h[C::NI][4];
+    uint32_t l[C::NI][4];
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
+            h[ni][c4] = *reinterpret_cast<const u32x2 *>(hi + pair_offset(lrow, lcol));
+            l[ni][c4] = *reinterpret_cast<const uint32_t *>(lo + lo8_offset(lrow, lcol));
+        }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const floatx4 x = join_bf16x4(h[ni][c4], l[ni][c4]);
+            floatx4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(a, x[q], accm[ni][4 * c4 + q]);
+            split_bf16x4(v, &h[ni][c4], &l[ni][c4]);
+        }
+#pragma unroll
+    for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const int lcol = ni * 32 + 8 * c4 + 4 * (lane >> 5);
+            *reinterpret_cast<u32x2 *>(hi + pair_offset(lrow, lcol)) = h[ni][c4];
+            *reinterpret_cast<uint32_t *>(lo + lo8_offset(lrow, lcol)) = l[ni][c4];
+        }
+    wait_lgkm0();  // the wave's writes land before its row-contiguous reads
+    asm volatile("" ::: "memory");
+}
+
 // Epilogue of an intermediate step: X' = a X + B X is written as the bf16 pair
 // (X'_hi to xb_next, X'_lo to xl in place).  Outside s x l it is zero without
 // a mask: X is zero there, so are the padded rows and columns of A and B, and
-// with them every term of X'.  Per round of
-// EPI_ROWS rows the wave's X_hi and X_lo rows arrive in a staging area by DMA;
-// the values are formed in the accumulator layout and rewritten there as fp32
-// rows, then read row-contiguously (16 lanes per row) so the stores move whole
-// rows.  Two staging areas: round 0's DMA was issued under the last stage of
-// the main loop, round 1's on entry, and the DMA of round h+2 once round h's
-// reads are done, so one round is always in flight.  Per round and lane:
-// EPI_ROWS/8 + EPI_ROWS/16 DMA instructions (X_hi, X_lo) and 2*EPI_ROWS/4
-// stores, unconditionally;
-// every vector-memory instruction retires in issue order, so the wait before
-// round h allows exactly the instructions issued after round h's DMA: round
-// h-1's stores and round h+1's DMA.
-template <bool BOUNDED>
+// with them every term of X'.  Per round of EPI_ROWS rows the wave's X_hi and
+// X_lo rows arrive by DMA in a staging place, the encoded X' pair replaces
+// them there (stage_pair) and is read back row-contiguously (16 lanes per
+// row) so the stores move whole rows.  A round takes 6 KB of the wave's 20 KB
+// (8 KB of each ring slot and 4 KB of lds_wbuf): rounds 0 and 1 were loaded
+// under the last stage of the main loop (slot 0, whose 2 KB tail holds round
+// 1's X_lo, and lds_wbuf, which the K loop does not use), round 2 is loaded
+// into slot 1 on entry and round 3 into round 0's place once round 0's rows
+// are read.  Every vector-memory instruction retires in issue order, so each
+// wait allows exactly what was issued after that round's DMA.
 __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::MI][Cfg::NI], const Geom &g,
                                                     const Work &w, const NsStep &p, const ApplyTile &t,
-                                                    char *const (&area)[2], int lane) {
+                                                    char *slot0, char *slot1, char *wb, int lane) {
     using C = Cfg;
     constexpr int ROUNDS = C::WM / C::EPI_ROWS;
-    constexpr int DMA_PER_ROUND = C::EPI_ROWS / 8 + C::EPI_ROWS / 16;
-    constexpr int STORES_PER_ROUND = 2 * (C::EPI_ROWS / 4);
+    constexpr int DMA = C::EPI_ROWS / 8 + C::EPI_ROWS / 16;  // X_hi, X_lo instructions per round
+    constexpr int STORES = 2 * (C::EPI_ROWS / 4);
     static_assert(ROUNDS == 4 && C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
-    static_assert(C::EPI_ROWS * 128 == PAIR_HALF, "X_hi and X_lo rows fill one staging area");
+    static_assert(C::EPI_ROWS * 128 == PAIR_HALF && C::EPI_BYTES == 8192, "a round's pair takes 6 KB");
+    static_assert(DMA + STORES + DMA + STORES + DMA < 64, "vmcnt range");
+    char *const hi[ROUNDS] = {slot0, wb, slot1, slot0};
+    char *const lo[ROUNDS] = {slot0 + PAIR_HALF, slot0 + PAIR_HALF + 2048, slot1 + PAIR_HALF, slot0 + PAIR_HALF};
     uint8_t *xl = static_cast<uint8_t *>(w.xl) + t.e * w.x_stride;
     uint16_t *xh_out = static_cast<uint16_t *>(w.xb_next) + t.e * w.x_stride;
     const XRows x = x_rows(g, w, t);
@@ -821,33 +866,31 @@ __device__ __forceinline__ void apply_epilogue_next(const floatx16 (&acc)[Cfg::M
     const uint32_t off_lo = static_cast<uint32_t>(rr * g.lp + 4 * chunk);
     const uint32_t off_hi = 2 * off_lo;
     const int64_t row0 = uniform64(t.row0), col0 = uniform64(t.col0);
-    dma_x_round(area[1], x, 1, lane);
+    dma_x_round_to(hi[2], lo[2], x, 2, lane);
 #pragma unroll
     for (int h = 0; h < ROUNDS; ++h) {
         if (h == 0)
-            fenced_wait_vmcnt<DMA_PER_ROUND>();
-        else if (h + 1 < ROUNDS)
-            fenced_wait_vmcnt<STORES_PER_ROUND + DMA_PER_ROUND>();
+            fenced_wait_vmcnt<2 * DMA>();  // rounds 1 and 2 may be in flight
+        else if (h == 1)
+            fenced_wait_vmcnt<DMA + STORES + DMA>();  // round 2, round 0's stores, round 3
+        else if (h == 2)
+            fenced_wait_vmcnt<STORES + DMA + STORES>();  // round 0's stores, round 3, round 1's stores
         else
-            fenced_wait_vmcnt<STORES_PER_ROUND>();
-        char *reg = area[h & 1];
-        stage_values<C, BOUNDED>(acc[h], reg, a, lane);
+            fenced_wait_vmcnt<2 * STORES>();  // rounds 1 and 2's stores
+        stage_pair<C>(acc[h], hi[h], lo[h], a, lane);
 #pragma unroll
         for (int r4 = 0; r4 < C::EPI_ROWS / 4; ++r4) {
-            const floatx4 v = *reinterpret_cast<const floatx4 *>(reg + epi_offset(4 * r4 + rr, chunk));
+            const int row = 4 * r4 + rr;
+            const u32x2 hv = *reinterpret_cast<const u32x2 *>(hi[h] + pair_offset(row, 4 * chunk));
+            const uint32_t lv = *reinterpret_cast<const uint32_t *>(lo[h] + lo8_offset(row, 4 * chunk));
             const int64_t base = (row0 + C::EPI_ROWS * h + 4 * r4) * g.lp + col0;
-            char *ph = reinterpret_cast<char *>(xh_out + base);
-            char *pl = reinterpret_cast<char *>(xl + base);
-            u32x2 hi;
-            uint32_t lo;
-            split_bf16x4<true>(v, &hi, &lo);  // |X'| <= ~1.2: X is normalised
-            store_saddr(ph, off_hi, hi);
-            store_saddr(pl, off_lo, lo);
+            store_saddr(reinterpret_cast<char *>(xh_out + base), off_hi, hv);
+            store_saddr(reinterpret_cast<char *>(xl + base), off_lo, lv);
         }
-        if (h + 2 < ROUNDS) {
-            wait_lgkm0();  // this round's LDS reads are done before the DMA refills the area
+        if (h == 0) {
+            wait_lgkm0();  // round 0's LDS reads are done before the DMA refills its place
             asm volatile("" ::: "memory");
-            dma_x_round(area[h & 1], x, h + 2, lane);
+            dma_x_round_to(hi[3], lo[3], x, 3, lane);
         }
     }
 }
@@ -995,7 +1038,7 @@ __device__ __forceinline__ void apply_epilogue_update_staged(const floatx16 (&ac
             dma_x_round(area[(h + 1) & 1], x, h + 1, lane);  // its area was last read in round h-1
             asm volatile("" ::: "memory");
         }
-        stage_values<C, true>(acc[h], reg, a, lane);
+        stage_values<C>(acc[h], reg, a, lane);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             if (half == 1) {
@@ -1029,9 +1072,7 @@ __device__ __forceinline__ void apply_epilogue_update_staged(const floatx16 (&ac
     }
 }
 
-// MODE 0: intermediate step (X' to the workspace); 4: the same after the first
-// step, where X is a Newton-Schulz iterate (|X| <= ~1.2), so its residual
-// decodes without the exponent cap; 1 / 2: last step with the
+// MODE 0: intermediate step (X' to the workspace); 1 / 2: last step with the
 // fused update of an fp32 / bf16 parameter; 3: the same for a bf16 parameter
 // through apply_epilogue_update_staged after the first step (NsStep::w_staged:
 // no transpose, s and l multiples of 256, 16-byte aligned parameters).  One epilogue per
@@ -1067,7 +1108,15 @@ __global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__r
         return ApplyTile{e, static_cast<int64_t>(ti) * C::BM + wm * C::WM,
                          static_cast<int64_t>(tj) * C::BN + wn * C::WN};
     };
-    auto pre_last = [&] { dma_x_round(epi_area<0>(wave), x_rows(g, w, tile_of()), 0, lane); };
+    // Before the last stage (slot 0 free): the first epilogue round into slot 0,
+    // and for MODE 0 the second too (its X_hi into lds_wbuf, its X_lo into the
+    // last 2 KB of the wave's part of slot 0).
+    auto pre_last = [&] {
+        const XRows xr = x_rows(g, w, tile_of());
+        dma_x_round(epi_area<0>(wave), xr, 0, lane);
+        if constexpr (MODE == 0)
+            dma_x_round_to(lds_wbuf + wave * 4096, epi_area<0>(wave) + PAIR_HALF + 2048, xr, 1, lane);
+    };
     main_loop<C, APPLY>(acc, src, static_cast<int>(k_extent(g.s, g.sp) / C::BK), wave, wm, wn, lane, pre_last);
     const ApplyTile t_ = tile_of();
 
@@ -1079,8 +1128,8 @@ __global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__r
     char *const area[2] = {epi_area<0>(wave), epi_area<1>(wave)};
     wait_lgkm0();
     stage_barrier();  // every wave is done with the operand ring
-    if constexpr (MODE == 0 || MODE == 4)
-        apply_epilogue_next<MODE == 4>(acc, g, w, p, t_, area, lane);
+    if constexpr (MODE == 0)
+        apply_epilogue_next(acc, g, w, p, t_, area[0], area[1], lds_wbuf + wave * 4096, lane);
     else if constexpr (MODE == 3)
         apply_epilogue_update_staged(acc, descs[e], g, w, p, t_, area, lds_wbuf + wave * 4096, lane);
     else
@@ -1123,9 +1172,7 @@ hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const 
     const int64_t tiles = (g.sp / Cfg::BM) * (g.lp / Cfg::BN);
     const int64_t nblocks = tiles * nmat;
     const dim3 grid(static_cast<unsigned>(nblocks)), block(Cfg::NT);
-    if (!p.final_update && !p.unnormalized)
-        ns_apply_kernel<4><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
-    else if (!p.final_update)
+    if (!p.final_update)
         ns_apply_kernel<0><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
     else if (p.param_bf16 && p.w_staged && !p.unnormalized)
         ns_apply_kernel<3><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);

@@ -47,3 +47,14 @@ def assert_bitexact(got, ref, what):
 
 def scale_of(rows, cols, gamma):
     return math.sqrt(max(rows, cols)) * gamma
+
+
+def pair_hi(x):
+    """The bf16 hi of the Newton-Schulz pair (hi, 8-bit residual) as the kernels
+    store X: the top 16 bits of x's fp32 bit pattern plus 0x8080 (x rounded to
+    the nearest bf16, low halves from 0x7f80 rounding up; the pattern capped at
+    0x7fff7f7f and the sum saturated, which only NaNs reach), as float32."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.int32).astype(np.int64)
+    y = np.minimum((np.minimum(b, 0x7FFF7F7F) & 0xFFFFFFFF) + 0x8080, 0xFFFFFFFF)
+    return ((y >> 16) << 16).astype(np.uint32).view(np.float32)
+

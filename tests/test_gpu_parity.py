@@ -82,10 +82,11 @@ def test_ns_only_spectral(ctx, torch_mod, shape, precision):
 @pytest.mark.parametrize("precision", ["bf16", "f32"])
 def test_ns_only_zero_steps_is_normalisation(ctx, torch_mod, precision):
     """With an empty schedule the output is X_0 = N / ||N||_F.  The fp32 path keeps X
-    in fp32 (error ~1e-7); the bf16 path keeps it as hi = bf16(x) plus an 8-bit
-    residual in steps of 2^-15 of hi's power of two: at most half a step (2^-16
-    of the element) where the residual fits, one step (2^-15) where it clamps,
-    and 2^-16 overall in Frobenius norm."""
+    in fp32 (error ~1e-7); the bf16 path keeps values as a bf16 hi plus an 8-bit
+    residual that together hold the fp32 bit pattern rounded to its top 24 bits,
+    within 0x80 units of the last place (2^-16 of the element).  N is stored so by
+    the momentum pass and X = N / ||N|| again by the normalisation: at most 2^-15
+    per element, and 2^-16 in Frobenius norm (the two roundings are independent)."""
     ms = _ms()
     n = np.random.default_rng(5).standard_normal((40, 90)).astype(np.float32)
     hp = ms.make_hparams(coeffs=[], ns_precision=ms.MUON_NS_BF16 if precision == "bf16" else ms.MUON_NS_F32)

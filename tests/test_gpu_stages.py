@@ -4,13 +4,13 @@ each run alone through the muon_ns_stage hook exactly as muon_step runs it for
 one matrix of that shape (same tiles, same split of long K loops), and compared
 element by element with fp64 products of the *same* bf16 operands:
 
-  GRAM   A = bf16(X_hi X_hi^T)            X_hi = bf16(X)
+  GRAM   A = bf16(X_hi X_hi^T)            X_hi the pair's hi of X
   POLY   B = bf16(b A + c A A)            A given, rounded to bf16
   APPLY  X' = a X + B X_hi                B rounded to bf16, X kept as hi + residual
 
 The bounds are those of the arithmetic: the final rounding to bf16 (half an
 ulp of an 8-bit significand: 2^-8 relative) or to the hi + residual pair
-(2^-15 relative), plus K 2^-24 times the
+(2^-16 relative, on the way in and out), plus K 2^-24 times the
 product of the absolute values for the fp32 accumulation over K terms (doubled
 to cover the split-K partial sums).  A dropped term, a wrong index, a
 transposed operand or a misplaced tile breaks them by orders of magnitude.
@@ -19,7 +19,7 @@ Mirrored elements of A and B must be exactly symmetric."""
 import numpy as np
 import pytest
 
-from gpu_util import say, to_dev, to_np
+from gpu_util import pair_hi, say, to_dev, to_np
 from oracle import bf16_round_f32
 
 pytestmark = pytest.mark.gpu
@@ -94,7 +94,7 @@ def test_gram_stage(ctx, torch_mod, shape):
     ctx.muon_ns_stage(ms.MUON_STAGE_GRAM, out, x=to_dev(x, torch_mod.float32))
     torch_mod.cuda.synchronize()
     got = to_np(out)
-    xh = bf16_round_f32(x).astype(np.float64)
+    xh = pair_hi(x).astype(np.float64)
     exact = xh @ xh.T
     absprod = np.abs(xh) @ np.abs(xh).T
     say(f"gram {shape}")
@@ -136,13 +136,62 @@ def test_apply_stage(ctx, torch_mod, shape):
     torch_mod.cuda.synchronize()
     got = to_np(out)
     bb = bf16_round_f32(b_in).astype(np.float64)
-    xh = bf16_round_f32(x).astype(np.float64)
+    xh = pair_hi(x).astype(np.float64)
     x64 = x.astype(np.float64)
     exact = a * x64 + bb @ xh
     absprod = np.abs(bb) @ np.abs(xh)
-    # X as hi + residual carries x to 2^-15 (2^-16 unless the residual clamps), and
-    # so does the pair X' is stored in; then the fp32 accumulation and the fma
-    bound = (2.0 ** -15 * (abs(a) * np.abs(x64) + 1.01 * np.abs(exact)) + 2.02 * s * U * absprod
+    # X as hi + residual carries x to 2^-16 of its magnitude, and so does the pair
+    # X' is stored in; then the fp32 accumulation and the fma
+    bound = (1.01 * 2.0 ** -16 * (abs(a) * np.abs(x64) + np.abs(exact)) + 2.02 * s * U * absprod
              + 2.0 * U * np.abs(exact) + 1e-37)
     say(f"apply {shape}")
     _check(got, exact, bound, "X'")
+
+
+def _pair_round_trip(x):
+    """Emulated decode(encode(x)) of the pair codec, on fp32 bit patterns: hi = top
+    16 bits of b + 0x8080 (b capped at 0x7fff7f7f, the sum saturating), residual
+    = bits 8..15 of b + 0x80 read as a signed byte, value (hi << 16) + (q << 8)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.int32).astype(np.int64)
+    y = np.minimum((np.minimum(b, 0x7FFF7F7F) & 0xFFFFFFFF) + 0x8080, 0xFFFFFFFF)
+    hi = y >> 16
+    q = (((y >> 8) & 0xFF) ^ 0x80).astype(np.uint8).view(np.int8).astype(np.int64)
+    return ((((hi << 16) + (q << 8)) & 0xFFFFFFFF).astype(np.uint32)).view(np.float32)
+
+
+def test_pair_codec_round_trip(ctx, torch_mod):
+    """X' = 1 X + 0 X_hi through the apply stage returns, for every finite input
+    whose hi stays finite, the decode of its encoding in the (hi, residual) pair,
+    bit for bit (-0 comes back as +0: the product term is +0).  The inputs cover
+    zeros, subnormals, every exponent, and low halves of the bit pattern at the
+    rounding boundaries of hi (0x7f80, 0x8000) and of the residual (0x7f, 0x80)."""
+    import muon_step_amd as ms
+    r = np.random.default_rng(77)
+    pats = [0x00000000, 0x80000000, 0x00000001, 0x80000001, 0x000000FF, 0x00007F80, 0x00008000,
+            0x007FFFFF, 0x807FFFFF, 0x00800000, 0x7F7F7F7F, 0xFF7F7F7F]
+    for e in range(1, 255, 2):
+        for low in (0x0000, 0x007F, 0x0080, 0x00FF, 0x7F7F, 0x7F80, 0x7FFF, 0x8000, 0x8001, 0x807F, 0x8080, 0xFFFF):
+            m = (int(r.integers(0, 128)) << 16) | low
+            for sign in (0, 1):
+                pats.append((sign << 31) | (e << 23) | m)
+    pats = np.array(pats, dtype=np.uint64)
+    pats = pats[(pats & 0x7FFFFFFF) < 0x7F7F7F80]          # hi stays finite (0 x inf would be NaN)
+    s, l = 32, 128
+    rand = (r.standard_normal(s * l - pats.size) * np.exp2(r.integers(-60, 60, s * l - pats.size))).astype(np.float32)
+    x = np.concatenate([pats.astype(np.uint32).view(np.float32), rand]).reshape(s, l)
+    out = torch_mod.empty((s, l), dtype=torch_mod.float32, device="cuda")
+    ctx.muon_ns_stage(ms.MUON_STAGE_APPLY, out, x=to_dev(x, torch_mod.float32),
+                      m=to_dev(np.zeros((s, s), np.float32), torch_mod.float32), a=1.0)
+    torch_mod.cuda.synchronize()
+    got = to_np(out)
+    want = _pair_round_trip(x)
+    want = np.where(want == 0, np.float32(0.0), want)       # -0 + (+0) = +0
+    say(f"pair codec: {x.size} values")
+    bad = got.view(np.uint32) != want.view(np.uint32)
+    if np.any(bad):
+        i = np.argwhere(bad)[:5]
+        raise AssertionError(f"{int(bad.sum())} values differ, first "
+                             f"{[(hex(int(x.view(np.uint32)[tuple(k)])), hex(int(got.view(np.uint32)[tuple(k)])), hex(int(want.view(np.uint32)[tuple(k)]))) for k in i]}")
+    rel = np.abs(got.astype(np.float64) - x) / np.maximum(np.abs(x.astype(np.float64)), 1e-300)
+    normal = np.abs(x) >= np.finfo(np.float32).tiny
+    assert np.max(rel[normal]) <= 2.0 ** -16 * (1 + 2.0 ** -7)
