@@ -172,9 +172,26 @@ __global__ __launch_bounds__(256) void nesterov_rows_kernel(const MatDesc *__res
     if (threadIdx.x == 0) w.partials[blockIdx.x] = s;
 }
 
+// Four consecutive gradient values as floats (8-byte bf16 or 16-byte fp32 load).
+template <typename GradT> __device__ __forceinline__ floatx4 load4_val(const GradT *p);
+template <> __device__ __forceinline__ floatx4 load4_val<float>(const float *p) {
+    return *reinterpret_cast<const floatx4 *>(p);
+}
+template <> __device__ __forceinline__ floatx4 load4_val<uint16_t>(const uint16_t *p) {
+    const u32x2 h = *reinterpret_cast<const u32x2 *>(p);
+    return floatx4{__uint_as_float(h[0] << 16), __uint_as_float(h[0] & 0xffff0000u), __uint_as_float(h[1] << 16),
+                   __uint_as_float(h[1] & 0xffff0000u)};
+}
+
 // Stage 1, rows > cols: X = N^T.  64 x 64 tiles of W transposed through LDS so
-// both the W-side and the X-side accesses are coalesced.
-template <typename GradT>
+// both the W-side and the X-side accesses are coalesced.  VEC (16-byte
+// aligned G and M, cols a multiple of 4): in a tile wholly inside the matrix
+// each thread moves four consecutive elements per access, on the W side four
+// columns of one row (G, M read, M written), on the X side four consecutive
+// W rows of one column, encoded into the pair together; tiles at the edge
+// take the element path.  The LDS row stride of 65 floats keeps the row
+// writes and the column reads free of bank conflicts.
+template <typename GradT, bool VEC>
 __global__ __launch_bounds__(256) void nesterov_tile_kernel(const MatDesc *__restrict__ descs,
                                                             Geom g, Work w, float mu,
                                                             int nesterov, int tiles_c,
@@ -191,32 +208,71 @@ __global__ __launch_bounds__(256) void nesterov_tile_kernel(const MatDesc *__res
     float *__restrict__ xf = w.xf ? w.xf + e * w.x_stride : nullptr;  // fp32 path
     uint16_t *__restrict__ xh = static_cast<uint16_t *>(w.xb) + e * w.x_stride;  // bf16 path
     uint8_t *__restrict__ xl = static_cast<uint8_t *>(w.xl) + e * w.x_stride;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     double acc = 0.0;
-    for (int r = 0; r < 16; ++r) {
-        const int ii = ty + 4 * r;
-        const int64_t i = i0 + ii, j = j0 + tx;
-        float n = 0.0f;
-        if (i < g.rows && j < g.cols) {
-            const int64_t src = i * g.cols + j;
-            const float gv = load_val<GradT>(gp, src);
-            const float m1 = mu * mp[src] + gv;
-            n = nesterov ? (mu * m1 + gv) : m1;
-            mp[src] = m1;
-            acc += static_cast<double>(n) * static_cast<double>(n);
+    if (VEC && i0 + 64 <= g.rows && j0 + 64 <= g.cols) {
+        const int q4 = 4 * (threadIdx.x & 15), r16 = threadIdx.x >> 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ii = 16 * r + r16;
+            const int64_t src = (i0 + ii) * g.cols + j0 + q4;
+            const floatx4 gv = load4_val<GradT>(gp + src);
+            const floatx4 m = *reinterpret_cast<const floatx4 *>(mp + src);
+            floatx4 m1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                m1[q] = mu * m[q] + gv[q];
+                const float n = nesterov ? (mu * m1[q] + gv[q]) : m1[q];
+                acc += static_cast<double>(n) * static_cast<double>(n);
+                tile[ii][q4 + q] = n;
+            }
+            *reinterpret_cast<floatx4 *>(mp + src) = m1;
         }
-        tile[ii][tx] = n;
-    }
-    __syncthreads();
-    // X[j][i] = N[i][j]: X row = W col (j0 + jj), X col = W row (i0 + tx)
-    for (int r = 0; r < 16; ++r) {
-        const int jj = ty + 4 * r;
-        const int64_t xr = j0 + jj, xc = i0 + tx;
-        if (xr < g.cols && xc < g.rows) {
-            if (xf)
-                xf[xr * g.lp + xc] = tile[tx][jj];
-            else
-                split_bf16(tile[tx][jj], xh + xr * g.lp + xc, xl + xr * g.lp + xc);
+        __syncthreads();
+        // X[j][i] = N[i][j]: lane (jj, c4) takes X row j0 + jj, columns i0 + c4 .. +3
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int jj = 16 * r + r16;
+            floatx4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = tile[q4 + q][jj];
+            const int64_t off = (j0 + jj) * g.lp + i0 + q4;
+            if (xf) {
+                *reinterpret_cast<floatx4 *>(xf + off) = v;
+            } else {
+                u32x2 h;
+                uint32_t l;
+                split_bf16x4(v, &h, &l);
+                *reinterpret_cast<u32x2 *>(xh + off) = h;
+                *reinterpret_cast<uint32_t *>(xl + off) = l;
+            }
+        }
+    } else {
+        const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+        for (int r = 0; r < 16; ++r) {
+            const int ii = ty + 4 * r;
+            const int64_t i = i0 + ii, j = j0 + tx;
+            float n = 0.0f;
+            if (i < g.rows && j < g.cols) {
+                const int64_t src = i * g.cols + j;
+                const float gv = load_val<GradT>(gp, src);
+                const float m1 = mu * mp[src] + gv;
+                n = nesterov ? (mu * m1 + gv) : m1;
+                mp[src] = m1;
+                acc += static_cast<double>(n) * static_cast<double>(n);
+            }
+            tile[ii][tx] = n;
+        }
+        __syncthreads();
+        // X[j][i] = N[i][j]: X row = W col (j0 + jj), X col = W row (i0 + tx)
+        for (int r = 0; r < 16; ++r) {
+            const int jj = ty + 4 * r;
+            const int64_t xr = j0 + jj, xc = i0 + tx;
+            if (xr < g.cols && xc < g.rows) {
+                if (xf)
+                    xf[xr * g.lp + xc] = tile[tx][jj];
+                else
+                    split_bf16(tile[tx][jj], xh + xr * g.lp + xc, xl + xr * g.lp + xc);
+            }
         }
     }
     const double s = block_sum<256>(acc, sh);
@@ -771,11 +827,16 @@ hipError_t launch_nesterov(const MatDesc *descs, int nmat, const Geom &g, const 
     const int bpm = nesterov_blocks_per_mat(g, &rpb, &tc);
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(bpm) * nmat)), block(256);
     const bool vec = vec_ok && (g.cols % 4 == 0) && (g.lp % 4 == 0);
-    if (g.transposed) {
+    if (g.transposed && vec) {
         if (grad_bf16)
-            hipLaunchKernelGGL(nesterov_tile_kernel<uint16_t>, grid, block, 0, st, descs, g, w, mu, nesterov, tc, bpm);
+            hipLaunchKernelGGL((nesterov_tile_kernel<uint16_t, true>), grid, block, 0, st, descs, g, w, mu, nesterov, tc, bpm);
         else
-            hipLaunchKernelGGL(nesterov_tile_kernel<float>, grid, block, 0, st, descs, g, w, mu, nesterov, tc, bpm);
+            hipLaunchKernelGGL((nesterov_tile_kernel<float, true>), grid, block, 0, st, descs, g, w, mu, nesterov, tc, bpm);
+    } else if (g.transposed) {
+        if (grad_bf16)
+            hipLaunchKernelGGL((nesterov_tile_kernel<uint16_t, false>), grid, block, 0, st, descs, g, w, mu, nesterov, tc, bpm);
+        else
+            hipLaunchKernelGGL((nesterov_tile_kernel<float, false>), grid, block, 0, st, descs, g, w, mu, nesterov, tc, bpm);
     } else if (vec) {
         if (grad_bf16)
             hipLaunchKernelGGL((nesterov_rows_kernel<uint16_t, true>), grid, block, 0, st, descs, g, w, mu, nesterov, rpb, bpm);
