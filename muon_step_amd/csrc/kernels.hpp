@@ -93,6 +93,12 @@ struct NsStep {
     int gram_splits, gram_units;
     int poly_splits, poly_units;
     int64_t split_from;
+    // bf16 a X + B X of an intermediate step, likewise: the chunk's tiles
+    // (matrix, tile row within the column panel) from apply_split_from on run
+    // with K (= s) split into apply_splits ranges of apply_units x 128; a
+    // reduce adds a X and writes the X' pair.  The last step is never split.
+    int apply_splits, apply_units;
+    int64_t apply_split_from;
 };
 
 // kind: 0 = A = X X^T, 1 = B = bA + cA^2, 2 = X <- aX + BX (or the fused update).

@@ -1136,6 +1136,88 @@ __global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_kernel(const MatDesc *__r
         apply_epilogue_update<MODE == 2>(acc, descs[e], g, w, p, t_, area, lane);
 }
 
+// The K range ks of tile tl of a split a X + B X launch (tiles [tile_base,
+// tile_base + tile_count) of the chunk, in the order of ns_apply_kernel):
+// the product only, stored as an fp32 partial tile (slot tl * splits + ks of
+// w.kpart) for apply_reduce_kernel.  Workgroups of one K range are
+// consecutive, so the tiles of one matrix read the same K slab of X.
+__global__ __launch_bounds__(Cfg::NT, 1) void ns_apply_split_kernel(Geom g, Work w, int64_t tiles_per_mat,
+                                                                     int64_t nblocks, int64_t tile_base,
+                                                                     int64_t tile_count, int splits, int units) {
+    using C = Cfg;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int64_t L = xcd_swizzle(blockIdx.x, nblocks);
+    const int ks = static_cast<int>(L / tile_count);
+    const int64_t tl = L % tile_count;
+    const int64_t f = tile_base + tl;
+    const int64_t e = f / tiles_per_mat;
+    const int64_t t = f % tiles_per_mat;
+    const int nti = static_cast<int>(g.sp / C::BM);
+    const int tj = static_cast<int>(t / nti);
+    const int ti = static_cast<int>(t % nti);
+    const int64_t kdim = k_extent(g.s, g.sp);
+    const int64_t k0 = static_cast<int64_t>(ks) * units * 2 * C::BK;
+    const int64_t k1 = min(kdim, k0 + static_cast<int64_t>(units) * 2 * C::BK);
+    Src src;
+    src.ld_p = g.sp * 2;
+    src.ld_q = g.lp * 2;
+    src.p = static_cast<const char *>(w.bb) + e * w.a_stride * 2 + static_cast<int64_t>(ti) * C::BM * src.ld_p + k0 * 2;
+    src.q = static_cast<const char *>(w.xb) + e * w.x_stride * 2 + static_cast<int64_t>(tj) * C::BN * 2 + k0 * src.ld_q;
+    floatx16 acc[C::MI][C::NI];
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+    main_loop<C, APPLY>(acc, src, static_cast<int>((k1 - k0) / C::BK), wave, wm, wn, lane, [] {});
+    store_kpart<C>(acc, w.kpart + (tl * splits + ks) * KPART_VALUES, wave, lane);
+}
+
+// Finishes the split tiles of a X + B X: the partials of each element summed
+// in range order, then X' = a X + sum formed from the X pair and written as
+// the pair (X'_hi to xb_next, X'_lo to xl in place), as the unsplit epilogue
+// does.  Thread (item) = one partial float4 (wave, accumulator group, lane, as
+// store_kpart laid them out): four consecutive columns of one row; 64 blocks
+// of 256 threads per tile.
+__global__ __launch_bounds__(256) void apply_reduce_kernel(Geom g, Work w, NsStep p, int64_t tiles_per_mat,
+                                                           int64_t tile_base, int splits) {
+    using C = Cfg;
+    const int64_t tl = blockIdx.x / 64;
+    const int64_t tile = tile_base + tl;
+    const int item = static_cast<int>(blockIdx.x % 64) * 256 + threadIdx.x;
+    const int64_t e = tile / tiles_per_mat;
+    const int64_t t = tile % tiles_per_mat;
+    const int nti = static_cast<int>(g.sp / C::BM);
+    const int tj = static_cast<int>(t / nti), ti = static_cast<int>(t % nti);
+    const floatx4 *src = reinterpret_cast<const floatx4 *>(w.kpart) + tl * splits * (KPART_VALUES / 4) + item;
+    floatx4 sum = src[0];
+    for (int k = 1; k < splits; ++k) {
+        const floatx4 v = src[static_cast<int64_t>(k) * (KPART_VALUES / 4)];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum[q] += v[q];
+    }
+    const int wave = item >> 11, j = (item >> 6) & 31, lane = item & 63;
+    const int mi = j / (C::NI * 4), ni = (j / 4) % C::NI, c4 = j % 4;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int64_t row = static_cast<int64_t>(ti) * C::BM + wm * C::WM + mi * 32 + (lane & 31);
+    const int64_t col = static_cast<int64_t>(tj) * C::BN + wn * C::WN + ni * 32 + 8 * c4 + 4 * (lane >> 5);
+    const int64_t off = e * w.x_stride + row * g.lp + col;
+    const float a = p.unnormalized ? p.a * w.inv_norm[e] : p.a;
+    const u32x2 hv = *as_global(reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(w.xb) + off));
+    const uint32_t lv = *as_global(reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(w.xl) + off));
+    const floatx4 x = join_bf16x4(hv, lv);
+    floatx4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(a, x[q], sum[q]);
+    u32x2 h;
+    uint32_t l;
+    split_bf16x4(v, &h, &l);
+    *as_global(reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(w.xb_next) + off)) = h;
+    *as_global(reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(w.xl) + off)) = l;
+}
+
 }  // namespace bf16path
 
 hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const Geom &g, const Work &w,
@@ -1171,10 +1253,25 @@ hipError_t launch_ns_stage_bf16(int kind, const MatDesc *descs, int nmat, const 
     }
     const int64_t tiles = (g.sp / Cfg::BM) * (g.lp / Cfg::BN);
     const int64_t nblocks = tiles * nmat;
-    const dim3 grid(static_cast<unsigned>(nblocks)), block(Cfg::NT);
-    if (!p.final_update)
-        ns_apply_kernel<0><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
-    else if (p.param_bf16 && p.w_staged && !p.unnormalized)
+    const dim3 block(Cfg::NT);
+    if (!p.final_update) {
+        // tiles [0, from) whole, [from, all) split over K (none when apply_splits == 1)
+        const int64_t all = nblocks;
+        const int64_t from =
+            p.apply_splits > 1 ? std::min<int64_t>(std::max<int64_t>(p.apply_split_from, 0), all) : all;
+        if (from > 0)
+            ns_apply_kernel<0><<<dim3(static_cast<unsigned>(from)), block, 0, st>>>(descs, g, w, p, tiles, from);
+        if (from < all) {
+            const int64_t count = all - from, sblocks = count * p.apply_splits;
+            ns_apply_split_kernel<<<dim3(static_cast<unsigned>(sblocks)), block, 0, st>>>(
+                g, w, tiles, sblocks, from, count, p.apply_splits, p.apply_units);
+            apply_reduce_kernel<<<dim3(static_cast<unsigned>(count * 64)), dim3(256), 0, st>>>(g, w, p, tiles, from,
+                                                                                             p.apply_splits);
+        }
+        return hipGetLastError();
+    }
+    const dim3 grid(static_cast<unsigned>(nblocks));
+    if (p.param_bf16 && p.w_staged && !p.unnormalized)
         ns_apply_kernel<3><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);
     else if (p.param_bf16)
         ns_apply_kernel<2><<<grid, block, 0, st>>>(descs, g, w, p, tiles, nblocks);

@@ -221,7 +221,7 @@ Geom make_geom(int64_t rows, int64_t cols) {
     return g;
 }
 
-// Split-K of the bf16 Gram and A^2 products of a group (all 1 on the fp32
+// Split-K of the bf16 Gram, A^2 and apply products of a group (all 1 on the fp32
 // path).  The group's lower-triangle tiles, counted in the order (matrix,
 // tile of the matrix) over all its matrices, from `from` on run with K split
 // into ranges (gram / poly of them, of gram_units / poly_units x 128), their
@@ -231,6 +231,10 @@ Geom make_geom(int64_t rows, int64_t cols) {
 struct Splits {
     int gram = 1, gram_units = 0, poly = 1, poly_units = 0;
     int64_t from = 0;
+    // a X + B X of the intermediate steps, over its own tiles (sp/256 x lp/256
+    // per matrix, in ns_apply_kernel's order), from apply_from on
+    int apply = 1, apply_units = 0;
+    int64_t apply_from = 0;
     size_t per_matrix = 0;  // partial bytes per matrix of a chunk (every tile split)
     size_t fixed = 0;       // partial bytes of a chunk holding the split tail tiles
     size_t kpart(int64_t n) const { return per_matrix * static_cast<size_t>(n) + fixed; }
@@ -240,6 +244,7 @@ int64_t sym_tiles(const Geom &g) {
     const int64_t nt = g.sp / muon::kTile;
     return nt * (nt + 1) / 2;
 }
+int64_t apply_tiles(const Geom &g) { return (g.sp / muon::kTile) * (g.lp / muon::kTile); }
 
 constexpr size_t kPartTileBytes = size_t(256) * 256 * 4;  // one fp32 partial tile
 constexpr int64_t kCUs = 256;                              // workgroups in one wave (one per CU)
@@ -275,31 +280,54 @@ int tail_splits(int64_t count, int64_t units, int64_t max_splits, bool whole, in
 Splits plan_splits(const Geom &g, bool bf16, int64_t group_n) {
     Splits sp;
     if (!bf16) return sp;
-    const int64_t tiles = sym_tiles(g);
-    const int64_t w = tiles * group_n;
     // K extents of the loops (the true length rounded up to 128), in units of 128
     const int64_t gram_k = std::min(g.lp, round_up(g.l, 128)) / 128;
-    const int64_t poly_k = std::min(g.sp, round_up(g.s, 128)) / 128;
+    const int64_t s_k = std::min(g.sp, round_up(g.s, 128)) / 128;  // A^2 and a X + B X
     // partial tiles take at most half of a matrix's own workspace: per matrix
-    // when every tile of the group is split, in all when only the tail is
+    // when every tile of the group is split, in all when only the tail is; the
+    // Gram, A^2 and apply partials share the space (their reduces run in turn)
     const size_t x = static_cast<size_t>(g.sp * g.lp), a = static_cast<size_t>(g.sp * g.sp);
     const int64_t max_pieces = static_cast<int64_t>((x * 5 + a * 4) / 2 / kPartTileBytes);
     // a group under half a wave splits every tile; a larger one only the tiles
     // of its last, partial wave
-    const bool whole = w < kCUs / 2;
-    const int64_t count = whole ? w : w % kCUs;
-    const int64_t max_splits = whole ? max_pieces / tiles : (count > 0 ? max_pieces / count : 0);
+    auto plan = [&](int64_t tiles, int64_t *count, bool *whole, int64_t *max_splits) {
+        const int64_t w = tiles * group_n;
+        *whole = w < kCUs / 2;
+        *count = *whole ? w : w % kCUs;
+        *max_splits = *whole ? max_pieces / tiles : (*count > 0 ? max_pieces / *count : 0);
+        return w;
+    };
+    int64_t count, max_splits;
+    bool whole;
+    const int64_t st = sym_tiles(g);
+    const int64_t w = plan(st, &count, &whole, &max_splits);
     sp.from = w;
-    if (count == 0 || max_splits < 2) return sp;
-    sp.gram = tail_splits(count, gram_k, max_splits, whole, &sp.gram_units);
-    sp.poly = tail_splits(count, poly_k, max_splits, whole, &sp.poly_units);
-    if (sp.gram == 1 && sp.poly == 1) return sp;
-    const size_t piece = static_cast<size_t>(std::max(sp.gram, sp.poly)) * kPartTileBytes;
-    sp.from = w - count;
-    if (whole)
-        sp.per_matrix = static_cast<size_t>(tiles) * piece;
-    else
-        sp.fixed = static_cast<size_t>(count) * piece;
+    if (count > 0 && max_splits >= 2) {
+        sp.gram = tail_splits(count, gram_k, max_splits, whole, &sp.gram_units);
+        sp.poly = tail_splits(count, s_k, max_splits, whole, &sp.poly_units);
+        if (sp.gram > 1 || sp.poly > 1) {
+            const size_t piece = static_cast<size_t>(std::max(sp.gram, sp.poly)) * kPartTileBytes;
+            sp.from = w - count;
+            if (whole)
+                sp.per_matrix = static_cast<size_t>(st) * piece;
+            else
+                sp.fixed = static_cast<size_t>(count) * piece;
+        }
+    }
+    const int64_t at = apply_tiles(g);
+    const int64_t aw = plan(at, &count, &whole, &max_splits);
+    sp.apply_from = aw;
+    if (count > 0 && max_splits >= 2) {
+        sp.apply = tail_splits(count, s_k, max_splits, whole, &sp.apply_units);
+        if (sp.apply > 1) {
+            const size_t piece = static_cast<size_t>(sp.apply) * kPartTileBytes;
+            sp.apply_from = aw - count;
+            if (whole)
+                sp.per_matrix = std::max(sp.per_matrix, static_cast<size_t>(at) * piece);
+            else
+                sp.fixed = std::max(sp.fixed, static_cast<size_t>(count) * piece);
+        }
+    }
     return sp;
 }
 
@@ -718,7 +746,7 @@ void ns_work(int stage, const Geom &g, bool bf16, int n, bool ns_out, int psize,
 // separate pass applies the decay + update.
 muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom &gx, Work &w, bool bf16,
                    const muon_hparams *hp, bool update, int param_bf16, bool any_ns_out, float d, float s,
-                   hipStream_t st, const Splits &sp, const Run *runs, int nruns, int64_t chunk_tile0 = 0,
+                   hipStream_t st, const Splits &sp, const Run *runs, int nruns, int64_t chunk_m0 = 0,
                    bool params_aligned16 = false, int partial_bpm = 0, bool outs_aligned16 = false) {
     const bool unit_rms = update && hp->scale_mode == MUON_SCALE_UNIT_RMS;
     // the geometry the product launches see: W's own for a chunk of one run (the
@@ -773,7 +801,12 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
         p.gram_units = sp.gram_units;
         p.poly_splits = sp.poly;
         p.poly_units = sp.poly_units;
-        p.split_from = sp.from - chunk_tile0;  // the launch clamps it to the chunk
+        // the group's first split tiles, counted from the chunk's first matrix
+        // chunk_m0 (the launches clamp them to the chunk)
+        p.split_from = sp.from - chunk_m0 * sym_tiles(g);
+        p.apply_splits = sp.apply;
+        p.apply_units = sp.apply_units;
+        p.apply_split_from = sp.apply_from - chunk_m0 * apply_tiles(g);
         for (int kind = 0; kind < 3; ++kind) {
             const int stage = kind == 0 ? ST_GRAM : kind == 1 ? ST_POLY : (p.final_update ? ST_APPLY_UPDATE : ST_APPLY);
             double fl = 0, by = 0;
@@ -962,7 +995,7 @@ muon_status step_impl(muon_context *ctx, const muon_matrix *mats, int64_t count,
                 if (e != hipSuccess) return hip_fail(ctx, e, "norm launch");
             }
             s = run_ns(ctx, dd, n, gp.g, w, bf16, hp, true, gp.param_dtype == MUON_BF16, any_out, d, sc, st,
-                       gp.splits, runs, nruns, c0 * sym_tiles(gp.g), params_aligned, gp.bpm, outs_aligned);
+                       gp.splits, runs, nruns, c0, params_aligned, gp.bpm, outs_aligned);
             if (s != MUON_OK) return s;
         }
         pos += static_cast<size_t>(n_all);
@@ -1301,6 +1334,9 @@ muon_status muon_ns_stage(muon_context *ctx, int32_t stage, const float *x, cons
     p.poly_splits = sp.poly;
     p.poly_units = sp.poly_units;
     p.split_from = sp.from;
+    p.apply_splits = sp.apply;
+    p.apply_units = sp.apply_units;
+    p.apply_split_from = sp.apply_from;
     hipError_t e = hipSuccess;
     if (stage != MUON_STAGE_POLY) e = muon::launch_import_pair(g, x, w, st);
     if (e == hipSuccess && stage != MUON_STAGE_GRAM)

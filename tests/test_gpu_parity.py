@@ -235,6 +235,21 @@ def test_step_split_k_products(ctx, torch_mod):
             assert np.array_equal(to_np(a).view(np.uint32), to_np(b).view(np.uint32))
 
 
+def test_step_split_k_apply(ctx, torch_mod):
+    """A single 4352^2 matrix: its a X + B X has 17 x 17 = 289 tiles, one wave of 256
+    and 33 more, and those 33 run split over K (7 ranges of 640, their partials reduced
+    in order before a X is added) in every step but the last; against the oracle, and
+    the call repeated bit for bit."""
+    S = synth.MatrixSpec
+    specs = [S(4352, 4352)]
+    say("step split-K apply (4352^2)")
+    _, dev1 = _run_step(ctx, torch_mod, specs, "bf16", seed=41)
+    _, dev2 = _run_step(ctx, torch_mod, specs, "bf16", seed=41)
+    for (p1, _, m1, o1), (p2, _, m2, o2) in zip(dev1, dev2):
+        for a, b in ((p1, p2), (o1, o2)):
+            assert np.array_equal(to_np(a).view(np.uint32), to_np(b).view(np.uint32))
+
+
 def test_step_split_k_tail(ctx, torch_mod):
     """A group whose Gram tiles fill one wave of 256 workgroups and two tiles of a
     second (43 x 768x8192: 258 tiles) splits only those last two tiles over K (16

@@ -46,9 +46,10 @@ def ctx(torch_mod):
 # 1 x 1 .. 33 x 65: sub-tile and ragged; 1408 x 2048: the 16B-MoE expert shape
 # (padded to 1536); 256 x 2048 (Gram in 4 K ranges), 2048 x 4096 (Gram and A^2
 # in 3): long K loops split over several workgroups; 300 x 3000: a split and
-# ragged K (Gram in 5).
+# ragged K (Gram in 5); 4352^2: the apply's 33 tiles past its first wave split
+# over K (7 ranges) and reduced with the a X term.
 SHAPES = [(1, 1), (1, 7), (33, 65), (256, 256), (300, 520), (1408, 2048), (256, 2048), (1024, 1536),
-          (2048, 4096), (300, 3000)]
+          (2048, 4096), (300, 3000), (4352, 4352)]
 
 
 def _x(shape, seed):
