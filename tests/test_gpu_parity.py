@@ -250,6 +250,51 @@ def test_step_split_k_apply(ctx, torch_mod):
             assert np.array_equal(to_np(a).view(np.uint32), to_np(b).view(np.uint32))
 
 
+def test_step_split_k_apply_chunked(torch_mod):
+    """Three 4352^2 matrices: the group's apply tiles past its last full wave (99 of
+    867, all in the third matrix) split over K.  The step runs once in one chunk and
+    once under a workspace cap that forces chunks of one matrix, where only the last
+    chunk holds split tiles: the same bits either way (the split depends on the group,
+    never on the chunking)."""
+    import ctypes
+    ms = _ms()
+    rows = cols = 4352
+    wl = synth.Workload("t", 43, tuple(synth.MatrixSpec(rows, cols) for _ in range(3)))
+    inputs = [synth.matrix_inputs(wl, i) for i in range(3)]
+    hp = ms.make_hparams()
+
+    def tensors():
+        dev, mats = [], []
+        for inp in inputs:
+            p = to_dev(inp["w"], torch_mod.bfloat16)
+            g = to_dev(inp["g"], torch_mod.bfloat16)
+            m = to_dev(inp["m"], torch_mod.float32)
+            o = torch_mod.empty((rows, cols), dtype=torch_mod.float32, device="cuda")
+            dev.append((p, g, m, o))
+            mats.append(ms.matrix(p, g, m, o))
+        return dev, mats
+
+    dev, mats = tensors()
+    need = ctypes.c_size_t()
+    arr = (ms.muon_matrix * 3)(*mats)
+    assert ms.load().muon_workspace_bytes(arr, 3, ctypes.byref(hp), ctypes.byref(need)) == ms.MUON_OK
+    outs = []
+    for cap in (0, int(need.value * 0.45)):
+        say(f"3 x 4352^2, workspace cap {cap}")
+        if cap:
+            dev, mats = tensors()
+        c = ms.Context(0, cap)
+        try:
+            c.muon_step(mats, hp)
+            torch_mod.cuda.synchronize()
+        finally:
+            c.close()
+        outs.append([(to_np(p), to_np(o), to_np(m)) for p, _, m, o in dev])
+    for (p1, o1, m1), (p2, o2, m2) in zip(*outs):
+        for a, b in ((p1, p2), (o1, o2), (m1, m2)):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 def test_step_split_k_tail(ctx, torch_mod):
     """A group whose Gram tiles fill one wave of 256 workgroups and two tiles of a
     second (43 x 768x8192: 258 tiles) splits only those last two tiles over K (16
