@@ -404,13 +404,20 @@ __device__ __forceinline__ const char *poly_a_rows(const Geom &g, const Work &w,
 // to bf16.  Vector-memory instructions retire in issue order; the wait before
 // POLY's round h allows what was issued after round h's DMA: round h-1's
 // stores (at least ROW_STORES) and round h+1's DMA.
+// POLY: A's rows of the four rounds are staged so that they arrive early:
+// rounds 0 and 1 under the last K stage (round 0 in the slot-0 area, round 1
+// in the wave's 4 KB of lds_wbuf, which the K loop does not use), round 2 in
+// the slot-1 area on entry, round 3 in lds_wbuf once round 1 has read it.  A
+// round's fp32 values go over its own A rows in a ring area, or, for rounds
+// 1 and 3, into the slot-0 area once the previous round's stores have read it.
 template <class C, int KIND>
 __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI], const Geom &g, const Work &w,
                                              const NsStep &p, int64_t e, int ti, int tj, int wm, int wn,
-                                             char *const (&area)[2], int lane) {
+                                             char *const (&area)[2], char *wb, int lane) {
     constexpr int ROUNDS = C::WM / C::EPI_ROWS;
     constexpr int DMA_PER_ROUND = C::EPI_ROWS / 8;
     constexpr int ROW_STORES = C::EPI_ROWS / 4;
+    constexpr int STORES = ROW_STORES + C::WN / 16;  // row and mirror stores of a round off the diagonal
     static_assert(ROUNDS == C::MI && C::EPI_ROWS == 32 && C::WN == 64, "one 32 x 64 accumulator block per round");
     const int64_t ld = g.sp;
     const int64_t row0 = static_cast<int64_t>(ti) * C::BM + wm * C::WM;
@@ -426,24 +433,33 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
     const float gscale = inv * inv;
     const float pb = p.b * inv, pc = p.c * inv;
     const char *a_in = poly_a_rows(g, w, e, row0, col0);
-    if constexpr (KIND == POLY) dma_bf16_rows<C>(area[1], a_in + C::EPI_ROWS * ld * 2, ld * 2, lane);
+    static_assert(ROUNDS == 4 && C::EPI_ROWS * 128 <= 4096, "a round's A rows fit the wave's lds_wbuf");
+    static_assert(2 * STORES + DMA_PER_ROUND + STORES < 64, "vmcnt range");
+    const char *const a_src[ROUNDS] = {area[0], wb, area[1], wb};
+    char *const f_area[ROUNDS] = {area[0], area[0], area[1], area[0]};
+    if constexpr (KIND == POLY) dma_bf16_rows<C>(area[1], a_in + 2 * C::EPI_ROWS * ld * 2, ld * 2, lane);
     const int lrow = lane & 31;
 #pragma unroll
     for (int h = 0; h < ROUNDS; ++h) {
-        char *reg = area[h & 1];
+        char *reg = KIND == POLY ? f_area[h] : area[h & 1];
         if constexpr (KIND == POLY) {
-            // a diagonal tile's round may issue no stores: there only round
-            // h+1's DMA may stay in flight
+            // Retirement is in issue order; each wait allows what was issued
+            // after round h's rows.  A diagonal tile's rounds may issue fewer
+            // stores, so there the waits count none of them.
             if (h == 0)
+                fenced_wait_vmcnt<2 * DMA_PER_ROUND>();  // rounds 1 and 2
+            else if (h == 1 && diag)
                 fenced_wait_vmcnt<DMA_PER_ROUND>();
-            else if (h + 1 < ROUNDS && diag)
+            else if (h == 1)
+                fenced_wait_vmcnt<DMA_PER_ROUND + STORES>();  // round 2, round 0's stores
+            else if (h == 2 && diag)
                 fenced_wait_vmcnt<DMA_PER_ROUND>();
-            else if (h + 1 < ROUNDS)
-                fenced_wait_vmcnt<ROW_STORES + DMA_PER_ROUND>();
+            else if (h == 2)
+                fenced_wait_vmcnt<STORES + STORES + DMA_PER_ROUND>();  // stores 0 and 1, round 3
             else if (diag)
                 fenced_wait_vmcnt<0>();
             else
-                fenced_wait_vmcnt<ROW_STORES>();
+                fenced_wait_vmcnt<STORES>();  // round 2's stores (round 3 followed round 1's)
         }
         const int brow = wm * C::MI + h;  // block row of this round (32-row blocks of the tile)
         floatx4 v[C::NI][4];
@@ -456,7 +472,7 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
 #pragma unroll
                     for (int q = 0; q < 4; ++q) v[ni][c4][q] = acc[h][ni][4 * c4 + q] * gscale;
                 } else {
-                    const u32x2 a2 = *reinterpret_cast<const u32x2 *>(reg + pair_offset(lrow, lcol));
+                    const u32x2 a2 = *reinterpret_cast<const u32x2 *>(a_src[h] + pair_offset(lrow, lcol));
                     const float a4[4] = {__uint_as_float(a2[0] << 16), __uint_as_float(a2[0] & 0xffff0000u),
                                          __uint_as_float(a2[1] << 16), __uint_as_float(a2[1] & 0xffff0000u)};
 #pragma unroll
@@ -502,10 +518,10 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
             }
         }
         if constexpr (KIND == POLY) {
-            if (h + 2 < ROUNDS) {
-                wait_lgkm0();  // this round's LDS reads are done before the DMA refills the area
+            if (h == 1) {
+                wait_lgkm0();  // round 1's reads of its A rows are done before the DMA refills lds_wbuf
                 asm volatile("" ::: "memory");
-                dma_bf16_rows<C>(reg, a_in + C::EPI_ROWS * (h + 2) * ld * 2, ld * 2, lane);
+                dma_bf16_rows<C>(wb, a_in + 3 * C::EPI_ROWS * ld * 2, ld * 2, lane);
             }
         }
     }
@@ -606,11 +622,12 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
     // product has no epilogue of its own (sym_reduce_kernel forms B)
     auto pre_last = [&] {
         if constexpr (KIND == POLY)
-            if (splits == 1)
-                dma_bf16_rows<C>(epi_area<0>(wave),
-                                 poly_a_rows(g, w, e, static_cast<int64_t>(ti) * C::BM + wm * C::WM,
-                                             static_cast<int64_t>(tj) * C::BN + wn * C::WN),
-                                 g.sp * 2, lane);
+            if (splits == 1) {
+                const char *a_rows = poly_a_rows(g, w, e, static_cast<int64_t>(ti) * C::BM + wm * C::WM,
+                                                 static_cast<int64_t>(tj) * C::BN + wn * C::WN);
+                dma_bf16_rows<C>(epi_area<0>(wave), a_rows, g.sp * 2, lane);
+                dma_bf16_rows<C>(lds_wbuf + wave * 4096, a_rows + C::EPI_ROWS * g.sp * 2, g.sp * 2, lane);
+            }
     };
     const int nk = static_cast<int>((k1 - k0) / C::BK);
     if (diag)
@@ -630,7 +647,7 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
     wait_lgkm0();
     stage_barrier();  // every wave is done with the operand ring
     char *const area[2] = {epi_area<0>(wave), epi_area<1>(wave)};
-    sym_epilogue<C, KIND>(acc, g, w, p, e, ti, tj, wm, wn, area, lane);
+    sym_epilogue<C, KIND>(acc, g, w, p, e, ti, tj, wm, wn, area, lds_wbuf + wave * 4096, lane);
 }
 
 // Split-K Gram / A^2: sums the K ranges' partials of one (matrix, tile) in
