@@ -36,7 +36,11 @@
 // element: X_hi and its 8-bit residual X_lo in and out; the fused update of
 // a bf16 W brings W's rows by DMA too).  K loops stop at the true length
 // rounded to 128 (the padding is zero).  Block ids are renumbered so one
-// matrix's tiles share an XCD (and its L2).
+// matrix's tiles share an XCD (and its L2).  Tiles that would run as a
+// launch's last, partial wave (every tile, for a Gram or A^2 of a group too
+// small to fill half a wave) may instead run split over K ranges whose fp32
+// partial tiles a reduce sums in a fixed order and finishes as the epilogue
+// would (sym_reduce_kernel, apply_reduce_kernel).
 #include <algorithm>
 
 #include "common.hpp"
