@@ -21,12 +21,14 @@
 // with v_mfma_f32_32x32x16_bf16 into fp32 accumulators.  Operand slabs of
 // 64 k (one 128-byte line per row) are copied global -> LDS by the
 // 16-byte-per-lane DMA (global_load_lds_dwordx4) into a ring of two stages
-// (128 KB).  Every product is followed by at most one fragment read for the
-// next 16-k substep; the last of a stage's four substeps also refills the
-// slot just read with the stage after next, so LDS reads and copies run
-// under the MFMAs; one barrier per stage, before its last substep.  The LDS
-// layouts are XOR-swizzled so that every 16-lane phase of a fragment read
-// touches all 64 banks once.  The X operand of B X is stored as it lies in
+// (128 KB); a diagonal tile of GRAM or POLY, whose output rows and columns
+// are the same rows of the operand, fills a slot with 128 k of those rows
+// instead of the same 64 k twice (CfgDiag).  Every product is followed by
+// at most one fragment read for the next 16-k substep; the last of a stage's
+// substeps also refills the slot just read with the stage after next, so LDS
+// reads and copies run under the MFMAs; one barrier per stage, before its
+// last substep.  The LDS layouts are XOR-swizzled so that every 16-lane
+// phase of a fragment read touches all 64 banks once.  The X operand of B X is stored as it lies in
 // memory (k rows, n contiguous) and read with ds_read_b64_tr_b16, which hands
 // each lane four consecutive k of one column.  The products are issued with
 // the operands swapped, so each lane's accumulators hold four consecutive
@@ -65,7 +67,8 @@ struct Cfg {
     static constexpr int STAGES = 2;
     static constexpr int BK = 64;                      // k per stage
     static constexpr int SUBSTEPS = BK / 16;           // 16-k MFMA substeps per stage
-    static constexpr int ROWB = BK * 2;                // bytes of one K-contiguous row per stage
+    static constexpr int ROWB = BK * 2;                // bytes of one K-contiguous row per slab
+    static constexpr int KT_BYTES = ROWB;              // bytes a K-contiguous operand advances per stage
     static constexpr int P_BYTES = BM * ROWB;          // 256 rows x 64 bf16
     static constexpr int Q_BYTES = BN * ROWB;          // BN rows x 64 bf16, or 64 k-rows x BN bf16
     static constexpr int SLOT_BYTES = P_BYTES + Q_BYTES;
@@ -79,6 +82,7 @@ struct Cfg {
     static constexpr int NF = MI + NI;                 // fragments per wave and substep
     static constexpr bool MFMA = true;                 // the wave's products are issued
     static constexpr bool DIAG = false;                // products selected by Src::mmask
+    static constexpr bool PACKED = false;              // a slot holds 128 k of one operand (CfgDiag)
 };
 
 // The K loop of a GRAM or POLY wave whose 128 output rows all lie in the zero
@@ -95,9 +99,19 @@ struct CfgIdle : Cfg {
 // waves take their 128 x 64 blocks in a permuted order and issue only the
 // needed products (Src::mmask), so that the two waves sharing a SIMD (w and
 // w + 4) hold 8 + 0, 8 + 0, 7 + 3 and 7 + 3 products per substep instead of
-// 8 + 8.
+// 8 + 8.  Output rows and columns are the same 256 rows of the operand, so a
+// slot holds 128 k of them, k .. k+63 in its P slab and k+64 .. k+127 in its
+// Q slab, and a stage runs eight substeps whose two fragments both come from
+// the P slab (substeps 0-3), then from the Q slab (4-7).  A stage of half
+// the products is no shorter than a full one (its length is set by the
+// copies' latency and the barrier), so a stage of twice the K with the same
+// bytes lets the diagonal tile finish in about half a tile's time; the sums
+// run over k in the same order as with 64-k stages.
 struct CfgDiag : Cfg {
     static constexpr bool DIAG = true;
+    static constexpr bool PACKED = true;
+    static constexpr int SUBSTEPS = 8;
+    static constexpr int KT_BYTES = 2 * ROWB;
     // wave w -> (wm, wn): (1,0) (1,1) (0,0) (1,2) (0,2) (0,3) (0,1) (1,3)
     static constexpr uint32_t WM_OF = 0x8Bu;    // bit w
     static constexpr uint32_t WN_OF = 0xDE84u;  // bits 2w, 2w+1
@@ -187,6 +201,7 @@ struct Src {
     const char *q;  // Q operand (output columns): K-contiguous rows, or X itself for APPLY
     int64_t ld_q;
     uint32_t mmask;  // C::DIAG: bit i set = product i of each substep is needed (wave-uniform)
+    uint32_t fmask;  // C::DIAG: bit j set = fragment j (read_frag's order) feeds a needed product
 };
 
 // DMA block j (0 <= j < LPS) of this wave for stage kt into slot S.  Blocks
@@ -202,7 +217,7 @@ __device__ __forceinline__ void dma_block(const Src &src, int kt, int j, int wav
         const int blk = wave * C::P_BLOCKS + j;
         const int row = blk * 8 + (lane >> 3);
         const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-        dma16(src.p + row * src.ld_p + kt * C::ROWB + chunk * 16, slot_p<S>() + blk * 1024);
+        dma16(src.p + row * src.ld_p + kt * C::KT_BYTES + chunk * 16, slot_p<S>() + blk * 1024);
     } else if constexpr (KIND == APPLY) {
         constexpr int UNITS = C::QROW / 16;  // 16-byte units per k-row
         const int blk = wave * C::Q_BLOCKS + (j - C::P_BLOCKS);
@@ -214,7 +229,7 @@ __device__ __forceinline__ void dma_block(const Src &src, int kt, int j, int wav
         const int blk = wave * C::Q_BLOCKS + (j - C::P_BLOCKS);
         const int row = blk * 8 + (lane >> 3);
         const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-        dma16(src.q + row * src.ld_q + kt * C::ROWB + chunk * 16, slot_q<S>() + blk * 1024);
+        dma16(src.q + row * src.ld_q + kt * C::KT_BYTES + chunk * 16, slot_q<S>() + blk * 1024);
     }
 }
 
@@ -231,6 +246,19 @@ template <class C, int KIND, int S>
 __device__ __forceinline__ void read_frag(Frags &f, int j, int ks, int wm, int wn, int lane) {
     const bool is_a = j == 0 || j > C::NI;
     const int idx = j == 0 ? 0 : (j <= C::NI ? j - 1 : j - C::NI);
+    if constexpr (C::PACKED) {
+        // both fragments are rows of the one operand: substeps 0-3 read the P
+        // slab, 4-7 the Q slab (the stage's second 64 k)
+        const char *slab = ks < 4 ? slot_p<S>() : slot_q<S>();
+        const int chunk = 2 * (ks & 3) + (lane >> 5);
+        const int row = (is_a ? wm * C::WM : wn * C::WN) + idx * 32 + (lane & 31);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(slab + kc_offset(row, chunk));
+        if (is_a)
+            f.a[idx] = v;
+        else
+            f.b[idx] = v;
+        return;
+    }
     const int chunk = 2 * ks + (lane >> 5);  // k = 8*chunk .. 8*chunk+7 of this stage
     if (is_a) {
         const int row = wm * C::WM + idx * 32 + (lane & 31);
@@ -285,25 +313,41 @@ __device__ __forceinline__ void substep(floatx16 (&acc)[C::MI][C::NI], const Fra
         } else if constexpr (C::MFMA) {
             mma_one<C>(acc, f, i);
         }
-        if (READ && i < C::NF) read_frag<C, KIND, S_READ>(g, i, ks_next, wm, wn, lane);
+        if constexpr (C::DIAG) {
+            if (READ && i < C::NF && (src.fmask & (1u << i))) read_frag<C, KIND, S_READ>(g, i, ks_next, wm, wn, lane);
+        } else {
+            if (READ && i < C::NF) read_frag<C, KIND, S_READ>(g, i, ks_next, wm, wn, lane);
+        }
         if (ISSUE_DMA && i % EVERY == 0) dma_block<C, KIND, S_DMA>(src, kt_dma, i / EVERY, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// Stage kt, held in slot S (= kt mod 2), four 16-k substeps; fa holds the
-// first substep's fragments on entry.  After the third substep each wave
-// waits for its own DMA of stage kt+1 (the only loads in flight) and for its
-// LDS reads, then the barrier: stage kt+1 has landed everywhere and no wave
-// reads slot S any more, so the fourth substep refills it with stage kt+2
-// while reading stage kt+1's first fragments from the other slot.
+// Substeps I .. SUBSTEPS-2 of a stage in slot S: substep i computes with the
+// fragments in fa (i even) or fb (i odd) and reads substep i+1's into the other.
+template <class C, int KIND, int S, int I>
+__device__ __forceinline__ void early_substeps(floatx16 (&acc)[C::MI][C::NI], const Src &src, int wave, int wm,
+                                               int wn, int lane, Frags &fa, Frags &fb) {
+    if constexpr (I < C::SUBSTEPS - 1) {
+        if constexpr (I % 2 == 0)
+            substep<C, KIND, S, true, S, false>(acc, fa, fb, I + 1, src, 0, wave, wm, wn, lane);
+        else
+            substep<C, KIND, S, true, S, false>(acc, fb, fa, I + 1, src, 0, wave, wm, wn, lane);
+        early_substeps<C, KIND, S, I + 1>(acc, src, wave, wm, wn, lane, fa, fb);
+    }
+}
+
+// Stage kt, held in slot S, of SUBSTEPS 16-k substeps; fa holds the first
+// substep's fragments on entry.  Before the last substep each wave waits for
+// its own DMA of stage kt+1 (the only loads in flight) and for its LDS reads,
+// then the barrier: stage kt+1 has landed everywhere and no wave reads slot S
+// any more, so the last substep refills it with stage kt+2 while reading
+// stage kt+1's first fragments from the other slot.
 template <class C, int KIND, int S, bool ISSUE, bool LAST>
 __device__ __forceinline__ void ring_stage(floatx16 (&acc)[C::MI][C::NI], const Src &src, int kt, int wave, int wm,
                                            int wn, int lane, Frags &fa, Frags &fb) {
-    static_assert(C::SUBSTEPS == 4, "four substeps per stage");
-    substep<C, KIND, S, true, S, false>(acc, fa, fb, 1, src, 0, wave, wm, wn, lane);
-    substep<C, KIND, S, true, S, false>(acc, fb, fa, 2, src, 0, wave, wm, wn, lane);
-    substep<C, KIND, S, true, S, false>(acc, fa, fb, 3, src, 0, wave, wm, wn, lane);
+    static_assert(C::SUBSTEPS % 2 == 0, "the last substep computes with fb");
+    early_substeps<C, KIND, S, 0>(acc, src, wave, wm, wn, lane, fa, fb);
     if constexpr (LAST) {
         substep<C, KIND, S, false, S, false>(acc, fb, fa, 0, src, 0, wave, wm, wn, lane);
     } else {
@@ -314,31 +358,54 @@ __device__ __forceinline__ void ring_stage(floatx16 (&acc)[C::MI][C::NI], const 
     }
 }
 
-// The K loop over nk stages (nk even, at least 2): stages 0 and 1 are loaded
-// up front (loads retire in issue order, so vmcnt(LPS) leaves exactly stage
-// 1's in flight once stage 0 has landed).  pre_last() runs before the last
-// stage, when no wave reads slot 0 any more (every wave has passed the
-// barrier of stage nk-2): it may start loads into slot 0.
+// The K loop over nk stages (nk even, at least 2; any nk >= 1 for C::PACKED):
+// stages 0 and 1 are loaded up front (loads retire in issue order, so
+// vmcnt(LPS) leaves exactly stage 1's in flight once stage 0 has landed).
+// The last stage runs in slot 1 (an odd count starts in slot 1), and
+// pre_last() runs before it, when no wave reads slot 0 any more (every wave
+// has passed the barrier of the stage before): it may start loads into slot 0.
 template <class C, int KIND, class PreLast>
 __device__ __forceinline__ void main_loop(floatx16 (&acc)[C::MI][C::NI], const Src &src, int nk, int wave, int wm,
                                           int wn, int lane, const PreLast &pre_last) {
     static_assert(C::STAGES == 2 && C::NF <= C::NM, "ring");
     constexpr int L = C::LPS;
-#pragma unroll
-    for (int j = 0; j < L; ++j) dma_block<C, KIND, 0>(src, 0, j, wave, lane);
-#pragma unroll
-    for (int j = 0; j < L; ++j) dma_block<C, KIND, 1>(src, 1, j, wave, lane);
-    wait_vmcnt<L>();
-    stage_barrier();
     Frags fa, fb;
-#pragma unroll
-    for (int j = 0; j < C::NF; ++j) read_frag<C, KIND, 0>(fa, j, 0, wm, wn, lane);
     int kt = 0;
+    bool odd = false;
+    if constexpr (C::PACKED) odd = nk & 1;
+    if (odd) {
+        // an odd count starts in slot 1 (stage 0 runs on its own), so that
+        // the last stage still runs in slot 1
+#pragma unroll
+        for (int j = 0; j < L; ++j) dma_block<C, KIND, 1>(src, 0, j, wave, lane);
+        if (nk > 1) {
+#pragma unroll
+            for (int j = 0; j < L; ++j) dma_block<C, KIND, 0>(src, 1, j, wave, lane);
+            wait_vmcnt<L>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        stage_barrier();
+#pragma unroll
+        for (int j = 0; j < C::NF; ++j) read_frag<C, KIND, 1>(fa, j, 0, wm, wn, lane);
+        if (nk > 1) ring_stage<C, KIND, 1, true, false>(acc, src, 0, wave, wm, wn, lane, fa, fb);
+        kt = 1;
+    } else {
+#pragma unroll
+        for (int j = 0; j < L; ++j) dma_block<C, KIND, 0>(src, 0, j, wave, lane);
+#pragma unroll
+        for (int j = 0; j < L; ++j) dma_block<C, KIND, 1>(src, 1, j, wave, lane);
+        wait_vmcnt<L>();
+        stage_barrier();
+#pragma unroll
+        for (int j = 0; j < C::NF; ++j) read_frag<C, KIND, 0>(fa, j, 0, wm, wn, lane);
+    }
     for (; kt < nk - 2; kt += 2) {
         ring_stage<C, KIND, 0, true, false>(acc, src, kt, wave, wm, wn, lane, fa, fb);
         ring_stage<C, KIND, 1, true, false>(acc, src, kt + 1, wave, wm, wn, lane, fa, fb);
     }
-    ring_stage<C, KIND, 0, false, false>(acc, src, kt, wave, wm, wn, lane, fa, fb);
+    // (a count of one has only the stage in slot 1)
+    if (!C::PACKED || nk > 1) ring_stage<C, KIND, 0, false, false>(acc, src, kt, wave, wm, wn, lane, fa, fb);
     pre_last();
     ring_stage<C, KIND, 1, false, true>(acc, src, kt + 1, wave, wm, wn, lane, fa, fb);
 }
@@ -588,11 +655,18 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
     Src src;
     {
         // product i = (mi, ni) covers block row wm*MI + mi, block column wn*NI + ni
-        uint32_t m = 0;
+        // and takes fragments a[mi] (read first for mi = 0, else after the
+        // b's) and b[ni]
+        uint32_t m = 0, fm = 0;
 #pragma unroll
         for (int i = 0; i < C::NM; ++i)
-            if (wm * C::MI + i / C::NI >= wn * C::NI + i % C::NI) m |= 1u << i;
+            if (wm * C::MI + i / C::NI >= wn * C::NI + i % C::NI) {
+                m |= 1u << i;
+                const int mi = i / C::NI, ni = i % C::NI;
+                fm |= (1u << (mi == 0 ? 0 : C::NI + mi)) | (1u << (1 + ni));
+            }
         src.mmask = __builtin_amdgcn_readfirstlane(m);
+        src.fmask = __builtin_amdgcn_readfirstlane(fm);
     }
     int64_t kdim;
     if (KIND == GRAM) {
@@ -634,9 +708,12 @@ __global__ __launch_bounds__(C::NT, 1) void ns_sym_kernel(Geom g, Work w, NsStep
             }
     };
     const int nk = static_cast<int>((k1 - k0) / C::BK);
-    if (diag)
-        main_loop<CfgDiag, KIND>(acc, src, nk, wave, wm, wn, lane, pre_last);
-    else if (__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(ti) * C::BM + wm * C::WM >= g.s)))
+    if (diag) {
+        // P and Q are the same rows: a slot holds 128 k of them (CfgDiag)
+        Src one = src;
+        one.q = src.p + C::ROWB;
+        main_loop<CfgDiag, KIND>(acc, one, nk / 2, wave, wm, wn, lane, pre_last);
+    } else if (__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<int64_t>(ti) * C::BM + wm * C::WM >= g.s)))
         main_loop<CfgIdle, KIND>(acc, src, nk, wave, wm, wn, lane, pre_last);
     else
         main_loop<C, KIND>(acc, src, nk, wave, wm, wn, lane, pre_last);

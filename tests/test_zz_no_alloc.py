@@ -59,10 +59,15 @@ def test_noalloc_matches_muon_step(torch_mod):
     # 43 x 768x8192: the group's last two Gram tiles run split over K; in the fixed
     # scratch the group runs in chunks of three matrices, whose last chunk holds them
     tail = [S(768, 8192)] * 43
+    # 21 x 1792x1792: the last five a X + B X tiles run split over K, three
+    # ranges each; they lie in the last matrix, which the fixed scratch runs
+    # as a chunk of its own
+    apply_tail = [S(1792, 1792)] * 21
     ctx = ms.Context(0)
     try:
         for k, (specs, seed, prec) in enumerate(((first, 201, ms.MUON_NS_BF16), (second, 202, ms.MUON_NS_BF16),
-                                                 (second, 203, ms.MUON_NS_F32), (tail, 205, ms.MUON_NS_BF16))):
+                                                 (second, 203, ms.MUON_NS_F32), (tail, 205, ms.MUON_NS_BF16),
+                                                 (apply_tail, 206, ms.MUON_NS_BF16))):
             hosts = _hosts(specs, seed)
             hp = ms.make_hparams(ns_precision=prec)
             say(f"call {k + 1}: {len(specs)} matrices, muon_step_noalloc then muon_step")
