@@ -188,15 +188,24 @@ __global__ __launch_bounds__(256) void nesterov_rows_kernel(const MatDesc *__res
     if (threadIdx.x == 0) w.partials[blockIdx.x] = s;
 }
 
-// Four consecutive gradient values as floats (8-byte bf16 or 16-byte fp32 load).
-template <typename GradT> __device__ __forceinline__ floatx4 load4_val(const GradT *p);
-template <> __device__ __forceinline__ floatx4 load4_val<float>(const float *p) {
-    return *reinterpret_cast<const floatx4 *>(p);
+// Four consecutive gradient values as floats, one non-temporal 8-byte (bf16)
+// or 16-byte (fp32) load of a stream read once.
+template <typename GradT> __device__ __forceinline__ floatx4 load4_nt(const GradT *p);
+template <> __device__ __forceinline__ floatx4 load4_nt<float>(const float *p) {
+    return __builtin_nontemporal_load(as_global(reinterpret_cast<const floatx4 *>(p)));
 }
-template <> __device__ __forceinline__ floatx4 load4_val<uint16_t>(const uint16_t *p) {
-    const u32x2 h = *reinterpret_cast<const u32x2 *>(p);
+template <> __device__ __forceinline__ floatx4 load4_nt<uint16_t>(const uint16_t *p) {
+    const u32x2 h = __builtin_nontemporal_load(as_global(reinterpret_cast<const u32x2 *>(p)));
     return floatx4{__uint_as_float(h[0] << 16), __uint_as_float(h[0] & 0xffff0000u), __uint_as_float(h[1] << 16),
                    __uint_as_float(h[1] & 0xffff0000u)};
+}
+
+// Non-temporal vector load and store (streams touched once).
+template <class T> __device__ __forceinline__ T ld_nt(const void *p) {
+    return __builtin_nontemporal_load(as_global(reinterpret_cast<const T *>(p)));
+}
+template <class T> __device__ __forceinline__ void st_nt(void *p, T v) {
+    __builtin_nontemporal_store(v, as_global(reinterpret_cast<T *>(p)));
 }
 
 // Stage 1, rows > cols: X = N^T.  64 x 64 tiles of W transposed through LDS so
@@ -226,22 +235,29 @@ __global__ __launch_bounds__(256) void nesterov_tile_kernel(const MatDesc *__res
     uint8_t *__restrict__ xl = static_cast<uint8_t *>(w.xl) + e * w.x_stride;
     double acc = 0.0;
     if (VEC && i0 + 64 <= g.rows && j0 + 64 <= g.cols) {
+        // all four rows' G and M are requested before any is used; every
+        // global access is a non-temporal stream
         const int q4 = 4 * (threadIdx.x & 15), r16 = threadIdx.x >> 4;
+        floatx4 gv[4], m[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t src = (i0 + 16 * r + r16) * g.cols + j0 + q4;
+            gv[r] = load4_nt<GradT>(gp + src);
+            m[r] = __builtin_nontemporal_load(as_global(reinterpret_cast<const floatx4 *>(mp + src)));
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int ii = 16 * r + r16;
             const int64_t src = (i0 + ii) * g.cols + j0 + q4;
-            const floatx4 gv = load4_val<GradT>(gp + src);
-            const floatx4 m = *reinterpret_cast<const floatx4 *>(mp + src);
             floatx4 m1;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                m1[q] = mu * m[q] + gv[q];
-                const float n = nesterov ? (mu * m1[q] + gv[q]) : m1[q];
+                m1[q] = mu * m[r][q] + gv[r][q];
+                const float n = nesterov ? (mu * m1[q] + gv[r][q]) : m1[q];
                 acc += static_cast<double>(n) * static_cast<double>(n);
                 tile[ii][q4 + q] = n;
             }
-            *reinterpret_cast<floatx4 *>(mp + src) = m1;
+            __builtin_nontemporal_store(m1, as_global(reinterpret_cast<floatx4 *>(mp + src)));
         }
         __syncthreads();
         // X[j][i] = N[i][j]: lane (jj, c4) takes X row j0 + jj, columns i0 + c4 .. +3
@@ -253,13 +269,13 @@ __global__ __launch_bounds__(256) void nesterov_tile_kernel(const MatDesc *__res
             for (int q = 0; q < 4; ++q) v[q] = tile[q4 + q][jj];
             const int64_t off = (j0 + jj) * g.lp + i0 + q4;
             if (xf) {
-                *reinterpret_cast<floatx4 *>(xf + off) = v;
+                __builtin_nontemporal_store(v, as_global(reinterpret_cast<floatx4 *>(xf + off)));
             } else {
                 u32x2 h;
                 uint32_t l;
                 split_bf16x4(v, &h, &l);
-                *reinterpret_cast<u32x2 *>(xh + off) = h;
-                *reinterpret_cast<uint32_t *>(xl + off) = l;
+                __builtin_nontemporal_store(h, as_global(reinterpret_cast<u32x2 *>(xh + off)));
+                __builtin_nontemporal_store(l, as_global(reinterpret_cast<uint32_t *>(xl + off)));
             }
         }
     } else {
@@ -442,7 +458,8 @@ __global__ __launch_bounds__(256) void update_from_work_kernel(const MatDesc *__
 // Decay + update from the bf16 workspace X when X has W's row layout (not
 // transposed, l a multiple of 8, 16-byte aligned W and ns_out): 8 consecutive
 // elements per lane, 16 + 8 bytes of X and 16 (bf16) or 32 (fp32) bytes of W
-// in one load each.  Same arithmetic as update_from_work_kernel.
+// in one load each, every access a non-temporal stream.  Same arithmetic as
+// update_from_work_kernel.
 template <typename ParamT>
 __global__ __launch_bounds__(256) void update_from_work_vec_kernel(const MatDesc *__restrict__ descs, Geom g,
                                                                    Work w, float dscale, float sscale,
@@ -455,10 +472,10 @@ __global__ __launch_bounds__(256) void update_from_work_vec_kernel(const MatDesc
     if (w.uscale) sscale = w.uscale[e];
     const MatDesc d = descs[e];
     const int64_t xo = e * w.x_stride + r * g.lp + c;
-    const uint4 h = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(w.xb) + xo);
-    const uint2 l = *reinterpret_cast<const uint2 *>(static_cast<const uint8_t *>(w.xl) + xo);
-    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
-    const uint32_t lw[2] = {l.x, l.y};
+    const u32x4 h = ld_nt<u32x4>(static_cast<const uint16_t *>(w.xb) + xo);
+    const u32x2 l = ld_nt<u32x2>(static_cast<const uint8_t *>(w.xl) + xo);
+    const uint32_t hw[4] = {h[0], h[1], h[2], h[3]};
+    const uint32_t lw[2] = {l[0], l[1]};
     float xv[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
@@ -466,9 +483,9 @@ __global__ __launch_bounds__(256) void update_from_work_vec_kernel(const MatDesc
                           static_cast<uint8_t>(lw[k >> 2] >> (8 * (k & 3))));
     const int64_t dst = r * g.cols + c;
     if constexpr (sizeof(ParamT) == 2) {
-        uint4 *pw = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(d.param) + dst);
-        const uint4 wv = *pw;
-        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+        uint16_t *pw = static_cast<uint16_t *>(d.param) + dst;
+        const u32x4 wv = ld_nt<u32x4>(pw);
+        const uint32_t ww[4] = {wv[0], wv[1], wv[2], wv[3]};
         uint32_t o[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -476,19 +493,18 @@ __global__ __launch_bounds__(256) void update_from_work_vec_kernel(const MatDesc
             const float r1 = dscale * bf16_bits_to_float(static_cast<uint16_t>(ww[k] >> 16)) - sscale * xv[2 * k + 1];
             o[k] = static_cast<uint32_t>(float_to_bf16_bits(r0)) | (static_cast<uint32_t>(float_to_bf16_bits(r1)) << 16);
         }
-        *pw = make_uint4(o[0], o[1], o[2], o[3]);
+        st_nt<u32x4>(pw, u32x4{o[0], o[1], o[2], o[3]});
     } else {
-        float4 *pw = reinterpret_cast<float4 *>(static_cast<float *>(d.param) + dst);
-        const float4 a = pw[0], b = pw[1];
-        pw[0] = make_float4(dscale * a.x - sscale * xv[0], dscale * a.y - sscale * xv[1],
-                            dscale * a.z - sscale * xv[2], dscale * a.w - sscale * xv[3]);
-        pw[1] = make_float4(dscale * b.x - sscale * xv[4], dscale * b.y - sscale * xv[5],
-                            dscale * b.z - sscale * xv[6], dscale * b.w - sscale * xv[7]);
+        float *pw = static_cast<float *>(d.param) + dst;
+        const floatx4 a = ld_nt<floatx4>(pw), b = ld_nt<floatx4>(pw + 4);
+        st_nt<floatx4>(pw, floatx4{dscale * a[0] - sscale * xv[0], dscale * a[1] - sscale * xv[1],
+                                     dscale * a[2] - sscale * xv[2], dscale * a[3] - sscale * xv[3]});
+        st_nt<floatx4>(pw + 4, floatx4{dscale * b[0] - sscale * xv[4], dscale * b[1] - sscale * xv[5],
+                                         dscale * b[2] - sscale * xv[6], dscale * b[3] - sscale * xv[7]});
     }
     if (d.ns_out) {
-        float4 *po = reinterpret_cast<float4 *>(d.ns_out + dst);
-        po[0] = make_float4(xv[0], xv[1], xv[2], xv[3]);
-        po[1] = make_float4(xv[4], xv[5], xv[6], xv[7]);
+        st_nt<floatx4>(d.ns_out + dst, floatx4{xv[0], xv[1], xv[2], xv[3]});
+        st_nt<floatx4>(d.ns_out + dst + 4, floatx4{xv[4], xv[5], xv[6], xv[7]});
     }
 }
 
@@ -496,8 +512,9 @@ __global__ __launch_bounds__(256) void update_from_work_vec_kernel(const MatDesc
 // 64 x 64 tile per block.  X rows j0 .. j0+63, columns i0 .. i0+63 are read
 // 8 columns per load (16 + 8 bytes) into LDS, always inside the padded
 // workspace (sp and lp are multiples of 256); W rows i0 .. i0+63 are then
-// written 8 columns (W cols = X rows) per lane.  Needs cols % 8 == 0 so that
-// every 8-wide group of a W row is inside the matrix or wholly outside it.
+// written 8 columns (W cols = X rows) per lane, with non-temporal global
+// accesses.  Needs cols % 8 == 0 so that every 8-wide group of a W row is
+// inside the matrix or wholly outside it.
 template <typename ParamT>
 __global__ __launch_bounds__(256) void update_from_work_tvec_kernel(const MatDesc *__restrict__ descs, Geom g,
                                                                     Work w, float dscale, float sscale,
@@ -515,10 +532,10 @@ __global__ __launch_bounds__(256) void update_from_work_tvec_kernel(const MatDes
         const int q = threadIdx.x + 256 * half;
         const int row = q >> 3, cg = (q & 7) * 8;
         const int64_t xo = (j0 + row) * g.lp + i0 + cg;
-        const uint4 h = *reinterpret_cast<const uint4 *>(xh + xo);
-        const uint2 l = *reinterpret_cast<const uint2 *>(xl + xo);
-        const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
-        const uint32_t lw[2] = {l.x, l.y};
+        const u32x4 h = ld_nt<u32x4>(xh + xo);
+        const u32x2 l = ld_nt<u32x2>(xl + xo);
+        const uint32_t hw[4] = {h[0], h[1], h[2], h[3]};
+        const uint32_t lw[2] = {l[0], l[1]};
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             tile[row][cg + k] = join_bf16(static_cast<uint16_t>(hw[k >> 1] >> (16 * (k & 1))),
@@ -537,9 +554,9 @@ __global__ __launch_bounds__(256) void update_from_work_tvec_kernel(const MatDes
         for (int k = 0; k < 8; ++k) xv[k] = tile[wc + k][wr];
         const int64_t dst = i * g.cols + j;
         if constexpr (sizeof(ParamT) == 2) {
-            uint4 *pw = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(d.param) + dst);
-            const uint4 wv = *pw;
-            const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+            uint16_t *pw = static_cast<uint16_t *>(d.param) + dst;
+            const u32x4 wv = ld_nt<u32x4>(pw);
+            const uint32_t ww[4] = {wv[0], wv[1], wv[2], wv[3]};
             uint32_t o[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -549,19 +566,18 @@ __global__ __launch_bounds__(256) void update_from_work_tvec_kernel(const MatDes
                 o[k] = static_cast<uint32_t>(float_to_bf16_bits(r0)) |
                        (static_cast<uint32_t>(float_to_bf16_bits(r1)) << 16);
             }
-            *pw = make_uint4(o[0], o[1], o[2], o[3]);
+            st_nt<u32x4>(pw, u32x4{o[0], o[1], o[2], o[3]});
         } else {
-            float4 *pw = reinterpret_cast<float4 *>(static_cast<float *>(d.param) + dst);
-            const float4 a = pw[0], b = pw[1];
-            pw[0] = make_float4(dscale * a.x - sscale * xv[0], dscale * a.y - sscale * xv[1],
-                                dscale * a.z - sscale * xv[2], dscale * a.w - sscale * xv[3]);
-            pw[1] = make_float4(dscale * b.x - sscale * xv[4], dscale * b.y - sscale * xv[5],
-                                dscale * b.z - sscale * xv[6], dscale * b.w - sscale * xv[7]);
+            float *pw = static_cast<float *>(d.param) + dst;
+            const floatx4 a = ld_nt<floatx4>(pw), b = ld_nt<floatx4>(pw + 4);
+            st_nt<floatx4>(pw, floatx4{dscale * a[0] - sscale * xv[0], dscale * a[1] - sscale * xv[1],
+                                         dscale * a[2] - sscale * xv[2], dscale * a[3] - sscale * xv[3]});
+            st_nt<floatx4>(pw + 4, floatx4{dscale * b[0] - sscale * xv[4], dscale * b[1] - sscale * xv[5],
+                                             dscale * b[2] - sscale * xv[6], dscale * b[3] - sscale * xv[7]});
         }
         if (d.ns_out) {
-            float4 *po = reinterpret_cast<float4 *>(d.ns_out + dst);
-            po[0] = make_float4(xv[0], xv[1], xv[2], xv[3]);
-            po[1] = make_float4(xv[4], xv[5], xv[6], xv[7]);
+            st_nt<floatx4>(d.ns_out + dst, floatx4{xv[0], xv[1], xv[2], xv[3]});
+            st_nt<floatx4>(d.ns_out + dst + 4, floatx4{xv[4], xv[5], xv[6], xv[7]});
         }
     }
 }
