@@ -167,9 +167,13 @@ __device__ __forceinline__ void stage_barrier() {
 // them (lgkmcnt 0), which stalls the fragment pipeline; the kernels count
 // these loads themselves (wait_vmcnt) and fence LDS reads with barriers that
 // carry a memory clobber.
-__device__ __forceinline__ void dma16(const char *g, const char *l) {
+template <bool NT = false> __device__ __forceinline__ void dma16(const char *g, const char *l) {
     const unsigned m0 = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>(l)));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(m0)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
 
 // K-contiguous tile (rows x 128 bytes): 16-byte chunk c of row r lives at
@@ -414,13 +418,13 @@ __device__ __forceinline__ void main_loop(floatx16 (&acc)[C::MI][C::NI], const S
 // at `src` (row pitch ld bytes) into a staging area: instructions of 8 rows
 // each; lane i carries row i/8, chunk i%8 stored at chunk (i%8) ^ ((row/2)%8),
 // so 16 consecutive rows reading one chunk touch 16 distinct bank groups.
-template <class C>
+template <class C, bool NT = false>
 __device__ __forceinline__ void dma_bf16_rows(char *dst, const char *src, int64_t ld, int lane) {
 #pragma unroll
     for (int t = 0; t < C::EPI_ROWS / 8; ++t) {
         const int row = 8 * t + (lane >> 3);
         const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-        dma16(src + row * ld + chunk * 16, dst + t * 1024);
+        dma16<NT>(src + row * ld + chunk * 16, dst + t * 1024);
     }
 }
 __device__ __forceinline__ int pair_offset(int row, int col) {
@@ -431,13 +435,13 @@ __device__ __forceinline__ int pair_offset(int row, int col) {
 // at `src` (row pitch ld bytes) into a staging area: instructions of 16 rows
 // each; lane i carries row i/4, chunk i%4 stored at chunk (i%4) ^ ((row/4)%4),
 // so 16 consecutive rows reading one 4-byte word touch 16 distinct banks.
-template <class C>
+template <class C, bool NT = false>
 __device__ __forceinline__ void dma_lo8_rows(char *dst, const char *src, int64_t ld, int lane) {
 #pragma unroll
     for (int t = 0; t < C::EPI_ROWS / 16; ++t) {
         const int row = 16 * t + (lane >> 2);
         const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-        dma16(src + row * ld + chunk * 16, dst + t * 1024);
+        dma16<NT>(src + row * ld + chunk * 16, dst + t * 1024);
     }
 }
 __device__ __forceinline__ int lo8_offset(int row, int col) {
@@ -569,7 +573,8 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
             u32x2 pk;
             pk[0] = pack_bf16x2(x[0], x[1]);
             pk[1] = pack_bf16x2(x[2], x[3]);
-            if (!diag || brow >= wn * C::NI + (chunk >> 3)) *reinterpret_cast<u32x2 *>(dst + idx) = pk;
+            if (!diag || brow >= wn * C::NI + (chunk >> 3))
+                __builtin_nontemporal_store(pk, as_global(reinterpret_cast<u32x2 *>(dst + idx)));
         }
         {
             // column c of the block -> row col0 + c of the mirrored tile; lane
@@ -585,7 +590,7 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
                 u32x4 pk;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) pk[k] = pack_bf16x2(f[2 * k], f[2 * k + 1]);
-                *reinterpret_cast<u32x4 *>(dst + (col0 + c) * ld + rbase + 8 * part) = pk;
+                __builtin_nontemporal_store(pk, as_global(reinterpret_cast<u32x4 *>(dst + (col0 + c) * ld + rbase + 8 * part)));
             }
         }
         if constexpr (KIND == POLY) {
@@ -809,10 +814,10 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 // (the compiler builds a 64-bit vector address per store otherwise).  Plain
 // vector stores: they count in vmcnt like any other.
 __device__ __forceinline__ void store_saddr(char *base, uint32_t off, const u32x2 &v) {
-    asm volatile("global_store_dwordx2 %0, %1, %2" ::"v"(off), "v"(v), "s"(base) : "memory");
+    asm volatile("global_store_dwordx2 %0, %1, %2 nt" ::"v"(off), "v"(v), "s"(base) : "memory");
 }
 __device__ __forceinline__ void store_saddr(char *base, uint32_t off, uint32_t v) {
-    asm volatile("global_store_dword %0, %1, %2" ::"v"(off), "v"(v), "s"(base) : "memory");
+    asm volatile("global_store_dword %0, %1, %2 nt" ::"v"(off), "v"(v), "s"(base) : "memory");
 }
 
 // Output block of one wave in the apply epilogue.
@@ -837,8 +842,8 @@ __device__ __forceinline__ XRows x_rows(const Geom &g, const Work &w, const Appl
             g.lp};
 }
 __device__ __forceinline__ void dma_x_round(char *dst, const XRows &x, int h, int lane) {
-    dma_bf16_rows<Cfg>(dst, x.hi + Cfg::EPI_ROWS * h * x.ld_hi, x.ld_hi, lane);
-    dma_lo8_rows<Cfg>(dst + PAIR_HALF, x.lo + Cfg::EPI_ROWS * h * x.ld_lo, x.ld_lo, lane);
+    dma_bf16_rows<Cfg, true>(dst, x.hi + Cfg::EPI_ROWS * h * x.ld_hi, x.ld_hi, lane);
+    dma_lo8_rows<Cfg, true>(dst + PAIR_HALF, x.lo + Cfg::EPI_ROWS * h * x.ld_lo, x.ld_lo, lane);
 }
 
 // Row lrow's four columns lcol .. lcol+3 of a X + B X, with X = X_hi + X_lo
@@ -885,8 +890,8 @@ __device__ __forceinline__ void stage_values(const floatx16 (&accm)[C::NI], char
 
 // DMA of round h's X_hi rows to hi and X_lo rows to lo (two staging places).
 __device__ __forceinline__ void dma_x_round_to(char *hi, char *lo, const XRows &x, int h, int lane) {
-    dma_bf16_rows<Cfg>(hi, x.hi + Cfg::EPI_ROWS * h * x.ld_hi, x.ld_hi, lane);
-    dma_lo8_rows<Cfg>(lo, x.lo + Cfg::EPI_ROWS * h * x.ld_lo, x.ld_lo, lane);
+    dma_bf16_rows<Cfg, true>(hi, x.hi + Cfg::EPI_ROWS * h * x.ld_hi, x.ld_hi, lane);
+    dma_lo8_rows<Cfg, true>(lo, x.lo + Cfg::EPI_ROWS * h * x.ld_lo, x.ld_lo, lane);
 }
 
 // The wave's 32 x 64 block of X' = a X + acc, X read from the pair staged at
@@ -1095,7 +1100,7 @@ __device__ __forceinline__ void apply_epilogue_update(const floatx16 (&acc)[Cfg:
 // rows of 128 bytes: lane i of instruction t carries row 8t + i/8, chunk i%8.
 __device__ __forceinline__ void dma_w_half(char *dst, const char *src, int64_t ld, int lane) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) dma16(src + (8 * t + (lane >> 3)) * ld + (lane & 7) * 16, dst + t * 1024);
+    for (int t = 0; t < 2; ++t) dma16<true>(src + (8 * t + (lane >> 3)) * ld + (lane & 7) * 16, dst + t * 1024);
 }
 
 // The fused update for a bf16 W in the orientation of X', on a wave block that
