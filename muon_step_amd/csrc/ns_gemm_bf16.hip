@@ -812,12 +812,16 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 
 // Global stores addressed as a scalar base plus a 32-bit per-lane offset
 // (the compiler builds a 64-bit vector address per store otherwise).  Plain
-// vector stores: they count in vmcnt like any other.
+// vector stores: they count in vmcnt like any other.  In the apply epilogue
+// the 8-byte form carries X'_hi, whole 128-byte lines, and goes out
+// non-temporal; the 4-byte form carries X'_lo, whose rows are 64-byte halves
+// of a line (the other half is another wave's), and stays temporal so that
+// L2 merges the halves before write-back.
 __device__ __forceinline__ void store_saddr(char *base, uint32_t off, const u32x2 &v) {
     asm volatile("global_store_dwordx2 %0, %1, %2 nt" ::"v"(off), "v"(v), "s"(base) : "memory");
 }
 __device__ __forceinline__ void store_saddr(char *base, uint32_t off, uint32_t v) {
-    asm volatile("global_store_dword %0, %1, %2 nt" ::"v"(off), "v"(v), "s"(base) : "memory");
+    asm volatile("global_store_dword %0, %1, %2" ::"v"(off), "v"(v), "s"(base) : "memory");
 }
 
 // Output block of one wave in the apply epilogue.
