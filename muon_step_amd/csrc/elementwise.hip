@@ -388,13 +388,23 @@ __global__ __launch_bounds__(256) void normalize_kernel(Geom g, Work w, int bloc
 }
 
 // Zeros the padding (outside s x l, inside sp x lp) of the pair (xb, xl)
-// that the momentum pass leaves untouched.  Block (e, i) handles padded row i.
-__global__ __launch_bounds__(256) void pad_zero_kernel(Geom g, Work w) {
-    const int64_t e = blockIdx.x / g.sp;
-    const int64_t i = blockIdx.x % g.sp;
+// that the momentum pass leaves untouched.  Block (e, r) handles padded row
+// row0 + r of matrix e: rows below s only hold padding when l < lp, so the
+// launch covers them only then.  A row at or beyond s is padding whole and
+// is cleared with 16-byte stores (rows start 256 elements apart from an
+// aligned base).
+__global__ __launch_bounds__(256) void pad_zero_kernel(Geom g, Work w, int64_t rows_per_mat, int64_t row0) {
+    const int64_t e = blockIdx.x / rows_per_mat;
+    const int64_t i = row0 + blockIdx.x % rows_per_mat;
     uint16_t *xh = static_cast<uint16_t *>(w.xb) + e * w.x_stride + i * g.lp;
     uint8_t *xl = static_cast<uint8_t *>(w.xl) + e * w.x_stride + i * g.lp;
-    for (int64_t j = (i < g.s ? g.l : 0) + threadIdx.x; j < g.lp; j += 256) {
+    if (i >= g.s) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int64_t j = threadIdx.x; j < g.lp / 8; j += 256) reinterpret_cast<u32x4 *>(xh)[j] = z;
+        for (int64_t j = threadIdx.x; j < g.lp / 16; j += 256) reinterpret_cast<u32x4 *>(xl)[j] = z;
+        return;
+    }
+    for (int64_t j = g.l + threadIdx.x; j < g.lp; j += 256) {
         xh[j] = 0;
         xl[j] = 0;
     }
@@ -904,7 +914,10 @@ hipError_t launch_normalize(int nmat, const Geom &g, const Work &w, int prenorm_
 }
 
 hipError_t launch_pad_zero(int nmat, const Geom &g, const Work &w, hipStream_t st) {
-    hipLaunchKernelGGL(pad_zero_kernel, dim3(static_cast<unsigned>(g.sp * nmat)), dim3(256), 0, st, g, w);
+    const int64_t row0 = g.l < g.lp ? 0 : g.s;  // rows below s hold padding only when l < lp
+    const int64_t rows = g.sp - row0;
+    if (rows <= 0 || nmat <= 0) return hipSuccess;
+    hipLaunchKernelGGL(pad_zero_kernel, dim3(static_cast<unsigned>(rows * nmat)), dim3(256), 0, st, g, w, rows, row0);
     return hipGetLastError();
 }
 hipError_t launch_update_plain(void *param, int param_bf16, const float *x, int64_t n, float d,
