@@ -16,33 +16,32 @@
 //                             X = X_hi + X_lo.  The last step instead
 //                             writes W <- d W - s_scale X' (and O'_t).
 //
-// Data movement.  All three products use 256 x 256 tiles, one workgroup of
-// 8 waves per CU (two per SIMD), each wave owning a 128 x 64 block computed
-// with v_mfma_f32_32x32x16_bf16 into fp32 accumulators.  Operand slabs of
-// 64 k (one 128-byte line per row) are copied global -> LDS by the
-// 16-byte-per-lane DMA (global_load_lds_dwordx4) into a ring of two stages
-// (128 KB); a diagonal tile of GRAM or POLY, whose output rows and columns
-// are the same rows of the operand, fills a slot with 128 k of those rows
-// instead of the same 64 k twice (CfgDiag).  Every product is followed by
-// at most one fragment read for the next 16-k substep; the last of a stage's
-// substeps also refills the slot just read with the stage after next, so LDS
-// reads and copies run under the MFMAs; one barrier per stage, before its
-// last substep.  The LDS layouts are XOR-swizzled so that every 16-lane
-// phase of a fragment read touches all 64 banks once.  The X operand of B X is stored as it lies in
-// memory (k rows, n contiguous) and read with ds_read_b64_tr_b16, which hands
-// each lane four consecutive k of one column.  The products are issued with
-// the operands swapped, so each lane's accumulators hold four consecutive
-// columns of one output row; every epilogue stages its block through LDS in
-// rounds of 32 rows and stores whole rows (GRAM/POLY also store the block's
-// columns as rows of the mirrored tile; APPLY moves 6 bytes per output
-// element: X_hi and its 8-bit residual X_lo in and out; the fused update of
-// a bf16 W brings W's rows by DMA too).  K loops stop at the true length
-// rounded to 128 (the padding is zero).  Block ids are renumbered so one
-// matrix's tiles share an XCD (and its L2).  Tiles that would run as a
-// launch's last, partial wave (every tile, for a Gram or A^2 of a group too
-// small to fill half a wave) may instead run split over K ranges whose fp32
-// partial tiles a reduce sums in a fixed order and finishes as the epilogue
-// would (sym_reduce_kernel, apply_reduce_kernel).
+// Data movement.  All three products use 256 x 256 tiles, one workgroup of 8
+// waves per CU (two per SIMD), each wave owning a 128 x 64 block computed with
+// v_mfma_f32_32x32x16_bf16 into fp32 accumulators.  Operand slabs of 64 k (one
+// 128-byte line per row) are copied global -> LDS by the 16-byte-per-lane DMA
+// (global_load_lds_dwordx4) into a ring of two stages (128 KB); a diagonal tile
+// of GRAM or POLY, whose output rows and columns are the same rows of the
+// operand, fills a slot with 128 k of those rows instead of the same 64 k twice
+// (CfgDiag).  Every product is followed by at most one fragment read for the
+// next 16-k substep; the last of a stage's substeps also refills the slot just
+// read with the stage after next, so LDS reads and copies run under the MFMAs;
+// one barrier per stage, before its last substep.  The LDS layouts are
+// XOR-swizzled so that every 16-lane phase of a fragment read touches all 64
+// banks once.  The X operand of B X is stored as it lies in memory (k rows, n
+// contiguous) and read with ds_read_b64_tr_b16, which hands each lane four
+// consecutive k of one column.  The products are issued with the operands
+// swapped, so each lane's accumulators hold four consecutive columns of one
+// output row; every epilogue stages its block through LDS in rounds of 32 rows
+// and stores whole rows (GRAM/POLY also store the block's columns as rows of
+// the mirrored tile; APPLY moves 6 bytes per output element: X_hi and its 8-bit
+// residual X_lo in and out; the fused update of a bf16 W brings W's rows by DMA
+// too).  K loops stop at the true length rounded to 128 (the padding is zero).
+// Block ids are renumbered so one matrix's tiles share an XCD (and its L2).
+// Tiles that would run as a launch's last, partial wave (every tile, for a Gram
+// or A^2 of a group too small to fill half a wave) may instead run split over K
+// ranges whose fp32 partial tiles a reduce sums in a fixed order and finishes
+// as the epilogue would (sym_reduce_kernel, apply_reduce_kernel).
 #include <algorithm>
 
 #include "common.hpp"
@@ -318,7 +317,8 @@ __device__ __forceinline__ void substep(floatx16 (&acc)[C::MI][C::NI], const Fra
             mma_one<C>(acc, f, i);
         }
         if constexpr (C::DIAG) {
-            if (READ && i < C::NF && (src.fmask & (1u << i))) read_frag<C, KIND, S_READ>(g, i, ks_next, wm, wn, lane);
+            if (READ && i < C::NF && (src.fmask & (1u << i)))
+                read_frag<C, KIND, S_READ>(g, i, ks_next, wm, wn, lane);
         } else {
             if (READ && i < C::NF) read_frag<C, KIND, S_READ>(g, i, ks_next, wm, wn, lane);
         }
@@ -590,7 +590,8 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
                 u32x4 pk;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) pk[k] = pack_bf16x2(f[2 * k], f[2 * k + 1]);
-                __builtin_nontemporal_store(pk, as_global(reinterpret_cast<u32x4 *>(dst + (col0 + c) * ld + rbase + 8 * part)));
+                __builtin_nontemporal_store(
+                    pk, as_global(reinterpret_cast<u32x4 *>(dst + (col0 + c) * ld + rbase + 8 * part)));
             }
         }
         if constexpr (KIND == POLY) {
