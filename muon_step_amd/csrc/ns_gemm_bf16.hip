@@ -317,8 +317,7 @@ __device__ __forceinline__ void substep(floatx16 (&acc)[C::MI][C::NI], const Fra
             mma_one<C>(acc, f, i);
         }
         if constexpr (C::DIAG) {
-            if (READ && i < C::NF && (src.fmask & (1u << i)))
-                read_frag<C, KIND, S_READ>(g, i, ks_next, wm, wn, lane);
+            if (READ && i < C::NF && (src.fmask & (1u << i))) read_frag<C, KIND, S_READ>(g, i, ks_next, wm, wn, lane);
         } else {
             if (READ && i < C::NF) read_frag<C, KIND, S_READ>(g, i, ks_next, wm, wn, lane);
         }
@@ -590,8 +589,7 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::MI][C::NI]
                 u32x4 pk;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) pk[k] = pack_bf16x2(f[2 * k], f[2 * k + 1]);
-                __builtin_nontemporal_store(
-                    pk, as_global(reinterpret_cast<u32x4 *>(dst + (col0 + c) * ld + rbase + 8 * part)));
+                __builtin_nontemporal_store(pk, as_global(reinterpret_cast<u32x4 *>(dst + (col0 + c) * ld + rbase + 8 * part)));
             }
         }
         if constexpr (KIND == POLY) {
