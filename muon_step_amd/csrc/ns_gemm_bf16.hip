@@ -345,7 +345,8 @@ __device__ __forceinline__ void early_substeps(floatx16 (&acc)[C::MI][C::NI], co
 // its own DMA of stage kt+1 (the only loads in flight) and for its LDS reads,
 // then the barrier: stage kt+1 has landed everywhere and no wave reads slot S
 // any more, so the last substep refills it with stage kt+2 while reading
-// stage kt+1's first fragments from the other slot.
+// stage kt+1's first fragments from the other slot.  That substep runs at a
+// raised wave priority (Gram and A^2 1-2% faster, apply unchanged).
 template <class C, int KIND, int S, bool ISSUE, bool LAST>
 __device__ __forceinline__ void ring_stage(floatx16 (&acc)[C::MI][C::NI], const Src &src, int kt, int wave, int wm,
                                            int wn, int lane, Frags &fa, Frags &fb) {
@@ -357,7 +358,11 @@ __device__ __forceinline__ void ring_stage(floatx16 (&acc)[C::MI][C::NI], const 
         wait_lgkm0();
         wait_vmcnt<0>();
         stage_barrier();
+        // the substep that issues the copies of stage kt+2 goes first on its
+        // SIMD, so that they leave as early as possible
+        __builtin_amdgcn_s_setprio(3);
         substep<C, KIND, 1 - S, true, S, ISSUE>(acc, fb, fa, 0, src, kt + 2, wave, wm, wn, lane);
+        __builtin_amdgcn_s_setprio(0);
     }
 }
 
