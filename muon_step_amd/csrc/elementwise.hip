@@ -846,22 +846,20 @@ hipError_t launch_stream_probe(const void *src, void *dst, int64_t nvec, int64_t
 // ---------------------------------------------------------------------------
 // Host launchers.
 
-int nesterov_blocks_per_mat(const Geom &g, int *rows_per_block, int *tiles_c) {
+int nesterov_blocks_per_mat(const Geom &g, int *tiles_c) {
     if (g.transposed) {
         *tiles_c = static_cast<int>((g.cols + 63) / 64);
-        *rows_per_block = 64;
         return static_cast<int>(((g.rows + 63) / 64) * *tiles_c);
     }
     // kMomElems consecutive elements per block (64 x 64 = one tile's worth)
-    *rows_per_block = 0;
     *tiles_c = 0;
     return static_cast<int>((g.rows * g.cols + kMomElems - 1) / kMomElems);
 }
 
 hipError_t launch_nesterov(const MatDesc *descs, int nmat, const Geom &g, const Work &w, float mu,
                            int nesterov, int grad_bf16, bool vec_ok, hipStream_t st) {
-    int rpb = 0, tc = 0;
-    const int bpm = nesterov_blocks_per_mat(g, &rpb, &tc);
+    int tc = 0;
+    const int bpm = nesterov_blocks_per_mat(g, &tc);
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(bpm) * nmat)), block(256);
     const bool vec = vec_ok && (g.cols % 4 == 0) && (g.lp % 4 == 0);
     if (g.transposed && vec) {

@@ -22,7 +22,10 @@ constexpr size_t kScratchBytes = size_t(128) << 20;
 hipError_t scratch_address(void **out);
 
 // ---- elementwise (elementwise.hip)
-int nesterov_blocks_per_mat(const Geom &g, int *rows_per_block, int *tiles_c);
+// Workgroups per matrix of the momentum pass, and so its ||N||^2 partial sums
+// per matrix: one per 4096 consecutive elements (rows <= cols), or one per
+// 64 x 64 tile of W when X is W transposed (*tiles_c: tiles per tile row).
+int nesterov_blocks_per_mat(const Geom &g, int *tiles_c);
 hipError_t launch_nesterov(const MatDesc *descs, int nmat, const Geom &g, const Work &w, float mu,
                            int nesterov, int grad_bf16, bool vec_ok, hipStream_t st);
 hipError_t launch_norm_finalize(const MatDesc *descs, int nmat, const Work &w, int blocks_per_mat,

@@ -449,9 +449,9 @@ muon_status plan_groups(const muon_matrix *mats, int64_t count, int32_t precisio
         // Keep every grouped launch inside a 32-bit grid.
         const int64_t apply_tiles = (gp.g.sp / muon::kTile) * (gp.g.lp / muon::kTile);
         n = std::min<int64_t>(n, std::max<int64_t>(1, ((int64_t(1) << 31) - 1) / apply_tiles));
-        int rpb = 0, tc = 0;
-        gp.bpm = std::max(muon::nesterov_blocks_per_mat(run_geom(gp.g, false), &rpb, &tc),
-                          muon::nesterov_blocks_per_mat(run_geom(gp.g, true), &rpb, &tc));
+        int tc = 0;
+        gp.bpm = std::max(muon::nesterov_blocks_per_mat(run_geom(gp.g, false), &tc),
+                          muon::nesterov_blocks_per_mat(run_geom(gp.g, true), &tc));
         n = std::min<int64_t>(n, std::max<int64_t>(1, ((int64_t(1) << 31) - 1) / gp.bpm));
         gp.chunk = n;
         *ws_bytes = std::max(*ws_bytes, chunk_layout(gp.g, bf16, n, sm.kpart(n)).total);
@@ -981,8 +981,8 @@ muon_status step_impl(muon_context *ctx, const muon_matrix *mats, int64_t count,
                     const muon_matrix &m = mats[gp.members[c0 + k]];
                     vec_ok = vec_ok && aligned16(m.momentum) && aligned16(m.grad);
                 }
-                int rpb = 0, tc = 0;
-                const int bpm = muon::nesterov_blocks_per_mat(run.g, &rpb, &tc);
+                int tc = 0;
+                const int bpm = muon::nesterov_blocks_per_mat(run.g, &tc);
                 const double elems = static_cast<double>(gp.g.s) * gp.g.l * run.n;
                 // M read and written (8), N written: fp32 (4) or hi + residual (3)
                 hipError_t e = timed(ctx, ST_MOMENTUM, 0.0, elems * (gsz + (bf16 ? 11.0 : 12.0)), st, [&] {
