@@ -265,18 +265,29 @@ def workload_step(args):
         ctx.muon_step(mats, hp, stream)
         torch.cuda.synchronize()
         log(f"warmup step {i + 1}/{args.warmup} done")
-    ctx.muon_profile_enable(True)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        ctx.muon_step(mats, hp, stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(stop) / args.steps
+
+    def timed_steps():
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            ctx.muon_step(mats, hp, stream)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps
+
+    # the step as a caller runs it (groups of different shapes concurrently),
+    # then with the groups in turn, and once more under per-stage timing (which
+    # runs them in turn) for the breakdown
+    ms_per_step = timed_steps()
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+    ctx.muon_set_concurrent_groups(False)
+    ms_in_turn = timed_steps()
+    log(f"timed {args.steps} steps with the groups in turn: {ms_in_turn:.3f} ms/step")
+    ctx.muon_profile_enable(True)
+    timed_steps()
     stages = ctx.muon_profile_read()
     ctx.close()
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
     for name, st in stages.items():
         rate = (f"{st['flops'] / st['total_ms'] / 1e9:8.1f} TFLOP/s" if st["flops"] else
                 f"{st['bytes'] / st['total_ms'] / 1e6:8.1f} GB/s" if st["total_ms"] else "")
@@ -295,6 +306,7 @@ def workload_step(args):
     print(json.dumps({
         "metric": f"Muon optimizer steps/sec + NS TFLOP/s (% bf16 MFMA peak), {wl.name}",
         "value": round(1000.0 / ms_per_step, 4), "unit": "steps/s", "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step_groups_in_turn": round(ms_in_turn, 3),
         "steps": args.steps, "warmup": args.warmup, "n_gpus": 1, "dtype": "bf16",
         "data": "synthetic (seeded low-rank-plus-noise bf16 gradients, N(0,0.02) bf16 params)",
         "config": {"workload": wl.name, "matrices": [[sp.rows, sp.cols] for sp in specs], "ns_steps": 10,

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MUON_STEP_ABI_VERSION 3
+#define MUON_STEP_ABI_VERSION 4
 
 /* Bytes of the fixed per-GPU device scratch muon_step_noalloc works in. */
 #define MUON_NOALLOC_SCRATCH_BYTES 134217728
@@ -198,8 +198,9 @@ muon_status muon_check_adamw_args(const muon_adamw_tensor *ts, int64_t count,
                                   const muon_adamw_hparams *hp, char *msg, size_t msg_cap);
 
 /* Workspace the library would allocate for this argument list when nothing
- * caps it: the largest per-group chunk of Newton-Schulz buffers plus the
- * per-matrix tables.  Pure host function; validates like
+ * caps it: the largest per-group chunk of Newton-Schulz buffers (with
+ * concurrent groups, the largest of each lane's groups summed over the
+ * lanes) plus the per-matrix tables.  Pure host function; validates like
  * muon_check_step_args. */
 muon_status muon_workspace_bytes(const muon_matrix *mats, int64_t count, const muon_hparams *hp,
                                  size_t *bytes_out);
@@ -228,9 +229,24 @@ const char *muon_last_error(const muon_context *ctx);
  * the first product).  Non-finite values propagate (IEEE): an Inf or NaN in
  * N_t makes ||N_t||^2 non-finite (muon_last_norms) and every element of
  * O'_t and W_t NaN, as the exact Algorithm 1 does (X = N / ||N|| is NaN
- * where N is infinite, and every product spreads it). */
+ * where N is infinite, and every product spreads it).  Groups of different
+ * shapes are independent ("each logically independent weight", DeepSeek-V4
+ * book ch. 6 §5): unless disabled (muon_set_concurrent_groups) they run
+ * concurrently on up to three side streams that the context creates (at the
+ * default priority), forked from hip_stream by an event and joined back to
+ * it before the call returns, each lane of groups in a workspace slice of
+ * its own; a nonzero workspace cap that those slices together would exceed
+ * runs the groups in turn instead.  Either way the results are the same,
+ * bit for bit. */
 muon_status muon_step(muon_context *ctx, const muon_matrix *mats, int64_t count,
                       const muon_hparams *hp, void *hip_stream);
+
+/* Enables (1, the default) or disables (0) the concurrent execution of a
+ * muon_step call's groups described above; disabled, every group runs in
+ * turn on the caller's stream in one workspace.  Per-stage timing
+ * (muon_profile_enable) and muon_step_noalloc always run them in turn.
+ * Returns MUON_ERR_INVALID_ARGUMENT for a NULL context or another value. */
+muon_status muon_set_concurrent_groups(muon_context *ctx, int32_t enable);
 
 /* For callers that cannot allocate device memory during a step (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation):

@@ -34,7 +34,7 @@ EXPORTS = (
     "muon_check_adamw_args", "muon_workspace_bytes", "muon_create", "muon_destroy",
     "muon_last_error", "muon_step", "muon_adamw_step", "muon_ns_only", "muon_apply_update",
     "muon_last_norms", "muon_profile_enable", "muon_profile_read", "muon_step_noalloc",
-    "muon_stream_probe", "muon_ns_stage",
+    "muon_stream_probe", "muon_ns_stage", "muon_set_concurrent_groups",
 )
 
 MUON_STAGE_GRAM = 0
@@ -119,6 +119,7 @@ def load(path=LIB_PATH):
         "muon_stream_probe": (i32, [vp, vp, vp, i64, i64, i32, i32, vp]),
         "muon_ns_stage": (i32, [vp, i32, vp, vp, vp, i64, i64, c.c_double, c.c_double, c.c_double, vp]),
         "muon_profile_enable": (i32, [vp, i32]),
+        "muon_set_concurrent_groups": (i32, [vp, i32]),
         "muon_profile_read": (i32, [vp, c.POINTER(muon_stage_stats), i32, c.POINTER(i32)]),
     }
     for name, (res, args) in sig.items():
@@ -334,6 +335,10 @@ class Context:
         st = self.lib.muon_stream_probe(self.handle, src.data_ptr(), dst.data_ptr(), stream_bytes, pitch, reads,
                                         writes, _stream_handle(stream))
         _check(self.lib, self.handle, st, "muon_stream_probe")
+
+    def muon_set_concurrent_groups(self, enable=True):
+        _check(self.lib, self.handle, self.lib.muon_set_concurrent_groups(self.handle, 1 if enable else 0),
+               "muon_set_concurrent_groups")
 
     def muon_profile_enable(self, enable=True):
         _check(self.lib, self.handle, self.lib.muon_profile_enable(self.handle, 1 if enable else 0),

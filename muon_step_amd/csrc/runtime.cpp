@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <limits>
 #include <map>
 #include <new>
 #include <string>
@@ -496,6 +497,12 @@ struct muon_context {
     void *noalloc_pinned = nullptr;
     hipEvent_t noalloc_upload_done = nullptr;
     bool noalloc_upload_recorded = false;
+    // concurrent groups: side streams (default priority) forked from the
+    // caller's stream and joined back to it, created on first use
+    static constexpr int kSide = 3;
+    hipStream_t side[kSide] = {};
+    hipEvent_t fork_ev = nullptr, join_ev[kSide] = {};
+    bool concurrent = true;
     // per-stage timing
     bool prof_on = false;
     std::vector<hipEvent_t> ev_pool;
@@ -843,6 +850,77 @@ muon_status run_ns(muon_context *ctx, const MatDesc *descs, int nmat, const Geom
     return MUON_OK;
 }
 
+// Concurrent groups.  Groups share only the descriptor table and the
+// per-call norms, so they may run at the same time: lane 0 is the caller's
+// stream, lanes 1.. side streams forked from it and joined back to it.  A
+// group too small to fill the chip, or the last partial wave of a group's
+// launch, then leaves CUs that another group's work takes.  A large group
+// (an apply launch of 8 waves of the chip or more) has few such CUs and
+// loses L2 locality when another large group shares the chip (the
+// 2048 x 7168 batch split in two concurrent halves runs 3% slower), so the
+// large groups run in turn on lane 0 and only the others go to side lanes,
+// longest first (by Newton-Schulz FLOPs) onto the least loaded lane (lane 0
+// too when no group is large).  A lane runs its groups in turn in a slice
+// of the workspace (ws_off) and of the norm tables (tb_off) of its own,
+// sized for its largest chunk.  One lane (every group in turn on the
+// caller's stream, in one shared slice) when fewer than two groups are
+// left to share the chip, or when the slices side by side exceed a nonzero
+// cap.
+struct Lanes {
+    int n = 1;
+    std::vector<int> lane_of;          // per group
+    std::vector<size_t> ws_off{0, 0};  // lane l's workspace slice: [ws_off[l], ws_off[l + 1])
+    std::vector<size_t> tb_off{0, 0};  // lane l's norm-table slice
+};
+
+Lanes plan_lanes(const std::vector<GroupPlan> &plan, int max_lanes, size_t cap) {
+    Lanes L;
+    const size_t ng = plan.size();
+    L.lane_of.assign(ng, 0);
+    const int n = static_cast<int>(std::min<size_t>(ng, static_cast<size_t>(std::max(max_lanes, 1))));
+    if (n < 2) return L;
+    auto work = [&](size_t i) {
+        const double sd = static_cast<double>(plan[i].g.s), ld = static_cast<double>(plan[i].g.l);
+        return static_cast<double>(plan[i].members.size()) * (3.0 * ld * sd * sd + sd * sd * sd);
+    };
+    auto large = [&](size_t i) {
+        return apply_tiles(plan[i].g) * static_cast<int64_t>(plan[i].members.size()) >= 8 * kCUs;
+    };
+    std::vector<size_t> order;
+    bool any_large = false;
+    for (size_t i = 0; i < ng; ++i) {
+        if (large(i))
+            any_large = true;  // lane 0
+        else
+            order.push_back(i);
+    }
+    if (order.empty() || (!any_large && order.size() < 2)) return L;
+    std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) { return work(a) > work(b); });
+    std::vector<double> load(static_cast<size_t>(n), 0.0);
+    if (any_large) load[0] = std::numeric_limits<double>::infinity();
+    for (size_t i : order) {
+        const size_t l = static_cast<size_t>(std::min_element(load.begin(), load.end()) - load.begin());
+        L.lane_of[i] = static_cast<int>(l);
+        load[l] += work(i);
+    }
+    std::vector<size_t> lws(static_cast<size_t>(n), 0), ltb(static_cast<size_t>(n), 0);
+    for (size_t i = 0; i < ng; ++i) {
+        const GroupPlan &gp = plan[i];
+        const size_t l = static_cast<size_t>(L.lane_of[i]);
+        lws[l] = std::max(lws[l], chunk_layout(gp.g, gp.bf16, gp.chunk, gp.splits.kpart(gp.chunk)).total);
+        ltb[l] = std::max(ltb[l], align_up(tabs_bytes(static_cast<size_t>(gp.chunk) * gp.bpm, gp.chunk)));
+    }
+    L.ws_off.assign(static_cast<size_t>(n) + 1, 0);
+    L.tb_off.assign(static_cast<size_t>(n) + 1, 0);
+    for (size_t l = 0; l < static_cast<size_t>(n); ++l) {
+        L.ws_off[l + 1] = L.ws_off[l] + align_up(lws[l]);
+        L.tb_off[l + 1] = L.tb_off[l] + ltb[l];
+    }
+    if (cap && L.ws_off.back() > cap) return Lanes{1, std::vector<int>(ng, 0)};
+    L.n = n;
+    return L;
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // Copies the descriptor table into the fixed scratch through the context's
@@ -914,9 +992,31 @@ muon_status step_impl(muon_context *ctx, const muon_matrix *mats, int64_t count,
     }
     DeviceGuard guard(ctx->device);
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    // groups on concurrent lanes (plan_lanes), except in the allocation-free
+    // step and under per-stage timing, which run them in turn
+    Lanes lanes;
+    if (!fixed && !ctx->prof_on && ctx->concurrent) {
+        lanes = plan_lanes(plan, 1 + muon_context::kSide, ctx->cap);
+        // the side streams and the fork / join events, made once per context
+        for (int i = 0; lanes.n > 1 && i < lanes.n - 1; ++i) {
+            hipError_t e = hipSuccess;
+            if (!ctx->side[i]) e = hipStreamCreateWithFlags(&ctx->side[i], hipStreamNonBlocking);
+            if (e == hipSuccess && !ctx->join_ev[i])
+                e = hipEventCreateWithFlags(&ctx->join_ev[i], hipEventDisableTiming);
+            if (e == hipSuccess && !ctx->fork_ev) e = hipEventCreateWithFlags(&ctx->fork_ev, hipEventDisableTiming);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                lanes = Lanes{};
+            }
+        }
+    }
+    if (lanes.n == 1) lanes.lane_of.assign(plan.size(), 0);
+    const int nlanes = lanes.n;
+    const size_t tabs_total = nlanes > 1 ? lanes.tb_off.back() : tabs_bytes(parts, max_chunk);
+    if (nlanes > 1) ws = lanes.ws_off.back();
     if (!fixed) {
         if ((s = ensure(ctx, ctx->ws, ws, "workspace")) != MUON_OK) return s;
-        if ((s = ensure(ctx, ctx->tabs, tabs_bytes(parts, max_chunk), "norm tables")) != MUON_OK) return s;
+        if ((s = ensure(ctx, ctx->tabs, tabs_total, "norm tables")) != MUON_OK) return s;
         if ((s = ensure(ctx, ctx->call_nrm2, static_cast<size_t>(count) * sizeof(double), "norm output")) != MUON_OK)
             return s;
         mem = CallMem{static_cast<char *>(ctx->ws.p), static_cast<char *>(ctx->tabs.p),
@@ -946,8 +1046,11 @@ muon_status step_impl(muon_context *ctx, const muon_matrix *mats, int64_t count,
     }
     const MatDesc *ddev = desc_dst;
     const float mu = static_cast<float>(hp->momentum);
-    size_t pos = 0;
-    for (const GroupPlan &gp : plan) {
+    // one group, on stream st, in the workspace and tables of `gm`; pos is its
+    // first entry in the descriptor table
+    auto run_group = [&](const GroupPlan &gp, size_t pos, const CallMem &gm, hipStream_t st) -> muon_status {
+        muon_status s = MUON_OK;
+        const CallMem &mem = gm;
         const bool bf16 = gp.bf16;
         float d = 0.f, sc = 0.f;
         muon_scalars(hp, gp.g.rows, gp.g.cols, &d, &sc);
@@ -998,8 +1101,37 @@ muon_status step_impl(muon_context *ctx, const muon_matrix *mats, int64_t count,
                        gp.splits, runs, nruns, c0, params_aligned, gp.bpm, outs_aligned);
             if (s != MUON_OK) return s;
         }
-        pos += static_cast<size_t>(n_all);
+        return s;
+    };
+    std::vector<hipStream_t> lane_st(static_cast<size_t>(nlanes), st);
+    int forked = 0;  // side streams that wait for the fork
+    if (nlanes > 1) {
+        hipError_t e = hipEventRecord(ctx->fork_ev, st);
+        if (e != hipSuccess) return hip_fail(ctx, e, "hipEventRecord");
+        for (int i = 0; i < nlanes - 1 && s == MUON_OK; ++i) {
+            e = hipStreamWaitEvent(ctx->side[i], ctx->fork_ev, 0);
+            if (e != hipSuccess) {
+                s = hip_fail(ctx, e, "hipStreamWaitEvent");
+                break;
+            }
+            lane_st[static_cast<size_t>(i) + 1] = ctx->side[i];
+            ++forked;
+        }
     }
+    size_t pos = 0;
+    for (size_t i = 0; i < plan.size() && s == MUON_OK; ++i) {
+        const size_t l = static_cast<size_t>(lanes.lane_of[i]);
+        const CallMem gm{mem.ws + lanes.ws_off[l], mem.tabs + lanes.tb_off[l], mem.call_nrm2};
+        s = run_group(plan[i], pos, gm, lane_st[l]);
+        pos += plan[i].members.size();
+    }
+    // every forked side stream joins the caller's stream, also after a failure
+    for (int i = 0; i < forked; ++i) {
+        hipError_t e = hipEventRecord(ctx->join_ev[i], ctx->side[i]);
+        if (e == hipSuccess) e = hipStreamWaitEvent(st, ctx->join_ev[i], 0);
+        if (e != hipSuccess && s == MUON_OK) s = hip_fail(ctx, e, "stream join");
+    }
+    if (s != MUON_OK) return s;
     ctx->last_stream = st;
     ctx->last_count = count;
     ctx->last_nrm2 = mem.call_nrm2;
@@ -1074,7 +1206,10 @@ muon_status muon_workspace_bytes(const muon_matrix *mats, int64_t count, const m
     int64_t mc = 0;
     s = plan_groups(mats, count, hp->ns_precision, 0, &plan, &ws, &parts, &mc, nullptr, 0);
     if (s != MUON_OK) return s;
-    *bytes_out = ws + tabs_bytes(parts, mc) + align_up(static_cast<size_t>(count) * sizeof(double)) +
+    const Lanes lanes = plan_lanes(plan, 1 + muon_context::kSide, 0);
+    const size_t tabs = lanes.n > 1 ? lanes.tb_off.back() : tabs_bytes(parts, mc);
+    if (lanes.n > 1) ws = lanes.ws_off.back();
+    *bytes_out = ws + tabs + align_up(static_cast<size_t>(count) * sizeof(double)) +
                  align_up(static_cast<size_t>(count) * sizeof(MatDesc));
     return MUON_OK;
 }
@@ -1133,6 +1268,11 @@ muon_status muon_destroy(muon_context *ctx) {
     if (ctx->upload_done) (void)hipEventDestroy(ctx->upload_done);
     if (ctx->noalloc_upload_done) (void)hipEventDestroy(ctx->noalloc_upload_done);
     for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
+    for (int i = 0; i < muon_context::kSide; ++i) {
+        if (ctx->side[i]) (void)hipStreamDestroy(ctx->side[i]);
+        if (ctx->join_ev[i]) (void)hipEventDestroy(ctx->join_ev[i]);
+    }
+    if (ctx->fork_ev) (void)hipEventDestroy(ctx->fork_ev);
     delete ctx;
     return MUON_OK;
 }
@@ -1393,6 +1533,12 @@ muon_status muon_last_norms(muon_context *ctx, double *out, int64_t capacity, in
     if (e != hipSuccess) return hip_fail(ctx, e, "hipStreamSynchronize");
     e = hipMemcpy(out, ctx->last_nrm2, static_cast<size_t>(n) * sizeof(double), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpy");
+    return MUON_OK;
+}
+
+muon_status muon_set_concurrent_groups(muon_context *ctx, int32_t enable) {
+    if (!ctx || (enable != 0 && enable != 1)) return MUON_ERR_INVALID_ARGUMENT;
+    ctx->concurrent = enable != 0;
     return MUON_OK;
 }
 

@@ -218,6 +218,27 @@ def test_workspace_bytes_moe_batch(lib):
     assert ns <= out.value <= ns + 64 * 1024 * 1024
 
 
+def test_workspace_bytes_concurrent_groups(lib):
+    """Groups of different shapes run on concurrent lanes, each lane in its own workspace
+    slice: a call of two groups needs about the sum of what each needs alone."""
+    hp = ms.make_hparams()
+
+    def need(shapes):
+        arr = (ms.muon_matrix * len(shapes))(*[_mat(i, r, c) for i, (r, c) in enumerate(shapes)])
+        out = ctypes.c_size_t()
+        assert lib.muon_workspace_bytes(arr, len(shapes), ctypes.byref(hp), ctypes.byref(out)) == ms.MUON_OK
+        return out.value
+
+    a, b = [(1024, 4096)] * 3, [(512, 2048), (2048, 512)]
+    both, one, two = need(a + b), need(a), need(b)
+    assert max(one, two) < both
+    assert abs(both - (one + two)) <= 4 * 1024 * 1024
+
+
+def test_set_concurrent_groups_validates(lib):
+    assert lib.muon_set_concurrent_groups(None, 1) == ms.MUON_ERR_INVALID_ARGUMENT
+
+
 def test_create_without_gpu_reports_device_error(lib):
     try:
         import torch

@@ -358,6 +358,48 @@ def test_step_is_deterministic(ctx, torch_mod):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+def test_concurrent_groups_match_sequential(torch_mod):
+    """Groups of different shapes run concurrently on side streams by default: two
+    consecutive steps (no synchronisation between them) over six groups, among them a
+    split-K Gram / A^2 group, a split-K apply tail, both orientations, fp32 products
+    and fp32 params, are bit-identical to the same two steps with every group in turn
+    on the caller's stream; the per-matrix norms too."""
+    ms = _ms()
+    S = synth.MatrixSpec
+    specs = [S(256, 4352), S(512, 768), S(768, 512), S(96, 300), S(300, 96), S(260, 260, "f32", "f32"),
+             S(4352, 256), S(2304, 2304), S(512, 768, "f32", "bf16")]
+    wl = synth.Workload("t", 29, tuple(specs))
+    inputs = [synth.matrix_inputs(wl, i) for i in range(len(specs))]
+    g2 = [synth.matrix_inputs(synth.Workload("t", 30, tuple(specs)), i)["g"] for i in range(len(specs))]
+    dt = {"bf16": torch_mod.bfloat16, "f32": torch_mod.float32}
+    results = []
+    for concurrent in (True, False):
+        c = ms.Context(0)
+        try:
+            c.muon_set_concurrent_groups(concurrent)
+            tensors, first, second = [], [], []
+            for i, sp in enumerate(specs):
+                p = to_dev(inputs[i]["w"], dt[sp.param_dtype])
+                ga, gb = to_dev(inputs[i]["g"], dt[sp.grad_dtype]), to_dev(g2[i], dt[sp.grad_dtype])
+                m = to_dev(inputs[i]["m"], torch_mod.float32)
+                o = torch_mod.empty((sp.rows, sp.cols), dtype=torch_mod.float32, device="cuda")
+                tensors.append((p, m, o, ga, gb))
+                first.append(ms.matrix(p, ga, m, o))
+                second.append(ms.matrix(p, gb, m, o))
+            say(f"  two steps over {len(specs)} matrices, concurrent groups {concurrent}")
+            c.muon_step(first, ms.make_hparams())
+            c.muon_step(second, ms.make_hparams())
+            torch_mod.cuda.synchronize()
+            norms = c.muon_last_norms(len(specs))
+            results.append(([to_np(t) for tt in tensors for t in tt[:3]], np.asarray(norms)))
+        finally:
+            c.close()
+    (a, na), (b, nb) = results
+    for i, (x, y) in enumerate(zip(a, b)):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), f"tensor {i}"
+    assert np.array_equal(na.view(np.uint64), nb.view(np.uint64))
+
+
 def test_two_steps_equal_resume(ctx, torch_mod):
     """Step 2 from saved state equals two consecutive steps (all state is caller-owned)."""
     ms = _ms()
