@@ -877,8 +877,7 @@ Lanes plan_lanes(const std::vector<GroupPlan> &plan, int max_lanes, size_t cap) 
     Lanes L;
     const size_t ng = plan.size();
     L.lane_of.assign(ng, 0);
-    const int n = static_cast<int>(std::min<size_t>(ng, static_cast<size_t>(std::max(max_lanes, 1))));
-    if (n < 2) return L;
+    if (ng < 2 || max_lanes < 2) return L;
     auto work = [&](size_t i) {
         const double sd = static_cast<double>(plan[i].g.s), ld = static_cast<double>(plan[i].g.l);
         return static_cast<double>(plan[i].members.size()) * (3.0 * ld * sd * sd + sd * sd * sd);
@@ -894,7 +893,9 @@ Lanes plan_lanes(const std::vector<GroupPlan> &plan, int max_lanes, size_t cap) 
         else
             order.push_back(i);
     }
-    if (order.empty() || (!any_large && order.size() < 2)) return L;
+    // lane 0 for the large groups (if any), one more per remaining group
+    const int n = static_cast<int>(std::min<size_t>(order.size() + (any_large ? 1 : 0), static_cast<size_t>(max_lanes)));
+    if (order.empty() || n < 2) return L;
     std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) { return work(a) > work(b); });
     std::vector<double> load(static_cast<size_t>(n), 0.0);
     if (any_large) load[0] = std::numeric_limits<double>::infinity();
