@@ -63,8 +63,8 @@ def _check_sampled(mats_dev, idx, w0_host, g_host, m0_host, rows, cols):
 
 
 def test_moe_expert_batch_full_size(torch_mod):
-    """256 x 2048x7168 bf16 in one call, as timed by bench.py; experts 0, 97 and 255
-    against the oracle, all 256 against the norm band."""
+    """256 x 2048x7168 bf16 in one call, as timed by bench.py; experts 0, 97, 160 and
+    255 against the oracle, all 256 against the norm band."""
     torch = torch_mod
     ms = _ms()
     rows, cols, count = 2048, 7168, 256
@@ -75,7 +75,7 @@ def test_moe_expert_batch_full_size(torch_mod):
     params = (torch.randn(count, rows, cols, generator=gen, device="cuda") * synth.gen.PARAM_STD).to(torch.bfloat16)
     moms = torch.zeros(count, rows, cols, dtype=torch.float32, device="cuda")
     w0 = params.clone()
-    sampled = (0, 97, 255)
+    sampled = (0, 97, 160, 255)
     outs = {e: torch.empty(rows, cols, dtype=torch.float32, device="cuda") for e in sampled}
     mats = [ms.matrix(params[e], grads[e], moms[e], outs.get(e)) for e in range(count)]
     ctx = ms.Context(0)
@@ -236,9 +236,11 @@ def test_dense_block_full_size(dense_run, name):
 def test_moe16b_full_step(torch_mod):
     """The full 16B-MoE optimizer step in two calls: Muon over all 27 x (4 + 192)
     matrices (workspace capped at 24 GiB, so each shape group runs in chunks) and
-    AdamW over the 102400x2048 embedding and head.  One matrix per shape against
-    the oracle, 96 spread over the list against the norm band, AdamW bit-exact on
-    8192 sampled elements of each tensor (first, last and random positions)."""
+    AdamW over the 102400x2048 embedding and head.  Against the oracle: layers 0
+    and 26 (their four attention matrices and experts 0 and 63, up, gate and
+    down) and the middle matrix of each shape; 96 spread over the list against
+    the norm band; AdamW bit-exact on 8192 sampled elements of each tensor
+    (first, last and random positions)."""
     torch = torch_mod
     ms = _ms()
     wl = synth.WORKLOADS["moe16b_full_step"]
@@ -257,7 +259,13 @@ def test_moe16b_full_step(torch_mod):
     params = [(torch.randn(sp.rows, sp.cols, generator=gen, device="cuda") * synth.gen.PARAM_STD).to(torch.bfloat16)
               for sp in specs]
     moms = [torch.zeros(sp.rows, sp.cols, device="cuda") for sp in specs]
+    per_layer = 4 + 3 * 64
     checked = {ids[len(ids) // 2] for ids in by_shape.values()}
+    for layer in (0, 26):
+        base = layer * per_layer
+        checked |= set(range(base, base + 4))                              # attention
+        checked |= {base + 4 + 3 * e + k for e in (0, 63) for k in range(3)}  # experts 0, 63
+    assert len(specs) == 27 * per_layer and specs[26 * per_layer + 4 + 3 * 63 + 2].name == "l26.e63.down"
     banded = set(range(0, len(specs), len(specs) // 96)) | checked
     w0 = {i: params[i].clone() for i in banded}
     outs = {i: torch.empty(specs[i].rows, specs[i].cols, device="cuda") for i in checked}
@@ -283,6 +291,7 @@ def test_moe16b_full_step(torch_mod):
         torch.cuda.synchronize()
     finally:
         ctx.close()
+    say(f"16B-MoE step: {len(checked)} matrices against the oracle")
     for i in sorted(checked):
         sp = specs[i]
         _check_sampled((params[i], grads[i], moms[i], outs[i]), sp.name, to_np(w0[i]), to_np(grads[i]),
