@@ -358,12 +358,13 @@ def test_step_is_deterministic(ctx, torch_mod):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-def test_concurrent_groups_match_sequential(torch_mod):
+@pytest.mark.parametrize("precision", ["bf16", "f32"])
+def test_concurrent_groups_match_sequential(torch_mod, precision):
     """Groups of different shapes run concurrently on side streams by default: two
-    consecutive steps (no synchronisation between them) over six groups, among them a
-    split-K Gram / A^2 group, a split-K apply tail, both orientations, fp32 products
-    and fp32 params, are bit-identical to the same two steps with every group in turn
-    on the caller's stream; the per-matrix norms too."""
+    consecutive steps (no synchronisation between them) over six groups, among them
+    (bf16 products) a split-K Gram / A^2 group and a split-K apply tail, both
+    orientations and fp32 params, are bit-identical to the same two steps with every
+    group in turn on the caller's stream; the per-matrix norms too."""
     ms = _ms()
     S = synth.MatrixSpec
     specs = [S(256, 4352), S(512, 768), S(768, 512), S(96, 300), S(300, 96), S(260, 260, "f32", "f32"),
@@ -386,9 +387,10 @@ def test_concurrent_groups_match_sequential(torch_mod):
                 tensors.append((p, m, o, ga, gb))
                 first.append(ms.matrix(p, ga, m, o))
                 second.append(ms.matrix(p, gb, m, o))
-            say(f"  two steps over {len(specs)} matrices, concurrent groups {concurrent}")
-            c.muon_step(first, ms.make_hparams())
-            c.muon_step(second, ms.make_hparams())
+            say(f"  two steps over {len(specs)} matrices, {precision} products, concurrent groups {concurrent}")
+            hp = ms.make_hparams(ns_precision=ms.MUON_NS_BF16 if precision == "bf16" else ms.MUON_NS_F32)
+            c.muon_step(first, hp)
+            c.muon_step(second, hp)
             torch_mod.cuda.synchronize()
             norms = c.muon_last_norms(len(specs))
             results.append(([to_np(t) for tt in tensors for t in tt[:3]], np.asarray(norms)))
