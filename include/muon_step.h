@@ -21,8 +21,11 @@
  *   - Pointers documented as "device" point to memory of the context's GPU;
  *     "host" pointers are read before the call returns and may be freed then.
  *   - Matrices are row-major and contiguous (row pitch == cols elements).
- *   - Work is enqueued on the given HIP stream (NULL = the null stream); no
- *     entry point synchronises the stream except where stated.
+ *   - Work is enqueued on the given HIP stream (NULL = the null stream), and
+ *     by muon_step also on side streams of the context that are forked from
+ *     it and joined back to it within the call, so that all of it is ordered
+ *     like work of the given stream; no entry point synchronises the stream
+ *     except where stated.
  *   - Every argument is validated before anything is enqueued: a non-OK
  *     status means no work was enqueued.  Launch failures return
  *     MUON_ERR_DEVICE.  No C++ exception crosses this boundary.
