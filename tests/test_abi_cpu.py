@@ -235,6 +235,22 @@ def test_workspace_bytes_concurrent_groups(lib):
     assert abs(both - (one + two)) <= 4 * 1024 * 1024
 
 
+def test_workspace_bytes_large_groups_in_turn(lib):
+    """Groups whose apply launch fills the chip 8 times or more run in turn in one
+    workspace slice: two such groups need about what the larger one needs alone."""
+    hp = ms.make_hparams()
+
+    def need(shapes):
+        arr = (ms.muon_matrix * len(shapes))(*[_mat(i, r, c) for i, (r, c) in enumerate(shapes)])
+        out = ctypes.c_size_t()
+        assert lib.muon_workspace_bytes(arr, len(shapes), ctypes.byref(hp), ctypes.byref(out)) == ms.MUON_OK
+        return out.value
+
+    a, b = [(2048, 7168)] * 16, [(1024, 4096)] * 40   # 3584 and 2560 apply tiles
+    both, one, two = need(a + b), need(a), need(b)
+    assert abs(both - max(one, two)) <= 4 * 1024 * 1024
+
+
 def test_set_concurrent_groups_validates(lib):
     assert lib.muon_set_concurrent_groups(None, 1) == ms.MUON_ERR_INVALID_ARGUMENT
 
